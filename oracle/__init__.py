@@ -1,0 +1,7 @@
+"""CPU oracle for the 3D-windowed joint-attention layer (test infrastructure only).
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+may import this package.  The product path (``video_dit_window_amd``) never
+imports it and shares no code with it.
+"""
+from .wsp_oracle import *  # noqa: F401,F403
