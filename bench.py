@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of one pass of the windowed joint-attention layer on one MI355X.
+
+A step is one pass of the whole hot path over the 1080p-shaped workload
+(T=21, H=68, W=120 latent grid, 171360 video tokens; windows from
+nt,nh,nw = 4,3,3; 20 heads x 128; 256 text tokens; bf16):
+  entry relayout of q, k, v (canonical -> regular), regular-layout window
+  attention + text mean, relayout of q, k, v (regular -> shifted),
+  shifted-layout window attention + text mean, exit relayout of the video
+  output (shifted -> canonical).
+Inputs are synthetic (seeded normal samples, N(0,1)/sqrt(128)) and resident in
+HBM before the timed region.  The JSON line reports window-attention TFLOP/s
+over the whole step, video tokens/s/layer, the roofline of the attention
+kernel and the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import wsp_inputs as I  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+METRIC = "window-attn TFLOP/s + video tokens/s/layer at 1080p grid; % MFMA peak"
+
+
+def attn_flops(lengths, heads, head_dim, text_len):
+    """Algorithmic FLOPs: QK^T and PV of every video and text query,
+    4 * D * H * sum_w (L_w + Lt)^2."""
+    L = np.asarray(lengths, dtype=np.int64) + text_len
+    return 4 * head_dim * heads * int((L * L).sum())
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle, as it stands, on a bounded sample of the workload: (window,
+    head) pairs of the regular layout in largest-first order until the time
+    budget is spent.  Returns the cpu_baseline object."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    op = O.plan(*geo, O.REGULAR)
+    rng = np.random.default_rng(12345)
+    tq, tk, tv = (rng.standard_normal((w.text_len, w.head_dim)) / np.sqrt(w.head_dim)
+                  for _ in range(3))
+    flops, pairs, el = 0, 0, 0.0
+    for win in op.lpt:
+        L = int(op.offsets[win + 1] - op.offsets[win])
+        for h in range(w.heads):
+            qv, kv, vv = (rng.standard_normal((L, w.head_dim)) / np.sqrt(w.head_dim) for _ in range(3))
+            t1 = time.perf_counter()
+            O.joint_attention(qv, kv, vv, tq, tk, tv)
+            el += time.perf_counter() - t1
+            flops += 4 * w.head_dim * (L + w.text_len) ** 2
+            pairs += 1
+            if el > budget_s:
+                break
+        if el > budget_s:
+            break
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{pairs} (window, head) pairs of the {w.name} regular layout, largest "
+                      f"windows first, float64 numpy; {el:.1f} s inside the oracle",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="1080p_bf16", choices=["720p_bf16", "1080p_bf16", "4k_bf16"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the multi-GPU window-parallel path is not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import video_dit_window_amd as W
+
+    w = I.WORKLOADS[args.workload]
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    layouts = [W.REGULAR if m == "regular" else W.SHIFTED for m in w.layouts]
+    plans = [W.Plan(*geo, m) for m in layouts]
+    canon = W.canonical(w.T, w.H, w.W)
+    inp = I.qkv(w, bits_only=True)
+    dev = {n: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda() for n, (_, b) in inp.items()}
+    del inp
+    N, Hh, D, Lt = w.n_tokens, w.heads, w.head_dim, w.text_len
+    bufs = {n: torch.empty_like(dev["q"]) for n in ("q", "k", "v")}
+    outs = [torch.empty_like(dev["q"]) for _ in plans]
+    out_c = torch.empty_like(dev["q"])
+    txts = [torch.empty_like(dev["txt_q"]) for _ in plans]
+    ws_bytes = max(W.window_attn_workspace(p, Hh, D, Lt, W.BF16) for p in plans)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    flops = [attn_flops(np.diff(p.tables()["offsets"]), Hh, D, Lt) for p in plans]
+    row_bytes = Hh * D * 2
+    stream = torch.cuda.current_stream()
+
+    ev = {"attn": [], "relayout": []}
+
+    def timed(kind, fn, record):
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev[kind].append((a, b))
+        else:
+            fn()
+
+    # q,k,v of consecutive layouts need distinct source/destination buffers.
+    bufs2 = {n: torch.empty_like(dev["q"]) for n in ("q", "k", "v")}
+
+    def step(record):
+        src, cur = canon, {"q": dev["q"], "k": dev["k"], "v": dev["v"]}
+        for li, p in enumerate(plans):
+            dst = bufs if li % 2 == 0 else bufs2
+            for n in ("q", "k", "v"):
+                timed("relayout", lambda n=n, dst=dst, src=src, p=p: W.relayout(cur[n], src, p, out=dst[n]), record)
+            cur, src = {n: dst[n] for n in ("q", "k", "v")}, p
+            timed("attn", lambda li=li, p=p, cur=cur: W.window_attn(
+                p, cur["q"], cur["k"], cur["v"], dev["txt_q"], dev["txt_k"], dev["txt_v"],
+                out=outs[li], txt_out=txts[li], workspace=ws), record)
+        timed("relayout", lambda: W.relayout(outs[-1], plans[-1], canon, out=out_c), record)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in ev["attn"]]
+    rel_ms = [a.elapsed_time(b) for a, b in ev["relayout"]]
+    step_flops = sum(flops)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    # dominant kernel: window attention (per call = attention kernel + text mean)
+    per_call_flops = step_flops / len(plans)
+    attn_avg_ms = float(np.mean(attn_ms))
+    attn_tflops = per_call_flops / (attn_avg_ms * 1e-3) / 1e12
+    rel_bytes = 2 * N * row_bytes + 4 * N
+    rel_avg_ms = float(np.mean(rel_ms))
+    rel_gbps = rel_bytes / (rel_avg_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "grid_thw": [w.T, w.H, w.W], "n_thw": [w.nt, w.nh, w.nw],
+                   "video_tokens": N, "heads": Hh, "head_dim": D, "text_len": Lt,
+                   "layers": list(w.layouts), "windows": [p.n_windows for p in plans]},
+        "video_tokens_per_s_per_layer": round(N / (attn_avg_ms * 1e-3), 1),
+        "attn_kernel_tflops": round(attn_tflops, 2),
+        "attn_mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "relayout_gbps": round(rel_gbps, 1),
+        "relayout_hbm_frac": round(rel_gbps / HBM_PEAK_GBPS, 4),
+        "breakdown_ms_per_step": {"attention+text_mean": round(sum(attn_ms) / args.steps, 4),
+                                  "relayout": round(sum(rel_ms) / args.steps, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel<128,1> (+ text_mean_kernel in the same call)",
+                     "flop_per_launch": per_call_flops, "avg_launch_ms": round(attn_avg_ms, 4)},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * wsp.h -- C ABI of the MI355X (gfx950) 3D-windowed joint-attention layer.
+ *
+ * The layer is the one described on the page "Window-Aligned Sequence
+ * Parallelism (SeedVR2)": a post-patch (T, H, W) video token grid is cut into
+ * regular or half-window-shifted, boundary-clipped 3D windows ("Window
+ * layouts"); inside each window the video tokens attend jointly with the
+ * replicated text tokens ("SeedVR2 integration"); the per-window text outputs
+ * are averaged over the window count ("Text stream"); and activations are
+ * permuted between layouts at layer boundaries ("Plan A redistribution",
+ * local-permutation case).  The joint call shape -- image Q/K/V plus separate
+ * text Q/K/V -- follows "Parallelize new models with USP (text replica)",
+ * section "3. Attention with USP".
+ *
+ * Conventions for every entry point:
+ *   - Return value: WSP_OK (0) or a negative wsp_status.  On error nothing is
+ *     launched and wsp_last_error() returns a message (thread-local, valid
+ *     until the calling thread's next wsp_* call).
+ *   - Device pointers are owned by the caller; the library never frees or
+ *     keeps them.  Plans are owned by the library until wsp_plan_free().
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Device work is
+ *     enqueued on it and the call returns without waiting for it.  The only
+ *     synchronous step is the first device use of a plan (or of a plan pair
+ *     in wsp_relayout, or of a new head/text-length shape in
+ *     wsp_window_attn) on a device: its index tables are then copied to that
+ *     device once and cached with the plan.
+ *   - Tensors are dense row-major.  A "row" is one token: [n_heads, head_dim]
+ *     elements for attention tensors, `row_bytes` bytes for wsp_relayout.
+ *   - Calls on different streams that share a plan are safe; output buffers
+ *     must not overlap inputs.
+ */
+#ifndef WSP_H
+#define WSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Window layout of one token grid (opaque). */
+typedef struct wsp_plan_t wsp_plan_t;
+
+enum wsp_method {
+    WSP_REGULAR = 0,   /* slice(i*w, min((i+1)*w, n)) on every axis           */
+    WSP_SHIFTED = 1,   /* every cut moved back by floor(w/2), clipped to [0,n) */
+    WSP_CANONICAL = 2  /* identity layout: one window, ids = 0..N-1           */
+};
+
+enum wsp_dtype { WSP_F32 = 0, WSP_BF16 = 1 };
+
+enum wsp_status {
+    WSP_OK = 0,
+    WSP_EINVAL = -1,      /* bad argument: geometry, method, dtype, pointer, size */
+    WSP_ERANGE = -2,      /* a size does not fit the library's index types        */
+    WSP_ENOMEM = -3,      /* host or device allocation failed                     */
+    WSP_EWORKSPACE = -4,  /* workspace missing or smaller than required           */
+    WSP_EDEVICE = -5      /* a HIP runtime call failed (message holds HIP's text) */
+};
+
+/* Order in which wsp_window_attn hands work to the GPU (tuning/measurement). */
+enum wsp_order {
+    WSP_ORDER_LPT_XCD = 0, /* largest window first, (window, head) groups spread
+                              over the 8 XCDs so each group's tiles share one L2 */
+    WSP_ORDER_LPT = 1,     /* largest window first, plain block order            */
+    WSP_ORDER_ID = 2       /* window id order                                    */
+};
+
+/*
+ * wsp_plan -- build the window tables of one layout.
+ *
+ * "Window-Aligned Sequence Parallelism (SeedVR2)", section "Window layouts":
+ *   scale = sqrt(45*80 / (H*W)) (IEEE double, the 720p reference area);
+ *   wh = ceil(round(H*scale) / nh), ww = ceil(round(W*scale) / nw) with
+ *   round() ties-to-even; wt = ceil(min(T, 30) / nt).  Regular cuts at
+ *   multiples of the window; shifted cuts at k*w - floor(w/2), clipped to the
+ *   axis (empty windows are not produced).  Windows are numbered with the w
+ *   axis outermost and t innermost; tokens inside a window are row-major in
+ *   (t, h, w); the canonical id of (t, h, w) is (t*H + h)*W + w.
+ *   Section "Planner": the largest-first order sorts windows by
+ *   (-video token count, window id).
+ *
+ * T, H, W     grid extents (> 0, T*H*W < 2^31)
+ * nt, nh, nw  window counts of the size rule (> 0); ignored for WSP_CANONICAL
+ * method      enum wsp_method
+ * out         receives the new plan (set to NULL on error)
+ * Errors: WSP_EINVAL (non-positive size, unknown method, a window size that
+ * rounds to zero), WSP_ERANGE (T*H*W >= 2^31), WSP_ENOMEM.
+ */
+int wsp_plan(int T, int H, int W, int nt, int nh, int nw, int method, wsp_plan_t **out);
+
+/*
+ * wsp_plan_info -- sizes of a plan.  Any output pointer may be NULL.
+ * n_tokens  T*H*W;  n_windows  window count;  win_size  {wt, wh, ww}
+ * Errors: WSP_EINVAL (p is NULL).
+ */
+int wsp_plan_info(const wsp_plan_t *p, int64_t *n_tokens, int32_t *n_windows, int32_t *win_size);
+
+/*
+ * wsp_plan_tables -- copy the host tables of a plan into caller buffers.
+ * Any pointer may be NULL (that table is skipped).
+ * offsets  [n_windows + 1]  window w owns layout rows offsets[w]..offsets[w+1]-1
+ * ids      [n_tokens]       canonical id held at each layout row
+ * inv      [n_tokens]       layout row of each canonical id (ids[inv[c]] == c)
+ * boxes    [6 * n_windows]  t0,t1,h0,h1,w0,w1 (half-open) per window
+ * lpt      [n_windows]      window ids, largest first, ties by id
+ * Errors: WSP_EINVAL (p is NULL).
+ */
+int wsp_plan_tables(const wsp_plan_t *p, int32_t *offsets, int32_t *ids, int32_t *inv,
+                    int32_t *boxes, int32_t *lpt);
+
+/* wsp_plan_free -- release a plan and its cached device tables (NULL is a no-op).
+ * The caller must make sure no enqueued work still reads them. */
+void wsp_plan_free(wsp_plan_t *p);
+
+/*
+ * wsp_relayout -- local permutation between two layouts of the same grid.
+ *
+ * "Window-Aligned Sequence Parallelism (SeedVR2)", sections "Motivation" and
+ * "Plan A redistribution": a layout transition in which no token changes
+ * owner is a local permutation.  y[j] = x[inv_src[ids_dst[j]]]: row j of
+ * the output is the row of x that holds canonical token ids_dst[j].  Bytes
+ * are moved unchanged (any dtype).
+ *
+ * x, y       device pointers, [n_tokens, row_bytes] each, 16-byte aligned,
+ *            non-overlapping
+ * row_bytes  bytes per token row, a positive multiple of 16
+ * src, dst   plans of the same (T, H, W) grid (either may be WSP_CANONICAL)
+ * Errors: WSP_EINVAL (NULL or misaligned pointer, bad row_bytes, grids
+ * differ, x == y), WSP_ERANGE (n_tokens*row_bytes overflows), WSP_ENOMEM,
+ * WSP_EDEVICE.
+ */
+int wsp_relayout(const void *x, void *y, int64_t row_bytes, const wsp_plan_t *src,
+                 const wsp_plan_t *dst, void *stream);
+
+/*
+ * wsp_window_attn_workspace -- device workspace (bytes) wsp_window_attn needs:
+ * n_windows * text_len * n_heads * head_dim * 4 (one float32 text output per
+ * window, reduced in window order).  0 when text_len == 0.
+ * Errors: WSP_EINVAL (bad plan/shape/dtype), WSP_ERANGE.
+ */
+int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, int text_len,
+                              int dtype, size_t *bytes);
+
+/*
+ * wsp_window_attn -- joint attention inside every window of p, and the
+ * window-averaged text output.
+ *
+ * "Window-Aligned Sequence Parallelism (SeedVR2)", section "SeedVR2
+ * integration": each window attends over the packed segment
+ * [video window; replicated text]; section "Text stream": each window yields
+ * one text output T_w and the text result is (sum over windows of T_w) /
+ * window count.  "Parallelize new models with USP (text replica)", section
+ * "3. Attention with USP": the attention is SDPA without mask or dropout,
+ * with image and text Q/K/V passed as separate tensors.
+ *
+ * For window w (layout rows a = offsets[w] .. b = offsets[w+1]-1) and head h:
+ *   Q = [q[a:b, h]; txt_q[:, h]],  K = [k[a:b, h]; txt_k[:, h]],
+ *   V = [v[a:b, h]; txt_v[:, h]],  O = softmax(Q K^T * scale) V;
+ *   out[a:b, h] = the first b-a rows of O; T_w = the last text_len rows.
+ *   txt_out[:, h] = (sum_w T_w) / n_windows (float32 sum in window order,
+ *   rounded once to dtype).
+ *
+ * p                 plan; q/k/v/out rows are in its layout
+ * q, k, v           device, [n_tokens, n_heads, head_dim] of dtype
+ * txt_q/k/v         device, [text_len, n_heads, head_dim] of dtype (may be
+ *                   NULL when text_len == 0)
+ * n_heads           1 .. 32767;  head_dim  64 or 128;  text_len  >= 0
+ * dtype             WSP_BF16 (MFMA path, float32 accumulation and softmax)
+ *                   or WSP_F32 (float32 throughout)
+ * scale             softmax scale; <= 0 selects 1/sqrt(head_dim)
+ * out               device, [n_tokens, n_heads, head_dim] of dtype
+ * txt_out           device, [text_len, n_heads, head_dim] of dtype (NULL
+ *                   allowed when text_len == 0)
+ * workspace         device, >= wsp_window_attn_workspace() bytes, 16-byte
+ *                   aligned; contents on entry are ignored
+ * Errors: WSP_EINVAL (pointer NULL or not 16-byte aligned, unsupported
+ * head_dim/dtype, n_heads out of range), WSP_ERANGE (a window longer than
+ * the kernel's tile index range), WSP_EWORKSPACE, WSP_ENOMEM, WSP_EDEVICE.
+ */
+int wsp_window_attn(const wsp_plan_t *p, const void *q, const void *k, const void *v,
+                    const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                    int head_dim, int text_len, int dtype, float scale, void *out,
+                    void *txt_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * wsp_set_attn_order -- process-wide dispatch order of wsp_window_attn
+ * (enum wsp_order; default WSP_ORDER_LPT_XCD).  "Window-Aligned Sequence
+ * Parallelism (SeedVR2)", section "Planner": ragged windows are balanced by
+ * token count, largest first; here that order sequences GPU work groups.
+ * Results do not depend on the order.  Errors: WSP_EINVAL.
+ */
+int wsp_set_attn_order(int order);
+
+/* wsp_last_error -- message of the calling thread's last failed call ("" if none). */
+const char *wsp_last_error(void);
+
+/* wsp_version -- ABI version of this header (major*10000 + minor*100 + patch). */
+int wsp_version(void);
+
+#define WSP_VERSION 100
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WSP_H */

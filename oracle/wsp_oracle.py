@@ -42,7 +42,7 @@ __all__ = [
     "REGULAR", "SHIFTED", "CANONICAL", "MAX_TEMPORAL_WINDOW", "SHIFT_FLOOR",
     "window_size", "axis_intervals", "Plan", "plan", "canonical_plan",
     "relayout", "relayout_perm", "layer_schedule", "transitions",
-    "window_attn", "text_mean", "attn_flops", "relayout_bytes",
+    "joint_attention", "window_attn", "text_mean", "attn_flops", "relayout_bytes",
 ]
 
 REGULAR = 0
@@ -234,6 +234,35 @@ def _softmax_rows(s: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def joint_attention(q_vid, k_vid, v_vid, txt_q, txt_k, txt_v, scale=None,
+                    dtype=np.float64, text_only=False):
+    """Attention of one window and one head over the joint segment.
+
+    q_vid/k_vid/v_vid: [L, D] video rows of the window; txt_q/k/v: [Lt, D].
+    Returns (video_out [L, D] or None when ``text_only``, text_out [Lt, D]).
+
+    [WSP] "SeedVR2 integration": the window's packed segment is
+    [video window; replicated text].  [USP] "3. Attention with USP": the
+    attention is SDPA of that joint sequence with no mask and no dropout;
+    scale defaults to 1/sqrt(D).
+    """
+    D = np.shape(txt_q)[-1] if np.size(txt_q) else np.shape(q_vid)[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    K = np.concatenate([k_vid, txt_k], axis=0).astype(dtype)
+    V = np.concatenate([v_vid, txt_v], axis=0).astype(dtype)
+    if text_only:
+        Q = np.asarray(txt_q).astype(dtype)
+    else:
+        Q = np.concatenate([q_vid, txt_q], axis=0).astype(dtype)
+    P = _softmax_rows((Q @ K.T) * dtype(scale))
+    O = P @ V
+    if text_only:
+        return None, O
+    L = len(q_vid)
+    return O[:L], O[L:]
+
+
 def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None,
                 windows=None, heads=None, dtype=np.float64, keep_windows=False):
     """Joint attention inside every window, plus the window-averaged text output.
@@ -245,13 +274,9 @@ def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None,
     text mean then only covers the listed heads (its divisor is always the
     layout's window count).
 
-    [WSP] "SeedVR2 integration": each window attends over the packed segment
-    [video window; replicated text].  [USP] "3. Attention with USP": the
-    attention is the plain SDPA of the joint sequence -- no causal mask, no
-    dropout, scale 1/sqrt(D) -- with the image and text Q/K/V passed apart.
-    [WSP] "Text stream": every window yields one text output T_w; the next
-    text state is the sum of all T_w divided by the number of windows (not a
-    token-weighted mean).
+    Each (window, head) is ``joint_attention``.  [WSP] "Text stream": every
+    window yields one text output T_w; the next text state is the sum of all
+    T_w divided by the number of windows (not a token-weighted mean).
     """
     q, k, v = (np.asarray(a) for a in (q, k, v))
     txt_q, txt_k, txt_v = (np.asarray(a) for a in (txt_q, txt_k, txt_v))
@@ -261,8 +286,6 @@ def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None,
         raise ValueError("q/k/v shape does not match the plan")
     if txt_q.shape != (Lt, Hh, D) or txt_k.shape != txt_q.shape or txt_v.shape != txt_q.shape:
         raise ValueError("text tensors must be [Lt, H, D]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
     windows = range(p.n_windows) if windows is None else list(windows)
     heads = range(Hh) if heads is None else list(heads)
     out = np.full((N, Hh, D), np.nan, dtype=dtype)
@@ -271,15 +294,12 @@ def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None,
     for w in windows:
         a, b = int(p.offsets[w]), int(p.offsets[w + 1])
         for h in heads:
-            Q = np.concatenate([q[a:b, h, :], txt_q[:, h, :]], axis=0).astype(dtype)
-            K = np.concatenate([k[a:b, h, :], txt_k[:, h, :]], axis=0).astype(dtype)
-            V = np.concatenate([v[a:b, h, :], txt_v[:, h, :]], axis=0).astype(dtype)
-            P = _softmax_rows((Q @ K.T) * dtype(scale))
-            O = P @ V
-            out[a:b, h, :] = O[: b - a]
-            tsum[:, h, :] += O[b - a:]
+            ov, ot = joint_attention(q[a:b, h], k[a:b, h], v[a:b, h], txt_q[:, h], txt_k[:, h],
+                                     txt_v[:, h], scale=scale, dtype=dtype)
+            out[a:b, h, :] = ov
+            tsum[:, h, :] += ot
             if keep_windows:
-                per_window[(w, h)] = O[b - a:].copy()
+                per_window[(w, h)] = ot.copy()
     txt_out = text_mean(tsum, p.n_windows)
     if keep_windows:
         return out, txt_out, per_window

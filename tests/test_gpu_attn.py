@@ -1,0 +1,207 @@
+"""GPU parity of wsp_window_attn against the CPU oracle.
+
+Small and mid-size grids are compared element by element in full (they span
+many 128-row query tiles and 64-key tiles, with ragged tails, tiny edge
+windows, D = 64 and 128, text lengths 0, 1 and odd).  The full-size 720p,
+1080p and 4K workloads are compared on sampled (window, head) pairs that the
+oracle computes one by one, and on the complete text mean of one head.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import video_dit_window_amd as W
+import wsp_inputs as I
+from helpers import check_bf16, check_f32, from_dev, log, to_dev
+
+pytestmark = pytest.mark.gpu
+METH = {"regular": (O.REGULAR, W.REGULAR), "shifted": (O.SHIFTED, W.SHIFTED)}
+
+
+def upload(inp, dtype):
+    return {k: to_dev(v, b, dtype) for k, (v, b) in inp.items()}
+
+
+def host_f64(inp, name):
+    v, b = inp[name]
+    return (v if v is not None else I.bf16_bits_to_f32(b)).astype(np.float64)
+
+
+def run_full(w, method, dtype_check, order=None, scale=None):
+    """Whole-grid comparison for a small workload: canonical inputs are
+    relayouted to the method's layout on the GPU, attended, and compared with
+    the oracle over every output element."""
+    import torch
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    om, wm = METH[method]
+    op, wp = O.plan(*geo, om), W.Plan(*geo, wm)
+    oc, wc = O.canonical_plan(*geo[:3]), W.canonical(*geo[:3])
+    inp = I.qkv(w)
+    d = upload(inp, w.dtype)
+    q, k, v = (W.relayout(d[n], wc, wp) for n in ("q", "k", "v"))
+    if order is not None:
+        W.set_attn_order(order)
+    try:
+        out, txt = W.window_attn(wp, q, k, v, d["txt_q"], d["txt_k"], d["txt_v"], scale=scale)
+    finally:
+        W.set_attn_order(W.ORDER_LPT_XCD)
+    out_c = W.relayout(out, wp, wc)
+    torch.cuda.synchronize()
+    h = {n: host_f64(inp, n) for n in I.QKV_NAMES}
+    ref_out, ref_txt = O.window_attn(op, *(O.relayout(h[n], oc, op) for n in ("q", "k", "v")),
+                                     h["txt_q"], h["txt_k"], h["txt_v"], scale=scale)
+    dtype_check(from_dev(out), ref_out, f"{w.name} {method} video")
+    dtype_check(from_dev(out_c), O.relayout(ref_out, op, oc), f"{w.name} {method} video (canonical)")
+    if w.text_len:
+        dtype_check(from_dev(txt), ref_txt, f"{w.name} {method} text mean")
+    return out, txt
+
+
+# ------------------------------------------------------------------ float32
+@pytest.mark.parametrize("method", ["regular", "shifted"])
+def test_tiny_f32_workload(gpu, method):
+    """The tiny float32 workload: 5x20x36 grid, 2x2x2 ragged windows, 4 heads
+    x 64, 16 text tokens, max |err| <= 1e-5 against the float64 oracle."""
+    run_full(I.WORKLOADS["tiny_f32"], method, check_f32)
+
+
+def test_tiny_f32_layer_pair_flow(gpu):
+    """Canonical -> regular layer -> relayout q,k,v -> shifted layer -> outputs
+    back to canonical order, as one pass of the tiny workload."""
+    import torch
+    w = I.WORKLOADS["tiny_f32"]
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    oc, orr, osh = O.canonical_plan(*geo[:3]), O.plan(*geo, O.REGULAR), O.plan(*geo, O.SHIFTED)
+    wc, wr, ws = W.canonical(*geo[:3]), W.Plan(*geo, W.REGULAR), W.Plan(*geo, W.SHIFTED)
+    inp = I.qkv(w)
+    d = upload(inp, "f32")
+    qr, kr, vr = (W.relayout(d[n], wc, wr) for n in "qkv")
+    out_r, txt_r = W.window_attn(wr, qr, kr, vr, d["txt_q"], d["txt_k"], d["txt_v"])
+    qs, ks, vs = (W.relayout(t, wr, ws) for t in (qr, kr, vr))
+    out_s, txt_s = W.window_attn(ws, qs, ks, vs, d["txt_q"], d["txt_k"], d["txt_v"])
+    out_s_c = W.relayout(out_s, ws, wc)
+    torch.cuda.synchronize()
+    h = {n: host_f64(inp, n) for n in I.QKV_NAMES}
+    t = (h["txt_q"], h["txt_k"], h["txt_v"])
+    ref_r, ref_tr = O.window_attn(orr, *(O.relayout(h[n], oc, orr) for n in "qkv"), *t)
+    ref_s, ref_ts = O.window_attn(osh, *(O.relayout(h[n], oc, osh) for n in "qkv"), *t)
+    check_f32(from_dev(out_r), ref_r, "regular video")
+    check_f32(from_dev(txt_r), ref_tr, "regular text")
+    check_f32(from_dev(out_s_c), O.relayout(ref_s, osh, oc), "shifted video (canonical)")
+    check_f32(from_dev(txt_s), ref_ts, "shifted text")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_mid_f32(gpu, D):
+    w = I.custom("mid_f32", 6, 30, 52, 2, 3, 3, 2, D, 37, "f32", index=201)
+    run_full(w, "shifted", check_f32)
+
+
+# ------------------------------------------------------------------ bfloat16
+MID = [  # (name, T, H, W, nt, nh, nw, heads, D, Lt)
+    ("mid_bf16", 6, 30, 52, 2, 3, 3, 3, 128, 40),
+    ("mid_bf16_d64", 6, 30, 52, 2, 3, 3, 3, 64, 40),
+    ("mid_bf16_notext", 6, 30, 52, 2, 3, 3, 2, 128, 0),
+    ("mid_bf16_text1", 6, 30, 52, 2, 3, 3, 2, 128, 1),
+    ("small_windows_bf16", 5, 24, 40, 3, 9, 12, 2, 128, 19),
+    ("one_window_bf16", 3, 12, 20, 1, 1, 1, 2, 128, 77),
+]
+
+
+@pytest.mark.parametrize("case", MID, ids=[c[0] for c in MID])
+@pytest.mark.parametrize("method", ["regular", "shifted"])
+def test_mid_bf16(gpu, case, method):
+    w = I.custom(*case, "bf16", index=300 + MID.index(case))
+    run_full(w, method, check_bf16)
+
+
+def test_bf16_unscaled_inputs(gpu):
+    """N(0,1) inputs give logits of standard deviation ~1 (the default
+    N(0,1)/sqrt(D) inputs give ~0.008, a nearly uniform softmax), which
+    stresses the running max and the exponentials."""
+    w = I.custom("mid_unscaled", 6, 30, 52, 2, 3, 3, 2, 128, 40, "bf16", std=1.0, index=320)
+    run_full(w, "regular", check_bf16)
+
+
+def test_bf16_explicit_scale(gpu):
+    w = I.custom("mid_scale", 6, 30, 52, 2, 3, 3, 2, 128, 40, "bf16", std=1.0, index=321)
+    run_full(w, "shifted", check_bf16, scale=0.05)
+
+
+def test_bf16_order_independent_and_deterministic(gpu):
+    """Results do not depend on the dispatch order, and repeat bit for bit."""
+    import torch
+    w = I.custom("mid_order", 6, 30, 52, 2, 3, 3, 3, 128, 40, "bf16", index=330)
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    p = W.Plan(*geo, W.SHIFTED)
+    d = upload(I.qkv(w), "bf16")
+    outs = []
+    for order in (W.ORDER_LPT_XCD, W.ORDER_LPT, W.ORDER_ID, W.ORDER_LPT_XCD):
+        W.set_attn_order(order)
+        o, t = W.window_attn(p, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"])
+        outs.append((o.clone(), t.clone()))
+    W.set_attn_order(W.ORDER_LPT_XCD)
+    torch.cuda.synchronize()
+    for o, t in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(t.view(torch.int16), outs[0][1].view(torch.int16))
+
+
+# ------------------------------------------------------------------ full-size, sampled
+def sampled_check(w, method, heads_full_text, n_samples=3, text_dtype=np.float64, q=None):
+    """Run the whole layer of workload w on the GPU; compare sampled
+    (window, head) video outputs and the complete text mean of the given
+    heads with the oracle computed window by window."""
+    import torch
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    om, wm = METH[method]
+    op, wp = O.plan(*geo, om), W.Plan(*geo, wm)
+    wc = W.canonical(*geo[:3])
+    log(f"  generating {w.name} inputs")
+    inp = I.qkv(w, bits_only=True)
+    d = upload(inp, "bf16")
+    qq, kk, vv = (W.relayout(d[n], wc, wp) for n in "qkv")
+    del d["q"], d["k"], d["v"]
+    out, txt = W.window_attn(wp, qq, kk, vv, d["txt_q"], d["txt_k"], d["txt_v"])
+    torch.cuda.synchronize()
+    bits = {n: inp[n][1] for n in I.QKV_NAMES}
+
+    def rows(name, idx, h):
+        return I.bf16_bits_to_f32(bits[name][idx, h]).astype(np.float64)
+
+    lpt = op.lpt
+    wins = sorted({int(lpt[0]), int(lpt[len(lpt) // 2]), int(lpt[-1])})[:n_samples]
+    heads = sorted({0, w.heads - 1})
+    for win in wins:
+        a, b = int(op.offsets[win]), int(op.offsets[win + 1])
+        ids = op.ids[a:b]
+        for h in heads:
+            ov, _ = O.joint_attention(rows("q", ids, h), rows("k", ids, h), rows("v", ids, h),
+                                      rows("txt_q", slice(None), h), rows("txt_k", slice(None), h),
+                                      rows("txt_v", slice(None), h))
+            check_bf16(from_dev(out[a:b, h]), ov, f"{w.name} {method} window {win} (L={b - a}) head {h}")
+    for h in heads_full_text:
+        acc = np.zeros((w.text_len, w.head_dim), dtype=text_dtype)
+        tq, tk, tv = (rows(n, slice(None), h) for n in ("txt_q", "txt_k", "txt_v"))
+        for win in range(op.n_windows):
+            ids = op.ids[op.offsets[win]:op.offsets[win + 1]]
+            _, ot = O.joint_attention(None, rows("k", ids, h), rows("v", ids, h), tq, tk, tv,
+                                      dtype=text_dtype, text_only=True)
+            acc += ot
+        check_bf16(from_dev(txt[:, h]), O.text_mean(acc, op.n_windows).astype(np.float64),
+                   f"{w.name} {method} text mean head {h} ({op.n_windows} windows)")
+    return out, txt
+
+
+def test_720p_regular_sampled(gpu):
+    sampled_check(I.WORKLOADS["720p_bf16"], "regular", heads_full_text=[0, 19])
+
+
+@pytest.mark.parametrize("method", ["regular", "shifted"])
+def test_1080p_sampled(gpu, method):
+    sampled_check(I.WORKLOADS["1080p_bf16"], method, heads_full_text=[7])
+
+
+@pytest.mark.timeout(900)
+def test_4k_shifted_sampled(gpu):
+    sampled_check(I.WORKLOADS["4k_bf16"], "shifted", heads_full_text=[3], text_dtype=np.float32)

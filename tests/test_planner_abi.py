@@ -1,0 +1,143 @@
+"""Host side of libwsp, no GPU needed: the C++ planner against the oracle
+(bit-exact tables), argument validation of the device entry points (all
+rejected before any HIP call), and the exported symbol set."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle as O
+import video_dit_window_amd as W
+import wsp_inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wsp.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wsp_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"wsp_plan", "wsp_relayout", "wsp_window_attn"} <= set(names)
+    lib = ctypes.CDLL(W.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert W.version() == 100
+
+
+def compare(geo, method):
+    o = O.plan(*geo, method) if method != O.CANONICAL else O.canonical_plan(*geo[:3])
+    p = W.Plan(*geo, method)
+    t = p.tables()
+    assert p.n_tokens == o.n_tokens and p.n_windows == o.n_windows
+    assert tuple(p.win_size) == tuple(o.win)
+    for name in ("offsets", "ids", "inv", "lpt"):
+        assert np.array_equal(t[name], getattr(o, name)), name
+    assert np.array_equal(t["boxes"], o.boxes)
+
+
+@pytest.mark.parametrize("name", list(I.WORKLOADS))
+@pytest.mark.parametrize("method", [O.REGULAR, O.SHIFTED])
+def test_planner_matches_oracle_on_workloads(name, method):
+    w = I.WORKLOADS[name]
+    compare((w.T, w.H, w.W, w.nt, w.nh, w.nw), method)
+
+
+@pytest.mark.parametrize("geo", [(5, 20, 36, 1, 1, 1), (31, 45, 80, 1, 3, 3), (40, 45, 80, 1, 3, 3),
+                                 (1, 75, 192, 1, 1, 1), (1, 25, 576, 1, 1, 1), (3, 9, 16, 2, 9, 16),
+                                 (12, 8, 12, 4, 60, 60), (1, 1, 1, 1, 1, 1), (2, 1, 300, 1, 1, 7)])
+@pytest.mark.parametrize("method", [O.REGULAR, O.SHIFTED, O.CANONICAL])
+def test_planner_matches_oracle_edge_geometries(geo, method):
+    compare(geo, method)
+
+
+@settings(max_examples=60, deadline=None)
+@given(T=st.integers(1, 40), H=st.integers(1, 80), Wd=st.integers(1, 80),
+       nt=st.integers(1, 8), nh=st.integers(1, 60), nw=st.integers(1, 60),
+       method=st.sampled_from([O.REGULAR, O.SHIFTED]))
+def test_planner_matches_oracle_random(T, H, Wd, nt, nh, nw, method):
+    try:
+        O.window_size(T, H, Wd, nt, nh, nw)
+    except ValueError:
+        with pytest.raises(W.WspError):
+            W.Plan(T, H, Wd, nt, nh, nw, method)
+        return
+    compare((T, H, Wd, nt, nh, nw), method)
+
+
+@pytest.mark.parametrize("bad", [(0, 4, 4, 1, 1, 1, 0), (2, -1, 4, 1, 1, 1, 0), (2, 4, 4, 0, 1, 1, 0),
+                                 (1, 1, 20000, 1, 1, 1, 0), (2, 4, 4, 1, 1, 1, 7)])
+def test_planner_rejects_invalid(bad):
+    with pytest.raises(W.WspError) as e:
+        W.Plan(*bad)
+    assert e.value.code == -1
+
+
+def test_planner_rejects_int32_overflow():
+    with pytest.raises(W.WspError) as e:
+        W.Plan(2048, 1024, 1024, 1, 1, 1, W.REGULAR)
+    assert e.value.code == -2
+
+
+# ------------------------------------------------ validation without a GPU
+def raw():
+    return W.lib()
+
+
+def test_relayout_argument_errors():
+    a = W.Plan(5, 20, 36, 2, 3, 3, W.REGULAR)
+    b = W.Plan(5, 20, 36, 2, 3, 3, W.SHIFTED)
+    c = W.Plan(5, 20, 35, 2, 3, 3, W.SHIFTED)
+    x, y = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
+    L = raw()
+    assert L.wsp_relayout(x, y, 256, a.handle, c.handle, None) == -1   # grids differ
+    assert L.wsp_relayout(x, y, 24, a.handle, b.handle, None) == -1    # row_bytes % 16
+    assert L.wsp_relayout(x, y, 0, a.handle, b.handle, None) == -1
+    assert L.wsp_relayout(None, y, 256, a.handle, b.handle, None) == -1
+    assert L.wsp_relayout(ctypes.c_void_p(0x1004), y, 256, a.handle, b.handle, None) == -1
+    assert L.wsp_relayout(x, x, 256, a.handle, b.handle, None) == -1
+    assert L.wsp_relayout(x, y, 256, None, b.handle, None) == -1
+    assert b"align" in L.wsp_last_error() or len(L.wsp_last_error()) > 0
+
+
+def test_window_attn_argument_errors():
+    p = W.Plan(5, 20, 36, 2, 3, 3, W.REGULAR)
+    L = raw()
+    a, b, c, o, t, ws = (ctypes.c_void_p(0x1000 * i) for i in range(1, 7))
+    args = dict(q=a, k=b, v=c, tq=a, tk=b, tv=c, H=4, D=64, Lt=16, dt=W.F32, sc=ctypes.c_float(0),
+                out=o, to=t, ws=ws, wsb=1 << 30)
+
+    def call(**kw):
+        d = dict(args, **kw)
+        return L.wsp_window_attn(p.handle, d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], d["H"],
+                                 d["D"], d["Lt"], d["dt"], d["sc"], d["out"], d["to"], d["ws"],
+                                 d["wsb"], None)
+
+    assert call(D=96) == -1
+    assert call(H=0) == -1
+    assert call(H=40000) == -1
+    assert call(dt=5) == -1
+    assert call(Lt=-1) == -1
+    assert call(q=None) == -1
+    assert call(k=ctypes.c_void_p(0x1008)) == -1
+    assert call(out=a) == -1                       # aliasing
+    assert call(tq=None) == -1                     # text needed when Lt > 0
+    assert call(wsb=16) == -4                      # workspace too small
+    assert call(ws=None) == -4
+    need = W.window_attn_workspace(p, 4, 64, 16, W.F32)
+    assert need == p.n_windows * 16 * 4 * 64 * 4
+    assert W.window_attn_workspace(p, 4, 64, 0, W.BF16) == 0
+
+
+def test_attn_order_option():
+    L = raw()
+    assert L.wsp_set_attn_order(7) == -1
+    for o in (W.ORDER_ID, W.ORDER_LPT, W.ORDER_LPT_XCD):
+        W.set_attn_order(o)

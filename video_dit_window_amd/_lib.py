@@ -1,0 +1,208 @@
+"""ctypes binding of libwsp.so (argument marshalling only).
+
+Every step of the layer runs inside libwsp's HIP kernels; this module only
+converts Python/torch arguments to the C ABI declared in include/wsp.h and
+allocates output tensors with torch (device memory plumbing).  There is no
+CPU fallback: if the library is missing the import of an entry point fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwsp.so")
+
+REGULAR, SHIFTED, CANONICAL = 0, 1, 2
+F32, BF16 = 0, 1
+ORDER_LPT_XCD, ORDER_LPT, ORDER_ID = 0, 1, 2
+METHODS = {"regular": REGULAR, "shifted": SHIFTED, "canonical": CANONICAL}
+
+_c_int, _c_i64, _c_sz, _c_vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+_i32p, _i64p, _szp = (ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
+                      ctypes.POINTER(ctypes.c_size_t))
+
+_SIGNATURES = {
+    "wsp_plan": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_vp)]),
+    "wsp_plan_info": (_c_int, [_c_vp, _i64p, _i32p, _i32p]),
+    "wsp_plan_tables": (_c_int, [_c_vp, _i32p, _i32p, _i32p, _i32p, _i32p]),
+    "wsp_plan_free": (None, [_c_vp]),
+    "wsp_relayout": (_c_int, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "wsp_window_attn_workspace": (_c_int, [_c_vp, _c_int, _c_int, _c_int, _c_int, _szp]),
+    "wsp_window_attn": (_c_int, [_c_vp] * 7 + [_c_int, _c_int, _c_int, _c_int, ctypes.c_float,
+                                                _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "wsp_set_attn_order": (_c_int, [_c_int]),
+    "wsp_last_error": (ctypes.c_char_p, []),
+    "wsp_version": (_c_int, []),
+}
+
+_lib = None
+
+
+class WspError(RuntimeError):
+    """A libwsp call returned an error status."""
+
+    def __init__(self, name, code, msg):
+        super().__init__(f"{name} failed ({code}): {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libwsp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m video_dit_window_amd.build` (no CPU fallback exists)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = l
+    return _lib
+
+
+def _check(name, rc):
+    if rc != 0:
+        raise WspError(name, rc, lib().wsp_last_error().decode())
+
+
+def _i32(a):
+    return a.ctypes.data_as(_i32p)
+
+
+class Plan:
+    """A window layout (owns a wsp_plan_t)."""
+
+    def __init__(self, T, H, W, nt=1, nh=1, nw=1, method=REGULAR):
+        if isinstance(method, str):
+            method = METHODS[method]
+        h = _c_vp()
+        _check("wsp_plan", lib().wsp_plan(T, H, W, nt, nh, nw, method, ctypes.byref(h)))
+        self._h = h
+        self.T, self.H, self.W, self.nt, self.nh, self.nw, self.method = T, H, W, nt, nh, nw, method
+        n, nwin, win = ctypes.c_int64(), ctypes.c_int32(), (ctypes.c_int32 * 3)()
+        _check("wsp_plan_info", lib().wsp_plan_info(h, ctypes.byref(n), ctypes.byref(nwin), win))
+        self.n_tokens, self.n_windows, self.win_size = n.value, nwin.value, tuple(win)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def tables(self):
+        """Host copies of offsets, ids, inv, boxes [nwin, 6], lpt (int32)."""
+        n, nw = self.n_tokens, self.n_windows
+        t = {"offsets": np.empty(nw + 1, np.int32), "ids": np.empty(n, np.int32),
+             "inv": np.empty(n, np.int32), "boxes": np.empty((nw, 6), np.int32),
+             "lpt": np.empty(nw, np.int32)}
+        _check("wsp_plan_tables", lib().wsp_plan_tables(
+            self._h, _i32(t["offsets"]), _i32(t["ids"]), _i32(t["inv"]), _i32(t["boxes"]),
+            _i32(t["lpt"])))
+        return t
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.wsp_plan_free(h)
+            self._h = None
+
+
+def plan(T, H, W, nt, nh, nw, method) -> Plan:
+    return Plan(T, H, W, nt, nh, nw, method)
+
+
+def canonical(T, H, W) -> Plan:
+    return Plan(T, H, W, 1, 1, 1, CANONICAL)
+
+
+# ---------------------------------------------------------------- device calls
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _c_vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev_ptr(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _c_vp(t.data_ptr())
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def relayout(x, src: Plan, dst: Plan, out=None, stream=None):
+    """y[j] = x[rows of src holding dst's token j] (whole rows, bytes unchanged)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    row_bytes = x[0].numel() * x.element_size() if x.shape[0] else 0
+    if x.shape[0] != src.n_tokens or out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("x/out shape does not match the plans")
+    _check("wsp_relayout", lib().wsp_relayout(_dev_ptr(x, "x"), _dev_ptr(out, "out"), row_bytes,
+                                              src.handle, dst.handle, _stream(stream)))
+    return out
+
+
+def window_attn_workspace(p: Plan, n_heads, head_dim, text_len, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    b = ctypes.c_size_t()
+    _check("wsp_window_attn_workspace",
+           lib().wsp_window_attn_workspace(p.handle, n_heads, head_dim, text_len, code, ctypes.byref(b)))
+    return b.value
+
+
+def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None, out=None, txt_out=None,
+                workspace=None, stream=None):
+    """Joint window attention; returns (out [N,H,D], txt_out [Lt,H,D])."""
+    torch = _torch()
+    N, Hh, D = q.shape
+    Lt = txt_q.shape[0]
+    code = _dtype_code(q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    for name, t in (("txt_k", txt_k), ("txt_v", txt_v)):
+        if t.shape != txt_q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match txt_q in shape and q in dtype")
+    if txt_q.shape[1:] != (Hh, D) or N != p.n_tokens:
+        raise ValueError("shapes do not match the plan / each other")
+    if out is None:
+        out = torch.empty_like(q)
+    if txt_out is None:
+        txt_out = torch.empty_like(txt_q)
+    need = window_attn_workspace(p, Hh, D, Lt, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    tp = [(_dev_ptr(t, n) if Lt else _c_vp(0)) for n, t in
+          (("txt_q", txt_q), ("txt_k", txt_k), ("txt_v", txt_v), ("txt_out", txt_out))]
+    _check("wsp_window_attn", lib().wsp_window_attn(
+        p.handle, _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), tp[0], tp[1], tp[2],
+        Hh, D, Lt, code, ctypes.c_float(0.0 if scale is None else float(scale)),
+        _dev_ptr(out, "out"), tp[3], _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)))
+    return out, txt_out
+
+
+def set_attn_order(order: int):
+    _check("wsp_set_attn_order", lib().wsp_set_attn_order(order))
+
+
+def version() -> int:
+    return lib().wsp_version()

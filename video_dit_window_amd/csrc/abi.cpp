@@ -1,0 +1,293 @@
+// C entry points of libwsp: argument validation, per-device table caches and
+// kernel dispatch.  See include/wsp.h for the contract of each call.
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "wsp_internal.h"
+
+namespace wsp {
+
+namespace {
+thread_local std::string g_last_error;
+std::atomic<int> g_attn_order{WSP_ORDER_LPT_XCD};
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+std::tuple<int, int, int, int> layout_key(const wsp_plan_t &p) {
+    if (p.method == WSP_CANONICAL) return {WSP_CANONICAL, 0, 0, 0};
+    return {p.method, p.nt, p.nh, p.nw};
+}
+
+template <typename T>
+int upload(const T *host, size_t count, T **dev_out) {
+    T *d = nullptr;
+    const size_t bytes = std::max<size_t>(count, 1) * sizeof(T);
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(&d), bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(e == hipErrorOutOfMemory ? WSP_ENOMEM : WSP_EDEVICE,
+                    std::string("hipMalloc of a plan table failed: ") + hipGetErrorString(e));
+    }
+    if (count) {
+        e = hipMemcpy(d, host, count * sizeof(T), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            (void)hipFree(d);
+            return hip_fail(e, "hipMemcpy of a plan table");
+        }
+    }
+    *dev_out = d;
+    return WSP_OK;
+}
+
+}  // namespace
+
+int fail(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(WSP_EDEVICE, std::string(what) + " failed: " + hipGetErrorString(e));
+}
+
+int device_offsets(wsp_plan_t &p, int dev, int32_t **out) {
+    std::lock_guard<std::mutex> lk(p.mu);
+    DeviceTables &t = p.dev[dev];
+    if (!t.offsets) {
+        int rc = upload(p.offsets.data(), p.offsets.size(), &t.offsets);
+        if (rc) return rc;
+    }
+    *out = t.offsets;
+    return WSP_OK;
+}
+
+int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out) {
+    const auto key = layout_key(src);
+    {
+        std::lock_guard<std::mutex> lk(dst.mu);
+        auto &m = dst.dev[dev].perm;
+        auto it = m.find(key);
+        if (it != m.end()) {
+            *out = it->second;
+            return WSP_OK;
+        }
+    }
+    std::vector<int32_t> perm;
+    try {
+        relayout_perm(src, dst, perm);
+    } catch (const std::bad_alloc &) {
+        return fail(WSP_ENOMEM, "host allocation of a relayout permutation failed");
+    }
+    int32_t *d = nullptr;
+    int rc = upload(perm.data(), perm.size(), &d);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lk(dst.mu);
+    auto &m = dst.dev[dev].perm;
+    auto ins = m.emplace(key, d);
+    if (!ins.second) (void)hipFree(d);  // another thread uploaded it first
+    *out = ins.first->second;
+    return WSP_OK;
+}
+
+int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
+                 Item **out, int *count) {
+    const auto key = std::make_tuple(n_heads, text_len, bm, order);
+    {
+        std::lock_guard<std::mutex> lk(p.mu);
+        auto &m = p.dev[dev].items;
+        auto it = m.find(key);
+        if (it != m.end()) {
+            *out = it->second.first;
+            *count = it->second.second;
+            return WSP_OK;
+        }
+    }
+    std::vector<Item> items;
+    int rc;
+    try {
+        rc = build_items(p, n_heads, text_len, bm, order, items);
+    } catch (const std::bad_alloc &) {
+        return fail(WSP_ENOMEM, "host allocation of the attention work list failed");
+    }
+    if (rc < 0) return rc;
+    Item *d = nullptr;
+    rc = upload(items.data(), items.size(), &d);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lk(p.mu);
+    auto &m = p.dev[dev].items;
+    auto ins = m.emplace(key, std::make_pair(d, int(items.size())));
+    if (!ins.second) (void)hipFree(d);
+    *out = ins.first->second.first;
+    *count = ins.first->second.second;
+    return WSP_OK;
+}
+
+}  // namespace wsp
+
+using namespace wsp;
+
+extern "C" {
+
+const char *wsp_last_error(void) { return g_last_error.c_str(); }
+
+int wsp_version(void) { return WSP_VERSION; }
+
+int wsp_plan(int T, int H, int W, int nt, int nh, int nw, int method, wsp_plan_t **out) {
+    g_last_error.clear();
+    if (!out) return fail(WSP_EINVAL, "out is NULL");
+    *out = nullptr;
+    wsp_plan_t *p = new (std::nothrow) wsp_plan_t;
+    if (!p) return fail(WSP_ENOMEM, "plan allocation failed");
+    int rc = build_plan(T, H, W, nt, nh, nw, method, *p);
+    if (rc) {
+        delete p;
+        return rc;
+    }
+    *out = p;
+    return WSP_OK;
+}
+
+int wsp_plan_info(const wsp_plan_t *p, int64_t *n_tokens, int32_t *n_windows, int32_t *win_size) {
+    g_last_error.clear();
+    if (!p) return fail(WSP_EINVAL, "plan is NULL");
+    if (n_tokens) *n_tokens = p->n;
+    if (n_windows) *n_windows = p->nwin;
+    if (win_size) {
+        win_size[0] = p->wt;
+        win_size[1] = p->wh;
+        win_size[2] = p->ww;
+    }
+    return WSP_OK;
+}
+
+int wsp_plan_tables(const wsp_plan_t *p, int32_t *offsets, int32_t *ids, int32_t *inv,
+                    int32_t *boxes, int32_t *lpt) {
+    g_last_error.clear();
+    if (!p) return fail(WSP_EINVAL, "plan is NULL");
+    if (offsets) std::memcpy(offsets, p->offsets.data(), p->offsets.size() * 4);
+    if (ids) std::memcpy(ids, p->ids.data(), p->ids.size() * 4);
+    if (inv) std::memcpy(inv, p->inv.data(), p->inv.size() * 4);
+    if (boxes) std::memcpy(boxes, p->boxes.data(), p->boxes.size() * 4);
+    if (lpt) std::memcpy(lpt, p->lpt.data(), p->lpt.size() * 4);
+    return WSP_OK;
+}
+
+void wsp_plan_free(wsp_plan_t *p) {
+    if (!p) return;
+    int cur = -1;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (auto &kv : p->dev) {
+        if (hipSetDevice(kv.first) != hipSuccess) continue;
+        DeviceTables &t = kv.second;
+        if (t.offsets) (void)hipFree(t.offsets);
+        for (auto &pm : t.perm) (void)hipFree(pm.second);
+        for (auto &it : t.items) (void)hipFree(it.second.first);
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+    delete p;
+}
+
+int wsp_relayout(const void *x, void *y, int64_t row_bytes, const wsp_plan_t *src,
+                 const wsp_plan_t *dst, void *stream) {
+    g_last_error.clear();
+    if (!src || !dst) return fail(WSP_EINVAL, "plan is NULL");
+    if (src->T != dst->T || src->H != dst->H || src->W != dst->W)
+        return fail(WSP_EINVAL, "relayout between plans of different grids");
+    if (row_bytes <= 0 || row_bytes % 16)
+        return fail(WSP_EINVAL, "row_bytes must be a positive multiple of 16, got " +
+                                    std::to_string(row_bytes));
+    if (!x || !y) return fail(WSP_EINVAL, "x or y is NULL");
+    if (!aligned16(x) || !aligned16(y)) return fail(WSP_EINVAL, "x and y must be 16-byte aligned");
+    if (x == y) return fail(WSP_EINVAL, "x and y must not alias");
+    if (row_bytes > (int64_t(1) << 40) / std::max<int64_t>(dst->n, 1))
+        return fail(WSP_ERANGE, "n_tokens * row_bytes too large");
+    int dev = 0;
+    WSP_HIP(hipGetDevice(&dev));
+    int32_t *perm = nullptr;
+    int rc = device_perm(*src, *const_cast<wsp_plan_t *>(dst), dev, &perm);
+    if (rc) return rc;
+    hipError_t e = launch_relayout(x, y, perm, dst->n, row_bytes, hipStream_t(stream));
+    if (e != hipSuccess) return hip_fail(e, "relayout kernel launch");
+    return WSP_OK;
+}
+
+int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, int text_len,
+                              int dtype, size_t *bytes) {
+    g_last_error.clear();
+    if (!p || !bytes) return fail(WSP_EINVAL, "plan or bytes is NULL");
+    if (n_heads < 1 || n_heads > 32767) return fail(WSP_EINVAL, "n_heads must be in 1..32767");
+    if (head_dim != 64 && head_dim != 128) return fail(WSP_EINVAL, "head_dim must be 64 or 128");
+    if (text_len < 0) return fail(WSP_EINVAL, "text_len must be >= 0");
+    if (dtype != WSP_F32 && dtype != WSP_BF16) return fail(WSP_EINVAL, "unknown dtype");
+    const double b = double(p->nwin) * text_len * n_heads * head_dim * 4.0;
+    if (b > 9e18) return fail(WSP_ERANGE, "workspace size overflows");
+    *bytes = size_t(p->nwin) * size_t(text_len) * size_t(n_heads) * size_t(head_dim) * 4u;
+    return WSP_OK;
+}
+
+int wsp_window_attn(const wsp_plan_t *pc, const void *q, const void *k, const void *v,
+                    const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                    int head_dim, int text_len, int dtype, float scale, void *out,
+                    void *txt_out, void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error.clear();
+    size_t need = 0;
+    int rc = wsp_window_attn_workspace(pc, n_heads, head_dim, text_len, dtype, &need);
+    if (rc) return rc;
+    wsp_plan_t *p = const_cast<wsp_plan_t *>(pc);
+    for (const void *ptr : {q, k, v, static_cast<const void *>(out)}) {
+        if (!ptr) return fail(WSP_EINVAL, "q, k, v and out must be non-NULL");
+        if (!aligned16(ptr)) return fail(WSP_EINVAL, "q, k, v and out must be 16-byte aligned");
+    }
+    if (out == q || out == k || out == v) return fail(WSP_EINVAL, "out must not alias q, k or v");
+    if (text_len > 0) {
+        for (const void *ptr : {txt_q, txt_k, txt_v, static_cast<const void *>(txt_out)}) {
+            if (!ptr) return fail(WSP_EINVAL, "text tensors and txt_out must be non-NULL when text_len > 0");
+            if (!aligned16(ptr)) return fail(WSP_EINVAL, "text tensors must be 16-byte aligned");
+        }
+        if (!workspace || workspace_bytes < need)
+            return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) +
+                                            " bytes required, got " + std::to_string(workspace_bytes));
+        if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
+    }
+    if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
+    const int order = g_attn_order.load();
+    const int bm = dtype == WSP_BF16 ? attn_bf16_tile_m(head_dim) : attn_f32_tile_m(head_dim);
+
+    int dev = 0;
+    WSP_HIP(hipGetDevice(&dev));
+    int32_t *d_off = nullptr;
+    if ((rc = device_offsets(*p, dev, &d_off))) return rc;
+    Item *items = nullptr;
+    int n_items = 0;
+    if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, &items, &n_items))) return rc;
+    hipStream_t s = hipStream_t(stream);
+    float *ws = static_cast<float *>(workspace);
+    hipError_t e;
+    if (dtype == WSP_BF16)
+        e = launch_attn_bf16(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, items,
+                             n_items, n_heads, text_len, scale, s);
+    else
+        e = launch_attn_f32(head_dim, static_cast<const float *>(q), static_cast<const float *>(k),
+                            static_cast<const float *>(v), static_cast<const float *>(txt_q),
+                            static_cast<const float *>(txt_k), static_cast<const float *>(txt_v),
+                            static_cast<float *>(out), ws, d_off, items, n_items, n_heads,
+                            text_len, scale, s);
+    if (e != hipSuccess) return hip_fail(e, "window attention kernel launch");
+    if (text_len > 0) {
+        e = launch_text_mean(ws, txt_out, int64_t(text_len) * n_heads * head_dim, p->nwin, dtype, s);
+        if (e != hipSuccess) return hip_fail(e, "text mean kernel launch");
+    }
+    return WSP_OK;
+}
+
+int wsp_set_attn_order(int order) {
+    g_last_error.clear();
+    if (order != WSP_ORDER_LPT_XCD && order != WSP_ORDER_LPT && order != WSP_ORDER_ID)
+        return fail(WSP_EINVAL, "unknown attention order " + std::to_string(order));
+    g_attn_order.store(order);
+    return WSP_OK;
+}
+
+}  // extern "C"

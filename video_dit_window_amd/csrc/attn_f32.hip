@@ -1,0 +1,149 @@
+// Float32 window joint attention (vector ALU, float32 throughout).
+//
+// "Window-Aligned Sequence Parallelism (SeedVR2)", section "SeedVR2
+// integration": each window attends over the packed segment
+// [video window; replicated text].  "Parallelize new models with USP (text
+// replica)", section "3. Attention with USP": plain SDPA, no mask, no dropout.
+//
+// One work group = one (window, head, 64-query tile) of the joint sequence
+// Q = [q_window; txt_q].  Four lanes share a query, each holding a quarter of
+// the head dimension (element d = 16*e + 4*sub + 0..3 for lane `sub`), so a
+// K/V row read from LDS is one 64-byte broadcast per quarter.  Keys stream
+// through LDS in tiles of 32 rows with an online (running max) softmax.
+// Video query rows write `out`; text query rows write their normalised
+// output T_w to the float32 workspace, reduced later in window order.
+
+#include "wsp_internal.h"
+
+namespace wsp {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 64;       // queries per work group
+constexpr int kBN = 32;       // keys per LDS tile
+constexpr int kThreads = 256; // 4 lanes per query
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ tq, const float *__restrict__ tk, const float *__restrict__ tv,
+    float *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
+    const Item *__restrict__ items, int H, int Lt, float scale) {
+    constexpr int E = D / 16;  // float4 groups per lane
+    __shared__ f32x4 Ks[kBN][D / 4];
+    __shared__ f32x4 Vs[kBN][D / 4];
+
+    const Item it = items[blockIdx.x];
+    if (it.x < 0) return;
+    const int w = it.x, h = it.y >> 16, qt = it.y & 0xFFFF;
+    const int64_t off = offsets[w];
+    const int Lw = offsets[w + 1] - int(off);
+    const int M = Lw + Lt;
+    const int64_t rs = int64_t(H) * D;  // row stride (elements)
+    const int tid = threadIdx.x, sub = tid & 3, qi = tid >> 2;
+    const int qrow = qt * kBM + qi;
+
+    // Query row (zeros past the end of the joint sequence).
+    f32x4 qv[E], o[E];
+    const float *qp = nullptr;
+    if (qrow < Lw) qp = q + (off + qrow) * rs + int64_t(h) * D;
+    else if (qrow < M) qp = tq + int64_t(qrow - Lw) * rs + int64_t(h) * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        qv[e] = qp ? *reinterpret_cast<const f32x4 *>(qp + 16 * e + 4 * sub) : f32x4{0, 0, 0, 0};
+        o[e] = f32x4{0, 0, 0, 0};
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int ntiles = (M + kBN - 1) / kBN;
+    for (int j = 0; j < ntiles; ++j) {
+        __syncthreads();
+        // Stage K and V rows j*32 .. j*32+31 (video rows, then text rows).
+        for (int c = tid; c < kBN * (D / 4); c += kThreads) {
+            const int r = c / (D / 4), col = c % (D / 4);
+            const int kr = j * kBN + r;
+            f32x4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+            if (kr < Lw) {
+                const int64_t o_ = (off + kr) * rs + int64_t(h) * D + 4 * col;
+                kk = *reinterpret_cast<const f32x4 *>(k + o_);
+                vv = *reinterpret_cast<const f32x4 *>(v + o_);
+            } else if (kr < M) {
+                const int64_t o_ = int64_t(kr - Lw) * rs + int64_t(h) * D + 4 * col;
+                kk = *reinterpret_cast<const f32x4 *>(tk + o_);
+                vv = *reinterpret_cast<const f32x4 *>(tv + o_);
+            }
+            Ks[r][col] = kk;
+            Vs[r][col] = vv;
+        }
+        __syncthreads();
+
+        float s[kBN];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < kBN; ++kk) {
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const f32x4 kv = Ks[kk][4 * e + sub];
+                acc = fmaf(qv[e].x, kv.x, acc);
+                acc = fmaf(qv[e].y, kv.y, acc);
+                acc = fmaf(qv[e].z, kv.z, acc);
+                acc = fmaf(qv[e].w, kv.w, acc);
+            }
+            acc += __shfl_xor(acc, 1);
+            acc += __shfl_xor(acc, 2);
+            s[kk] = (j * kBN + kk < M) ? acc * scale : -INFINITY;
+            mx = fmaxf(mx, s[kk]);
+        }
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = expf(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int kk = 0; kk < kBN; ++kk) {
+            const float p = expf(s[kk] - m_new);
+            l_run += p;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const f32x4 vv = Vs[kk][4 * e + sub];
+                o[e].x = fmaf(p, vv.x, o[e].x);
+                o[e].y = fmaf(p, vv.y, o[e].y);
+                o[e].z = fmaf(p, vv.z, o[e].z);
+                o[e].w = fmaf(p, vv.w, o[e].w);
+            }
+        }
+        m_run = m_new;
+    }
+
+    if (qrow >= M) return;
+    const float inv = 1.0f / l_run;
+    float *dst = (qrow < Lw) ? out + (off + qrow) * rs + int64_t(h) * D
+                             : ws + ((int64_t(w) * Lt + (qrow - Lw)) * H + h) * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) *reinterpret_cast<f32x4 *>(dst + 16 * e + 4 * sub) = o[e] * inv;
+}
+
+}  // namespace
+
+int attn_f32_tile_m(int) { return kBM; }
+
+hipError_t launch_attn_f32(int head_dim, const float *q, const float *k, const float *v,
+                           const float *tq, const float *tk, const float *tv, float *out,
+                           float *ws, const int32_t *offsets, const Item *items, int n_items,
+                           int n_heads, int text_len, float scale, hipStream_t s) {
+    if (n_items <= 0) return hipSuccess;
+    if (head_dim == 128)
+        attn_f32_kernel<128><<<dim3(n_items), dim3(kThreads), 0, s>>>(
+            q, k, v, tq, tk, tv, out, ws, offsets, items, n_heads, text_len, scale);
+    else if (head_dim == 64)
+        attn_f32_kernel<64><<<dim3(n_items), dim3(kThreads), 0, s>>>(
+            q, k, v, tq, tk, tv, out, ws, offsets, items, n_heads, text_len, scale);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace wsp

@@ -1,0 +1,167 @@
+// Host planner: window geometry, layout tables, relayout permutations and the
+// ordered work list of the attention kernels.
+//
+// Window rule and layouts: "Window-Aligned Sequence Parallelism (SeedVR2)",
+// section "Window layouts".  Largest-first order: same page, section "Planner".
+
+#include <algorithm>
+#include <cmath>
+#include <numeric>
+
+#include "wsp_internal.h"
+
+namespace wsp {
+
+namespace {
+
+// The temporal extent entering the size rule is capped at 30 frames.
+constexpr int kMaxTemporalWindow = 30;
+
+struct Interval {
+    int a, b;
+};
+
+// Cuts of one axis of length n with window w.  Regular: [i*w, min((i+1)*w, n)).
+// Shifted: every cut moves back by floor(w/2) and is clipped to [0, n]; the
+// first interval is therefore ceil(w/2) long and no interval wraps.
+void axis_cuts(int n, int w, int method, std::vector<Interval> &out) {
+    out.clear();
+    const int64_t s = (method == WSP_SHIFTED) ? w / 2 : 0;
+    for (int64_t i = 0; i * w - s < n; ++i) {
+        const int64_t a = std::max<int64_t>(i * w - s, 0);
+        const int64_t b = std::min<int64_t>((i + 1) * w - s, n);
+        if (b > a) out.push_back({int(a), int(b)});
+    }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int build_plan(int T, int H, int W, int nt, int nh, int nw, int method, wsp_plan_t &p) {
+    if (T <= 0 || H <= 0 || W <= 0)
+        return fail(WSP_EINVAL, "grid extents must be positive (T=" + std::to_string(T) +
+                                    ", H=" + std::to_string(H) + ", W=" + std::to_string(W) + ")");
+    if (method != WSP_REGULAR && method != WSP_SHIFTED && method != WSP_CANONICAL)
+        return fail(WSP_EINVAL, "unknown window method " + std::to_string(method));
+    const int64_t n = int64_t(T) * H * W;
+    if (n >= (int64_t(1) << 31))
+        return fail(WSP_ERANGE, "T*H*W = " + std::to_string(n) + " does not fit int32 token ids");
+    p.T = T; p.H = H; p.W = W; p.nt = nt; p.nh = nh; p.nw = nw; p.method = method;
+    p.n = n;
+
+    std::vector<Interval> ti, hi, wi;
+    if (method == WSP_CANONICAL) {
+        p.wt = T; p.wh = H; p.ww = W;
+        ti = {{0, T}}; hi = {{0, H}}; wi = {{0, W}};
+    } else {
+        if (nt <= 0 || nh <= 0 || nw <= 0)
+            return fail(WSP_EINVAL, "window counts nt, nh, nw must be positive");
+        // Size rule, evaluated in IEEE double like the page's Python:
+        // scale = sqrt(45*80 / (H*W)); round() ties to even (nearbyint under
+        // the default rounding mode).
+        const double scale = std::sqrt(3600.0 / (double(H) * double(W)));
+        const double rh = std::nearbyint(double(H) * scale);
+        const double rw = std::nearbyint(double(W) * scale);
+        if (!(rh >= 1.0) || !(rw >= 1.0))
+            return fail(WSP_EINVAL, "window size rounds to zero for H=" + std::to_string(H) +
+                                        ", W=" + std::to_string(W));
+        if (rh > 2e9 || rw > 2e9) return fail(WSP_ERANGE, "rescaled grid too large");
+        p.wh = int(ceil_div(int64_t(rh), nh));
+        p.ww = int(ceil_div(int64_t(rw), nw));
+        p.wt = int(ceil_div(std::min(T, kMaxTemporalWindow), nt));
+        axis_cuts(T, p.wt, method, ti);
+        axis_cuts(H, p.wh, method, hi);
+        axis_cuts(W, p.ww, method, wi);
+    }
+
+    const size_t nwin = ti.size() * hi.size() * wi.size();
+    try {
+        p.offsets.assign(1, 0);
+        p.offsets.reserve(nwin + 1);
+        p.boxes.clear();
+        p.boxes.reserve(6 * nwin);
+        p.ids.resize(size_t(n));
+        p.inv.resize(size_t(n));
+        p.lpt.resize(nwin);
+    } catch (const std::bad_alloc &) {
+        return fail(WSP_ENOMEM, "host allocation of plan tables failed");
+    }
+    // w outermost, t innermost; row-major (t, h, w) inside each box.
+    int64_t pos = 0;
+    for (const Interval &iw : wi)
+        for (const Interval &ih : hi)
+            for (const Interval &it : ti) {
+                p.boxes.insert(p.boxes.end(), {it.a, it.b, ih.a, ih.b, iw.a, iw.b});
+                for (int t = it.a; t < it.b; ++t)
+                    for (int h = ih.a; h < ih.b; ++h) {
+                        const int64_t row = (int64_t(t) * H + h) * W;
+                        for (int w = iw.a; w < iw.b; ++w) {
+                            p.ids[size_t(pos)] = int32_t(row + w);
+                            p.inv[size_t(row + w)] = int32_t(pos);
+                            ++pos;
+                        }
+                    }
+                p.offsets.push_back(int32_t(pos));
+            }
+    p.nwin = int32_t(nwin);
+    // Largest first, ties by window id.
+    std::iota(p.lpt.begin(), p.lpt.end(), 0);
+    std::stable_sort(p.lpt.begin(), p.lpt.end(), [&](int32_t a, int32_t b) {
+        const int32_t la = p.offsets[a + 1] - p.offsets[a], lb = p.offsets[b + 1] - p.offsets[b];
+        return la > lb;
+    });
+    return WSP_OK;
+}
+
+void relayout_perm(const wsp_plan_t &src, const wsp_plan_t &dst, std::vector<int32_t> &perm) {
+    // Destination row j holds canonical token dst.ids[j], found at src.inv[...].
+    perm.resize(size_t(dst.n));
+    for (int64_t j = 0; j < dst.n; ++j) perm[size_t(j)] = src.inv[size_t(dst.ids[size_t(j)])];
+}
+
+int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order,
+                std::vector<Item> &items) {
+    constexpr int kXcds = 8;
+    std::vector<int32_t> worder(size_t(p.nwin));
+    if (order == WSP_ORDER_ID)
+        std::iota(worder.begin(), worder.end(), 0);
+    else
+        worder = p.lpt;
+    items.clear();
+    auto tiles_of = [&](int32_t w) {
+        return ceil_div(int64_t(p.offsets[w + 1] - p.offsets[w]) + text_len, bm);
+    };
+    for (int32_t w : worder)
+        if (tiles_of(w) > 0xFFFF)
+            return fail(WSP_ERANGE, "window " + std::to_string(w) + " needs more than 65535 query tiles");
+    if (order != WSP_ORDER_LPT_XCD) {
+        for (int32_t w : worder)
+            for (int h = 0; h < n_heads; ++h)
+                for (int64_t t = 0; t < tiles_of(w); ++t) items.push_back({w, (h << 16) | int(t)});
+        return int(items.size());
+    }
+    // Work groups are handed to the XCDs round-robin by block index, so block
+    // b runs on XCD b % 8.  Each (window, head) group -- whose query tiles all
+    // read the same K/V -- goes whole to the least-loaded XCD (largest group
+    // first), and each XCD's list keeps the largest-first order.
+    std::vector<std::vector<Item>> lists(kXcds);
+    std::vector<int64_t> load(kXcds, 0);
+    for (int32_t w : worder) {
+        const int64_t tiles = tiles_of(w);
+        const int64_t cost = tiles * (int64_t(p.offsets[w + 1] - p.offsets[w]) + text_len);
+        for (int h = 0; h < n_heads; ++h) {
+            const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
+            for (int64_t t = 0; t < tiles; ++t) lists[x].push_back({w, (h << 16) | int(t)});
+            load[x] += cost;
+        }
+    }
+    size_t longest = 0;
+    for (auto &l : lists) longest = std::max(longest, l.size());
+    items.assign(longest * kXcds, Item{-1, 0});
+    for (int x = 0; x < kXcds; ++x)
+        for (size_t s = 0; s < lists[x].size(); ++s) items[s * kXcds + x] = lists[x][s];
+    return int(items.size());
+}
+
+}  // namespace wsp

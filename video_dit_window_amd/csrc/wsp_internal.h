@@ -1,0 +1,84 @@
+// Internal declarations of libwsp: the plan object, host table builders and
+// the kernel launchers.  Not part of the public ABI (include/wsp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "wsp.h"
+
+namespace wsp {
+
+// Work item of the attention kernels: x = window id (-1: nothing to do),
+// y = (head << 16) | query tile.
+using Item = int2;
+
+struct DeviceTables {
+    int32_t *offsets = nullptr;                                 // [n_windows + 1]
+    std::map<std::tuple<int, int, int, int>, int32_t *> perm;   // src layout -> perm
+    std::map<std::tuple<int, int, int, int>, std::pair<Item *, int>> items;  // (H, Lt, BM, order)
+};
+
+}  // namespace wsp
+
+struct wsp_plan_t {
+    int T = 0, H = 0, W = 0, nt = 0, nh = 0, nw = 0, method = 0;
+    int wt = 0, wh = 0, ww = 0;
+    int64_t n = 0;
+    int32_t nwin = 0;
+    std::vector<int32_t> offsets, ids, inv, boxes, lpt;
+    std::mutex mu;                               // guards dev
+    std::map<int, wsp::DeviceTables> dev;        // per device ordinal
+};
+
+namespace wsp {
+
+// ---- errors --------------------------------------------------------------
+int fail(int code, const std::string &msg);
+int hip_fail(hipError_t e, const char *what);
+#define WSP_HIP(call)                                   \
+    do {                                                \
+        hipError_t e_ = (call);                         \
+        if (e_ != hipSuccess) return hip_fail(e_, #call); \
+    } while (0)
+
+// ---- host planner (plan.cpp) ---------------------------------------------
+int build_plan(int T, int H, int W, int nt, int nh, int nw, int method, wsp_plan_t &p);
+void relayout_perm(const wsp_plan_t &src, const wsp_plan_t &dst, std::vector<int32_t> &perm);
+// Attention work list; returns the grid size (items.size()).
+int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order,
+                std::vector<Item> &items);
+
+// ---- device tables (abi.cpp) ----------------------------------------------
+int device_offsets(wsp_plan_t &p, int dev, int32_t **out);
+int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out);
+int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
+                 Item **out, int *count);
+
+// ---- kernel launchers -------------------------------------------------------
+// relayout.hip
+hipError_t launch_relayout(const void *x, void *y, const int32_t *perm, int64_t n_rows,
+                           int64_t row_bytes, hipStream_t s);
+// attn_bf16.hip: returns the query-tile height used by the bf16 kernel
+int attn_bf16_tile_m(int head_dim);
+hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
+                            const void *tq, const void *tk, const void *tv, void *out,
+                            float *ws, const int32_t *offsets, const Item *items, int n_items,
+                            int n_heads, int text_len, float scale, hipStream_t s);
+// attn_f32.hip
+int attn_f32_tile_m(int head_dim);
+hipError_t launch_attn_f32(int head_dim, const float *q, const float *k, const float *v,
+                           const float *tq, const float *tk, const float *tv, float *out,
+                           float *ws, const int32_t *offsets, const Item *items, int n_items,
+                           int n_heads, int text_len, float scale, hipStream_t s);
+// text_mean.hip
+hipError_t launch_text_mean(const float *ws, void *txt_out, int64_t per_window, int n_windows,
+                            int dtype, hipStream_t s);
+
+}  // namespace wsp

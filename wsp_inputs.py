@@ -110,30 +110,35 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def tensor(w: Workload, i: int, shape, seed=0, std=None):
+def tensor(w: Workload, i: int, shape, seed=0, std=None, bits_only=False):
     """Tensor ``i`` of workload ``w``.
 
     Returns (values_f32, bits) where bits is the uint16 bfloat16 pattern (or
     None for float32 workloads) and values_f32 holds exactly the values the
-    device will see.
+    device will see.  With ``bits_only`` (bf16 workloads) values_f32 is None;
+    widen rows on demand with bf16_bits_to_f32.
     """
     x = normal_f32(shape, [seed, w.index, i], w.std if std is None else std)
     if w.dtype == "bf16":
         bits = f32_to_bf16_bits(x)
-        return bf16_bits_to_f32(bits), bits
+        del x
+        return (None if bits_only else bf16_bits_to_f32(bits)), bits
     return x, None
 
 
-def qkv(w: Workload, seed=0, n_tokens=None):
+QKV_NAMES = ("q", "k", "v", "txt_q", "txt_k", "txt_v")
+
+
+def qkv(w: Workload, seed=0, n_tokens=None, bits_only=False):
     """Canonical-order q, k, v [N, heads, D] and txt_q/k/v [Lt, heads, D].
 
-    Returns a dict name -> (values_f32, bits_or_None)."""
+    Returns a dict name -> (values_f32 or None, bits or None)."""
     n = w.n_tokens if n_tokens is None else n_tokens
     shp = (n, w.heads, w.head_dim)
     tshp = (w.text_len, w.heads, w.head_dim)
-    names = ("q", "k", "v", "txt_q", "txt_k", "txt_v")
     shapes = (shp, shp, shp, tshp, tshp, tshp)
-    return {nm: tensor(w, i, s, seed) for i, (nm, s) in enumerate(zip(names, shapes))}
+    return {nm: tensor(w, i, s, seed, bits_only=bits_only)
+            for i, (nm, s) in enumerate(zip(QKV_NAMES, shapes))}
 
 
 def custom(name, T, H, W, nt, nh, nw, heads, head_dim, text_len, dtype, std=None, index=100):
