@@ -26,6 +26,8 @@
 // `out`; text query rows write their normalised float32 output to the
 // workspace (reduced over windows in id order by the text-mean kernel).
 
+#include <cstdlib>
+
 #include "wsp_internal.h"
 
 namespace wsp {
@@ -69,21 +71,36 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ inline float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ inline float halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed bf16 pair (round to nearest even), one v_cvt_pk.
+__device__ inline bf16x2 to_bf16x2(float lo, float hi) {
+    return __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+}
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
-    return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(lo))) |
-           (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(hi))) << 16);
+    return __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
 }
 
-// Row r of the joint sequence [video rows of the window; text rows].
+// Row r of the joint sequence [video rows of the window; text rows], with r
+// clamped to the last row M-1: rows past the end read real data, which the
+// score mask (keys) or the store guard (queries) then discards.  Branch-free:
+// two selects.
 __device__ inline const uint16_t *joint_row(const uint16_t *vid, const uint16_t *txt, int r,
                                             int Lw, int M, int64_t off, int64_t rs, int64_t hd) {
-    if (r < Lw) return vid + (off + r) * rs + hd;
-    if (r < M) return txt + int64_t(r - Lw) * rs + hd;
-    return nullptr;
+    r = min(r, M - 1);
+    const bool is_vid = r < Lw;
+    const int64_t row = is_vid ? off + r : int64_t(r - Lw);
+    return (is_vid ? vid : txt) + row * rs + hd;
 }
 
+// Rescale threshold of the running softmax maximum, in log2 units: the
+// accumulators are rescaled only when a tile's maximum exceeds the running
+// maximum by more than this, so probabilities stay below 2^8.
+constexpr float kRescaleLog2 = 8.0f;
+
 template <int D, int QB>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 3 - QB) void attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ tq,
     const uint16_t *__restrict__ tk, const uint16_t *__restrict__ tv,
@@ -111,24 +128,45 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
         const uint16_t *p = joint_row(q, tq, qrow[b], Lw, M, off, rs, hd);
 #pragma unroll
         for (int s = 0; s < S_::KSTEPS; ++s)
-            Qr[b][s] = p ? *reinterpret_cast<const bf16x8 *>(p + 16 * s + 8 * hh) : bf16x8{};
+            Qr[b][s] = *reinterpret_cast<const bf16x8 *>(p + 16 * s + 8 * hh);
     }
 
-    // Global -> register staging of one K/V tile.
+    // Global -> register staging of one K/V tile.  Each thread loads fixed
+    // rows of every tile: K rows rk + 256/CH*i (16-byte column kcol), V rows
+    // 4*vkb + r (column vdc).  Tiles made only of video rows advance
+    // per-thread row pointers by a whole tile; tiles that reach the text rows
+    // or the padded end pick each row through joint_row().
     u32x4 kreg[S_::K_LOADS], vreg[4];
+    const int kcol = tid % S_::CH, krow = tid / S_::CH;
     const int vdc = tid % S_::CH, vkb = tid / S_::CH;  // V: 16-byte chunk, block of 4 keys
+    const bool v_loader = tid < S_::V_PAIRS;
+    const int64_t tile_step = int64_t(kBN) * rs;
+    const uint16_t *kp0 = k + (off + krow) * rs + hd + 8 * kcol;
+    const uint16_t *vp0 = v + (off + 4 * vkb) * rs + hd + 8 * vdc;
+    constexpr int KSTRIDE = kThreads / S_::CH;  // rows between a thread's K loads
     auto gload = [&](int j) {
+        if ((j + 1) * kBN <= Lw) {
+            const int64_t o = int64_t(j) * tile_step;
 #pragma unroll
-        for (int i = 0; i < S_::K_LOADS; ++i) {
-            const int c = tid + kThreads * i, r = c / S_::CH, col = c % S_::CH;
-            const uint16_t *p = joint_row(k, tk, j * kBN + r, Lw, M, off, rs, hd);
-            kreg[i] = p ? *reinterpret_cast<const u32x4 *>(p + 8 * col) : u32x4{0, 0, 0, 0};
-        }
-        if (tid < S_::V_PAIRS) {
+            for (int i = 0; i < S_::K_LOADS; ++i)
+                kreg[i] = *reinterpret_cast<const u32x4 *>(kp0 + o + int64_t(KSTRIDE * i) * rs);
+            if (v_loader) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint16_t *p = joint_row(v, tv, j * kBN + 4 * vkb + r, Lw, M, off, rs, hd);
-                vreg[r] = p ? *reinterpret_cast<const u32x4 *>(p + 8 * vdc) : u32x4{0, 0, 0, 0};
+                for (int r = 0; r < 4; ++r)
+                    vreg[r] = *reinterpret_cast<const u32x4 *>(vp0 + o + int64_t(r) * rs);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < S_::K_LOADS; ++i) {
+                const uint16_t *p = joint_row(k, tk, j * kBN + krow + KSTRIDE * i, Lw, M, off, rs, hd);
+                kreg[i] = *reinterpret_cast<const u32x4 *>(p + 8 * kcol);
+            }
+            if (v_loader) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint16_t *p = joint_row(v, tv, j * kBN + 4 * vkb + r, Lw, M, off, rs, hd);
+                    vreg[r] = *reinterpret_cast<const u32x4 *>(p + 8 * vdc);
+                }
             }
         }
     };
@@ -140,11 +178,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
         uint8_t *Kb = smem + buf * S_::STAGE;
         uint8_t *Vb = Kb + S_::K_BYTES;
 #pragma unroll
-        for (int i = 0; i < S_::K_LOADS; ++i) {
-            const int c = tid + kThreads * i, r = c / S_::CH, col = c % S_::CH;
-            *reinterpret_cast<u32x4 *>(Kb + r * S_::K_ROW + col * 16) = kreg[i];
-        }
-        if (tid < S_::V_PAIRS) {
+        for (int i = 0; i < S_::K_LOADS; ++i)
+            *reinterpret_cast<u32x4 *>(Kb + (krow + KSTRIDE * i) * S_::K_ROW + kcol * 16) = kreg[i];
+        if (v_loader) {
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const uint32_t a0 = vreg[0][x], a1 = vreg[1][x], a2 = vreg[2][x], a3 = vreg[3][x];
@@ -214,40 +250,57 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
                     }
                 }
         }
-        // Online softmax; P^T as bf16 B operands, one per 16-key k-step.
-        bf16x8 P[QB][4];
+        // Online softmax.  The running maximum m_run moves (and O, l are
+        // rescaled) only when some lane of the wave sees a tile maximum more
+        // than 2^kRescaleLog2 above it -- a wave-uniform branch taken on the
+        // first tile and rarely after.  P^T leaves as bf16 B operands, one
+        // per 16-key k-step.
+        float mx[QB];
+        bool grow = false;
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
-            float mx = S[b][0][0];
+            float m = S[b][0][0];
 #pragma unroll
             for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[b][mk][r]);
-            mx = halves_max(mx);
-            const float m_new = fmaxf(m_run[b], mx);
-            const float alpha = __builtin_amdgcn_exp2f((m_run[b] - m_new) * c2);
-            const float mc = m_new * c2;
-            float sum = 0.f;
+                for (int r = 0; r < 16; ++r) m = fmaxf(m, S[b][mk][r]);
+            mx[b] = halves_max(m);
+            grow |= (mx[b] - m_run[b]) * c2 > kRescaleLog2;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-            for (int mk = 0; mk < 2; ++mk)
+            for (int b = 0; b < QB; ++b) {
+                const float m_new = fmaxf(m_run[b], mx[b]);
+                const float alpha = __builtin_amdgcn_exp2f((m_run[b] - m_new) * c2);
+                m_run[b] = m_new;
+                l_run[b] *= alpha;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(S[b][mk][r], c2, -mc));
-                    S[b][mk][r] = p;
-                    sum += p;
-                }
-            l_run[b] = l_run[b] * alpha + sum;
-            m_run[b] = m_new;
+                for (int t = 0; t < S_::DT; ++t) O[b][t] *= alpha;
+            }
+        }
+        // p = 2^(s*c2 - m*c2), packed to bf16 pairs; the row sum adds the
+        // same rounded values the PV product uses (one dot2 per pair).
+        bf16x8 P[QB][4];
+        const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
-            for (int t = 0; t < S_::DT; ++t) O[b][t] *= alpha;
+        for (int b = 0; b < QB; ++b) {
+            const float mc = m_run[b] * c2;
+            float sum = l_run[b];
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) {
                 const int mk = cs >> 1, r0 = 8 * (cs & 1);
                 u32x4 pk;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pk[i] = pack_bf16(S[b][mk][r0 + 2 * i], S[b][mk][r0 + 2 * i + 1]);
+                for (int i = 0; i < 4; ++i) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[b][mk][r0 + 2 * i], c2, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[b][mk][r0 + 2 * i + 1], c2, -mc));
+                    const bf16x2 pp = to_bf16x2(p0, p1);
+                    sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
+                    pk[i] = __builtin_bit_cast(uint32_t, pp);
+                }
                 P[b][cs] = __builtin_bit_cast(bf16x8, pk);
             }
+            l_run[b] = sum;
         }
         // O^T += V^T P^T over the tile's four 16-key k-steps.
 #pragma unroll
@@ -299,11 +352,31 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     }
 }
 
-constexpr int kQB = 1;
+// Query blocks of 32 rows per wavefront (1 or 2).  One block keeps a wave
+// within 256 registers, so two waves share each SIMD (the default); two
+// blocks halve the LDS reads per MFMA but run one wave per SIMD.  The
+// WSP_ATTN_QB environment variable selects 2 for measurements.
+int query_blocks() {
+    static const int qb = [] {
+        const char *e = std::getenv("WSP_ATTN_QB");
+        return (e && std::atoi(e) == 2) ? 2 : 1;
+    }();
+    return qb;
+}
+
+template <int D, int QB>
+void launch(const void *q, const void *k, const void *v, const void *tq, const void *tk,
+            const void *tv, void *out, float *ws, const int32_t *offsets, const Item *items,
+            int n_items, int n_heads, int text_len, float c2, hipStream_t s) {
+    auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
+    attn_bf16_kernel<D, QB><<<dim3(n_items), dim3(kThreads), 0, s>>>(
+        U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets, items,
+        n_heads, text_len, c2);
+}
 
 }  // namespace
 
-int attn_bf16_tile_m(int) { return Shape<128, kQB>::BM; }
+int attn_bf16_tile_m(int) { return 4 * 32 * query_blocks(); }
 
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
@@ -311,15 +384,15 @@ hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const vo
                             int n_heads, int text_len, float scale, hipStream_t s) {
     if (n_items <= 0) return hipSuccess;
     const float c2 = scale * kLog2e;
-    auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
-    if (head_dim == 128)
-        attn_bf16_kernel<128, kQB><<<dim3(n_items), dim3(kThreads), 0, s>>>(
-            U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets,
-            items, n_heads, text_len, c2);
+    const int qb = query_blocks();
+    if (head_dim == 128 && qb == 2)
+        launch<128, 2>(q, k, v, tq, tk, tv, out, ws, offsets, items, n_items, n_heads, text_len, c2, s);
+    else if (head_dim == 128)
+        launch<128, 1>(q, k, v, tq, tk, tv, out, ws, offsets, items, n_items, n_heads, text_len, c2, s);
+    else if (head_dim == 64 && qb == 2)
+        launch<64, 2>(q, k, v, tq, tk, tv, out, ws, offsets, items, n_items, n_heads, text_len, c2, s);
     else if (head_dim == 64)
-        attn_bf16_kernel<64, kQB><<<dim3(n_items), dim3(kThreads), 0, s>>>(
-            U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets,
-            items, n_heads, text_len, c2);
+        launch<64, 1>(q, k, v, tq, tk, tv, out, ws, offsets, items, n_items, n_heads, text_len, c2, s);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
