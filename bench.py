@@ -82,6 +82,9 @@ def main():
     ap.add_argument("--workload", default="1080p_bf16", choices=["720p_bf16", "1080p_bf16", "4k_bf16"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (a known-size "
+                         "reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
@@ -137,6 +140,12 @@ def main():
                 out=outs[li], txt_out=txts[li], workspace=ws), record)
         timed("relayout", lambda: W.relayout(outs[-1], plans[-1], canon, out=out_c), record)
 
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()

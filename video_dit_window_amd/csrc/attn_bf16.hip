@@ -7,26 +7,29 @@
 // models with USP (text replica)", section "3. Attention with USP": plain
 // SDPA (no mask, no dropout, scale 1/sqrt(D) unless given).
 //
-// Work item = (window w, head h, query tile of BM rows) of the joint query
+// Work item = (window w, head h, tile of 128 query rows) of the joint query
 // sequence [q rows of w; txt_q]; the key/value sequence is [k/v rows of w;
-// txt_k/v].  A work group has 4 wavefronts; each owns QB blocks of 32 query
-// rows.  Per 64-key tile:
-//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, K from LDS (A), Q in VGPRs (B);
-//                 the transposed product leaves each lane with ONE query
-//                 (column) and 16 keys per 32x32 block, so the softmax row
-//                 statistics need only in-lane reductions plus one swap
-//                 between the two 32-lane halves.
-//   online softmax in float32 (exp2 with the scale folded into one FMA);
-//   O^T += V^T P^T  the probabilities stay in VGPRs as the B operand
-//                 (bf16); V^T comes from LDS, where V is stored as blocks of
-//                 4 keys x 1 dim (8 bytes) so one lane reads 4 keys of one
-//                 head dimension with a single 8-byte LDS load.
-// K/V tiles are double-buffered in LDS; the next tile's global loads are in
-// flight while the current tile is multiplied.  Video query rows write bf16
-// `out`; text query rows write their normalised float32 output to the
-// workspace (reduced over windows in id order by the text-mean kernel).
-
-#include <cstdlib>
+// txt_k/v].  A work group is 4 wavefronts of 32 query rows; two work groups
+// share a compute unit (2 waves per SIMD, < 256 registers each).
+//
+// Per 64-key tile and wavefront:
+//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16 with K from LDS as the A operand
+//                   and Q in registers as B.  The transposed product leaves
+//                   each lane with ONE query column and 32 of its keys.
+//   softmax         float32, exp2 with the scale folded into one FMA; the
+//                   running maximum moves only when a tile's probabilities
+//                   would exceed 2^20 (detected from the row sum).
+//   O^T += V^T P^T  the probabilities stay in registers as bf16 B operands;
+//                   V^T comes from the row-major V tile through the gfx950
+//                   LDS transpose read (ds_read_b64_tr_b16).
+// K and V tiles travel global -> LDS by direct DMA loads (global_load_lds,
+// 16 bytes per lane, no staging registers), double-buffered: the DMA of tile
+// j+1 runs while tile j is multiplied.  Rows are stored unpadded, their
+// 16-byte chunks XOR-swizzled by row so that the K operand reads (16 rows,
+// one chunk) and the transpose reads (4 rows x 4 chunks) hit distinct banks.
+// Video query rows write bf16 `out`; text query rows write their normalised
+// float32 output to the workspace, reduced over windows in id order by the
+// text-mean kernel.
 
 #include "wsp_internal.h"
 
@@ -35,44 +38,53 @@ namespace wsp {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kBN = 64;        // keys per tile
-constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per work group
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D, int QB>
+// Largest per-lane tile sum of probabilities accepted without moving the
+// running maximum: every probability then stays below 2^20, far inside the
+// range of float32 accumulation and of bf16 operands.
+constexpr float kMaxTileSum = 1048576.0f;
+
+template <int D>
 struct Shape {
-    static constexpr int BM = 4 * 32 * QB;            // query rows per work group
-    static constexpr int KSTEPS = D / 16;             // k-steps of S^T over the head dim
-    static constexpr int DT = D / 32;                 // 32-row blocks of O^T
-    static constexpr int CH = D / 8;                  // 16-byte chunks per row
-    static constexpr int K_ROW = 2 * D + 16;          // LDS bytes per K row (padded)
-    static constexpr int K_BYTES = kBN * K_ROW;
-    static constexpr int VB_BYTES = 8 * D;            // one block of 4 keys x D dims
-    static constexpr int V_BYTES = (kBN / 4) * VB_BYTES;
-    static constexpr int STAGE = K_BYTES + V_BYTES;
-    static constexpr int K_LOADS = kBN * CH / kThreads;
-    static constexpr int V_PAIRS = (kBN / 4) * CH;    // (key block, chunk) pairs
-    static_assert(kBN * CH % kThreads == 0, "K tile must split evenly over threads");
-    static_assert(V_PAIRS <= kThreads, "V tile must fit one pass");
+    static constexpr int KSTEPS = D / 16;        // k-steps of S^T over the head dim
+    static constexpr int DT = D / 32;            // 32-row blocks of O^T
+    static constexpr int CH = D / 8;             // 16-byte chunks per row
+    static constexpr int ROW = 2 * D;            // bytes per K/V row in LDS
+    static constexpr int TILE = kBN * ROW;       // one K (or V) tile
+    static constexpr int ROWS_PER_LOAD = 1024 / ROW;            // rows per wave DMA
+    static constexpr int LOADS = kBN / ROWS_PER_LOAD / kWaves;  // DMAs per wave per tile
+    static_assert(LOADS * ROWS_PER_LOAD * kWaves == kBN, "tile must split over the waves");
 };
+
+// XOR swizzle of the 16-byte chunk index within row r (see the file comment).
+template <int D>
+__device__ __host__ constexpr int swz(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // max / sum of a lane's value and the value of the lane 32 apart (the other
-// half of the same query's keys).  A cross-half exchange through the LDS
-// crossbar (ds_bpermute); one call per tile.
+// half of the same query's keys), through ds_bpermute.
 __device__ inline float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ inline float halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Two floats to a packed bf16 pair (round to nearest even), one v_cvt_pk.
 __device__ inline bf16x2 to_bf16x2(float lo, float hi) {
@@ -82,32 +94,27 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
 }
 
-// Row r of the joint sequence [video rows of the window; text rows], with r
-// clamped to the last row M-1: rows past the end read real data, which the
-// score mask (keys) or the store guard (queries) then discards.  Branch-free:
-// two selects.
-__device__ inline const uint16_t *joint_row(const uint16_t *vid, const uint16_t *txt, int r,
-                                            int Lw, int M, int64_t off, int64_t rs, int64_t hd) {
+// Element offset of row r of the joint sequence [video rows of the window;
+// text rows] in its tensor, with r clamped to the last row M-1 (rows past
+// the end read real data, discarded by the key mask or the store guard);
+// `vid` tells which tensor.  Branch-free.
+__device__ inline int64_t joint_off(int r, int Lw, int M, int64_t off, int64_t rs, bool &vid) {
     r = min(r, M - 1);
-    const bool is_vid = r < Lw;
-    const int64_t row = is_vid ? off + r : int64_t(r - Lw);
-    return (is_vid ? vid : txt) + row * rs + hd;
+    vid = r < Lw;
+    return (vid ? off + r : int64_t(r - Lw)) * rs;
 }
 
-// Rescale threshold of the running softmax maximum, in log2 units: the
-// accumulators are rescaled only when a tile's maximum exceeds the running
-// maximum by more than this, so probabilities stay below 2^8.
-constexpr float kRescaleLog2 = 8.0f;
-
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads, 3 - QB) void attn_bf16_kernel(
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ tq,
     const uint16_t *__restrict__ tk, const uint16_t *__restrict__ tv,
     uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
     const Item *__restrict__ items, int H, int Lt, float c2) {
-    using S_ = Shape<D, QB>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S_::STAGE];
+    using S_ = Shape<D>;
+    // Two stages, each a K tile followed by a V tile.
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * S_::TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[2 * S_::TILE];
 
     const Item it = items[blockIdx.x];
     if (it.x < 0) return;
@@ -119,264 +126,202 @@ __global__ __launch_bounds__(kThreads, 3 - QB) void attn_bf16_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // Query rows of this lane (B operand of S^T = K Q^T): 8 dims per k-step.
-    bf16x8 Qr[QB][S_::KSTEPS];
-    int qrow[QB];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-        qrow[b] = qt * S_::BM + (wave * QB + b) * 32 + l32;
-        const uint16_t *p = joint_row(q, tq, qrow[b], Lw, M, off, rs, hd);
+    // Query row of this lane (B operand of S^T = K Q^T): 8 dims per k-step.
+    bf16x8 Qr[S_::KSTEPS];
+    const int qrow = qt * kBM + wave * 32 + l32;
+    {
+        bool vid;
+        const int64_t o = joint_off(qrow, Lw, M, off, rs, vid) + hd;
+        const uint16_t *p = (vid ? q : tq) + o;
 #pragma unroll
         for (int s = 0; s < S_::KSTEPS; ++s)
-            Qr[b][s] = *reinterpret_cast<const bf16x8 *>(p + 16 * s + 8 * hh);
+            Qr[s] = *reinterpret_cast<const bf16x8 *>(p + 16 * s + 8 * hh);
     }
 
-    // Global -> register staging of one K/V tile.  Each thread loads fixed
-    // rows of every tile: K rows rk + 256/CH*i (16-byte column kcol), V rows
-    // 4*vkb + r (column vdc).  Tiles made only of video rows advance
-    // per-thread row pointers by a whole tile; tiles that reach the text rows
-    // or the padded end pick each row through joint_row().
-    u32x4 kreg[S_::K_LOADS], vreg[4];
-    const int kcol = tid % S_::CH, krow = tid / S_::CH;
-    const int vdc = tid % S_::CH, vkb = tid / S_::CH;  // V: 16-byte chunk, block of 4 keys
-    const bool v_loader = tid < S_::V_PAIRS;
+    // DMA of one K/V tile.  Wave `wave` moves rows wave*16 + ROWS_PER_LOAD*i
+    // + lane/CH (i < LOADS); lane's 16 bytes land at LDS chunk lane%CH of its
+    // row and come from the row's chunk (lane%CH) ^ swz(row).
+    const int drow0 = wave * (kBN / kWaves) + lane / S_::CH;
+    const int dpc = lane % S_::CH;
+    int dchunk[S_::LOADS];
+#pragma unroll
+    for (int i = 0; i < S_::LOADS; ++i) dchunk[i] = 8 * (dpc ^ swz<D>(drow0 + S_::ROWS_PER_LOAD * i));
     const int64_t tile_step = int64_t(kBN) * rs;
-    const uint16_t *kp0 = k + (off + krow) * rs + hd + 8 * kcol;
-    const uint16_t *vp0 = v + (off + 4 * vkb) * rs + hd + 8 * vdc;
-    constexpr int KSTRIDE = kThreads / S_::CH;  // rows between a thread's K loads
-    auto gload = [&](int j) {
+    const int64_t vid_lane_off = (off + drow0) * rs + hd;  // video rows, tile 0, load 0
+    auto dma = [&](uint8_t LDS_AS *dst, int j) {
         if ((j + 1) * kBN <= Lw) {
-            const int64_t o = int64_t(j) * tile_step;
+            const int64_t base = vid_lane_off + int64_t(j) * tile_step;
 #pragma unroll
-            for (int i = 0; i < S_::K_LOADS; ++i)
-                kreg[i] = *reinterpret_cast<const u32x4 *>(kp0 + o + int64_t(KSTRIDE * i) * rs);
-            if (v_loader) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    vreg[r] = *reinterpret_cast<const u32x4 *>(vp0 + o + int64_t(r) * rs);
+            for (int i = 0; i < S_::LOADS; ++i) {
+                const int64_t o = base + int64_t(S_::ROWS_PER_LOAD * i) * rs + dchunk[i];
+                const int lo = (wave * (kBN / kWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
+                __builtin_amdgcn_global_load_lds(k + o, (void LDS_AS *)(dst + lo), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(v + o, (void LDS_AS *)(dst + S_::TILE + lo), 16, 0, 0);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < S_::K_LOADS; ++i) {
-                const uint16_t *p = joint_row(k, tk, j * kBN + krow + KSTRIDE * i, Lw, M, off, rs, hd);
-                kreg[i] = *reinterpret_cast<const u32x4 *>(p + 8 * kcol);
-            }
-            if (v_loader) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint16_t *p = joint_row(v, tv, j * kBN + 4 * vkb + r, Lw, M, off, rs, hd);
-                    vreg[r] = *reinterpret_cast<const u32x4 *>(p + 8 * vdc);
-                }
-            }
-        }
-    };
-    // Register -> LDS.  K rows are stored padded; V is transposed into
-    // 16-byte groups [dim 2x: keys 0..3][dim 2x+1: keys 0..3] of one key
-    // block, the group index XOR-swizzled so a quarter-wave of writes and a
-    // half-wave of 8-byte reads each touch distinct banks.
-    auto lstore = [&](int buf) {
-        uint8_t *Kb = smem + buf * S_::STAGE;
-        uint8_t *Vb = Kb + S_::K_BYTES;
-#pragma unroll
-        for (int i = 0; i < S_::K_LOADS; ++i)
-            *reinterpret_cast<u32x4 *>(Kb + (krow + KSTRIDE * i) * S_::K_ROW + kcol * 16) = kreg[i];
-        if (v_loader) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const uint32_t a0 = vreg[0][x], a1 = vreg[1][x], a2 = vreg[2][x], a3 = vreg[3][x];
-                u32x4 g;
-                g[0] = (a0 & 0xFFFFu) | (a1 << 16);
-                g[1] = (a2 & 0xFFFFu) | (a3 << 16);
-                g[2] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-                g[3] = (a2 >> 16) | (a3 & 0xFFFF0000u);
-                const int G = 4 * vdc + x, P = G ^ ((G >> 4) & 3);
-                *reinterpret_cast<u32x4 *>(Vb + vkb * S_::VB_BYTES + P * 16) = g;
+            for (int i = 0; i < S_::LOADS; ++i) {
+                bool vid;
+                const int64_t o = joint_off(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, Lw, M, off,
+                                            rs, vid) + hd + dchunk[i];
+                const int lo = (wave * (kBN / kWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
+                __builtin_amdgcn_global_load_lds((vid ? k : tk) + o, (void LDS_AS *)(dst + lo), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((vid ? v : tv) + o, (void LDS_AS *)(dst + S_::TILE + lo),
+                                                 16, 0, 0);
             }
         }
     };
 
-    f32x16 O[QB][S_::DT];
-    float m_run[QB], l_run[QB];
+    // LDS byte offsets of this lane's operands inside a stage.
+    //  K (A of S^T): row 32*mk + l32, logical chunk 2s + hh.
+    int kaddr[S_::KSTEPS];
 #pragma unroll
-    for (int b = 0; b < QB; ++b) {
-        m_run[b] = -INFINITY;
-        l_run[b] = 0.f;
+    for (int s = 0; s < S_::KSTEPS; ++s)
+        kaddr[s] = l32 * S_::ROW + 16 * ((2 * s + hh) ^ swz<D>(l32));
+    //  V^T (A of O^T) by transpose reads: for O^T block t and half B of a
+    //  16-key k-step, lane i = lane%16 of 16-lane group g reads 8 bytes of
+    //  row 16*cs + 8*B + 4*hh + i/4, dims 32t + 16*(g%2) + 4*(i%4) .. +3;
+    //  the transpose hands lane l dim 32t + l%32 of those four rows.
+    const int gi = lane & 15, ghalf = (lane >> 4) & 1;
+    int vaddr[S_::DT][2];
 #pragma unroll
-        for (int t = 0; t < S_::DT; ++t) O[b][t] = f32x16{};
-    }
+    for (int t = 0; t < S_::DT; ++t)
+#pragma unroll
+        for (int B = 0; B < 2; ++B) {
+            const int row = 8 * B + 4 * hh + (gi >> 2);
+            const int dim = 32 * t + 16 * ghalf + 4 * (gi & 3);
+            vaddr[t][B] = S_::TILE + row * S_::ROW + 16 * ((dim >> 3) ^ swz<D>(row)) + 2 * (dim & 7);
+        }
 
-    // LDS byte offset of this lane's V^T operand inside a key block.
-    int voff[S_::DT];
+    f32x16 O[S_::DT];
 #pragma unroll
-    for (int t = 0; t < S_::DT; ++t) {
-        const int d = 32 * t + l32, G = d >> 1, P = G ^ ((G >> 4) & 3);
-        voff[t] = P * 16 + (d & 1) * 8;
-    }
-
+    for (int t = 0; t < S_::DT; ++t) O[t] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     const int ntiles = (M + kBN - 1) / kBN;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < ntiles) gload(j + 1);
-        const uint8_t *Kb = smem + buf * S_::STAGE;
-        const uint8_t *Vb = Kb + S_::K_BYTES;
 
-        // S^T for 64 keys (two 32-key blocks) x 32 queries per block b.
-        f32x16 S[QB][2];
+    // One tile: cur holds tile j; the DMA of tile j+1 goes to nxt.
+    auto tile = [&](const uint8_t LDS_AS *cur, uint8_t LDS_AS *nxt, int j) {
+        if (j + 1 < ntiles) dma(nxt, j + 1);
+
+        // S^T for 64 keys (two 32-key blocks) x this wave's 32 queries.
+        f32x16 S[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int b = 0; b < QB; ++b) S[b][0] = S[b][1] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < S_::KSTEPS; ++s) {
+        for (int s = 0; s < S_::KSTEPS; ++s)
 #pragma unroll
             for (int mk = 0; mk < 2; ++mk) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                    Kb + (32 * mk + l32) * S_::K_ROW + (16 * s + 8 * hh) * 2);
-#pragma unroll
-                for (int b = 0; b < QB; ++b) S[b][mk] = mfma(a, Qr[b][s], S[b][mk]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 LDS_AS *>(cur + kaddr[s] + mk * 32 * S_::ROW);
+                S[mk] = mfma(a, Qr[s], S[mk]);
             }
-        }
-        // Keys past the end of the joint sequence (last tile only).
-        if ((j + 1) * kBN > M) {
+        if ((j + 1) * kBN > M) {  // keys past the end of the joint sequence
 #pragma unroll
             for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = j * kBN + 32 * mk + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key >= M) {
-#pragma unroll
-                        for (int b = 0; b < QB; ++b) S[b][mk][r] = -INFINITY;
-                    }
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (j * kBN + 32 * mk + 8 * (r >> 2) + 4 * hh + (r & 3) >= M) S[mk][r] = -INFINITY;
         }
-        // Online softmax.  The running maximum m_run moves (and O, l are
-        // rescaled) only when some lane of the wave sees a tile maximum more
-        // than 2^kRescaleLog2 above it -- a wave-uniform branch taken on the
-        // first tile and rarely after.  P^T leaves as bf16 B operands, one
-        // per 16-key k-step.
-        float mx[QB];
-        bool grow = false;
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-            float m = S[b][0][0];
-#pragma unroll
-            for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) m = fmaxf(m, S[b][mk][r]);
-            mx[b] = halves_max(m);
-            grow |= (mx[b] - m_run[b]) * c2 > kRescaleLog2;
-        }
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-            for (int b = 0; b < QB; ++b) {
-                const float m_new = fmaxf(m_run[b], mx[b]);
-                const float alpha = __builtin_amdgcn_exp2f((m_run[b] - m_new) * c2);
-                m_run[b] = m_new;
-                l_run[b] *= alpha;
-#pragma unroll
-                for (int t = 0; t < S_::DT; ++t) O[b][t] *= alpha;
-            }
-        }
-        // p = 2^(s*c2 - m*c2), packed to bf16 pairs; the row sum adds the
-        // same rounded values the PV product uses (one dot2 per pair).
-        bf16x8 P[QB][4];
-        const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-            const float mc = m_run[b] * c2;
-            float sum = l_run[b];
+
+        // p = 2^(s*c2 - m_run*c2) packed to bf16 pairs (P^T B operands, one
+        // per 16-key k-step); the row sum adds the same rounded values.
+        bf16x8 P[4];
+        auto probs = [&]() {
+            const float mc = m_run * c2;
+            float sum = 0.f;
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) {
                 const int mk = cs >> 1, r0 = 8 * (cs & 1);
                 u32x4 pk;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[b][mk][r0 + 2 * i], c2, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[b][mk][r0 + 2 * i + 1], c2, -mc));
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i], c2, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i + 1], c2, -mc));
                     const bf16x2 pp = to_bf16x2(p0, p1);
                     sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
                     pk[i] = __builtin_bit_cast(uint32_t, pp);
                 }
-                P[b][cs] = __builtin_bit_cast(bf16x8, pk);
+                P[cs] = __builtin_bit_cast(bf16x8, pk);
             }
-            l_run[b] = sum;
+            return sum;
+        };
+        // Only when some probability would exceed 2^20 (always on the first
+        // tile, where m_run = -inf) does the wave take the exact path: tile
+        // maximum, rescale of O and l by 2^((m_old - m_new)*c2), recompute.
+        float tsum = probs();
+        if (__builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
+            float m = S[0][0];
+#pragma unroll
+            for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) m = fmaxf(m, S[mk][r]);
+            const float m_new = fmaxf(m_run, halves_max(m));
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < S_::DT; ++t) O[t] *= alpha;
+            tsum = probs();
         }
+        l_run += tsum;
+
         // O^T += V^T P^T over the tile's four 16-key k-steps.
 #pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-            const uint8_t *v0 = Vb + (4 * cs + hh) * S_::VB_BYTES;      // keys 16cs+4hh+0..3
-            const uint8_t *v1 = Vb + (4 * cs + 2 + hh) * S_::VB_BYTES;  // keys 16cs+8+4hh+0..3
+        for (int cs = 0; cs < 4; ++cs)
 #pragma unroll
             for (int t = 0; t < S_::DT; ++t) {
-                const u32x2 lo = *reinterpret_cast<const u32x2 *>(v0 + voff[t]);
-                const u32x2 hi = *reinterpret_cast<const u32x2 *>(v1 + voff[t]);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-                for (int b = 0; b < QB; ++b) O[b][t] = mfma(a, P[b][cs], O[b][t]);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 LDS_AS *)(cur + vaddr[t][0] + cs * 16 * S_::ROW));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 LDS_AS *)(cur + vaddr[t][1] + cs * 16 * S_::ROW));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+                O[t] = mfma(a, P[cs], O[t]);
             }
-        }
-        if (j + 1 < ntiles) lstore(buf ^ 1);
+        // The DMA of tile j+1 has landed (vmcnt) and every wave is done with
+        // `cur` before it is overwritten two tiles later.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
+    };
+
+    uint8_t LDS_AS *const st0 = (uint8_t LDS_AS *)stage0;
+    uint8_t LDS_AS *const st1 = (uint8_t LDS_AS *)stage1;
+    dma(st0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int j = 0; j < ntiles; j += 2) {
+        tile(st0, st1, j);
+        if (j + 1 < ntiles) tile(st1, st0, j + 1);
     }
 
-    // Normalise and store: lane holds query qrow[b], dims 32t + 8g + 4hh + 0..3.
+    // Normalise and store: lane holds query qrow, dims 32t + 8g + 4hh + 0..3.
+    const float l = halves_sum(l_run);
+    if (qrow >= M) return;
+    const float inv = 1.0f / l;
+    if (qrow < Lw) {
+        uint16_t *dst = out + (off + qrow) * rs + hd;
 #pragma unroll
-    for (int b = 0; b < QB; ++b) {
-        const float l = halves_sum(l_run[b]);
-        if (qrow[b] >= M) continue;
-        const float inv = 1.0f / l;
-        if (qrow[b] < Lw) {
-            uint16_t *dst = out + (off + qrow[b]) * rs + hd;
+        for (int t = 0; t < S_::DT; ++t)
 #pragma unroll
-            for (int t = 0; t < S_::DT; ++t)
+            for (int g = 0; g < 4; ++g) {
+                u32x2 st;
+                st[0] = pack_bf16(O[t][4 * g] * inv, O[t][4 * g + 1] * inv);
+                st[1] = pack_bf16(O[t][4 * g + 2] * inv, O[t][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2 *>(dst + 32 * t + 8 * g + 4 * hh) = st;
+            }
+    } else {
+        float *dst = ws + ((int64_t(w) * Lt + (qrow - Lw)) * H + h) * D;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x16 &o = O[b][t];
-                    u32x2 st;
-                    st[0] = pack_bf16(o[4 * g] * inv, o[4 * g + 1] * inv);
-                    st[1] = pack_bf16(o[4 * g + 2] * inv, o[4 * g + 3] * inv);
-                    *reinterpret_cast<u32x2 *>(dst + 32 * t + 8 * g + 4 * hh) = st;
-                }
-        } else {
-            float *dst = ws + ((int64_t(w) * Lt + (qrow[b] - Lw)) * H + h) * D;
+        for (int t = 0; t < S_::DT; ++t)
 #pragma unroll
-            for (int t = 0; t < S_::DT; ++t)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x16 &o = O[b][t];
-                    *reinterpret_cast<f32x4 *>(dst + 32 * t + 8 * g + 4 * hh) =
-                        f32x4{o[4 * g] * inv, o[4 * g + 1] * inv, o[4 * g + 2] * inv, o[4 * g + 3] * inv};
-                }
-        }
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4 *>(dst + 32 * t + 8 * g + 4 * hh) =
+                    f32x4{O[t][4 * g] * inv, O[t][4 * g + 1] * inv, O[t][4 * g + 2] * inv,
+                          O[t][4 * g + 3] * inv};
     }
-}
-
-// Query blocks of 32 rows per wavefront (1 or 2).  One block keeps a wave
-// within 256 registers, so two waves share each SIMD (the default); two
-// blocks halve the LDS reads per MFMA but run one wave per SIMD.  The
-// WSP_ATTN_QB environment variable selects 2 for measurements.
-int query_blocks() {
-    static const int qb = [] {
-        const char *e = std::getenv("WSP_ATTN_QB");
-        return (e && std::atoi(e) == 2) ? 2 : 1;
-    }();
-    return qb;
-}
-
-template <int D, int QB>
-void launch(const void *q, const void *k, const void *v, const void *tq, const void *tk,
-            const void *tv, void *out, float *ws, const int32_t *offsets, const Item *items,
-            int n_items, int n_heads, int text_len, float c2, hipStream_t s) {
-    auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
-    attn_bf16_kernel<D, QB><<<dim3(n_items), dim3(kThreads), 0, s>>>(
-        U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets, items,
-        n_heads, text_len, c2);
 }
 
 }  // namespace
 
-int attn_bf16_tile_m(int) { return 4 * 32 * query_blocks(); }
+int attn_bf16_tile_m(int) { return kBM; }
 
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
@@ -384,15 +329,15 @@ hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const vo
                             int n_heads, int text_len, float scale, hipStream_t s) {
     if (n_items <= 0) return hipSuccess;
     const float c2 = scale * kLog2e;
-    const int qb = query_blocks();
-    if (head_dim == 128 && qb == 2)
-        launch<128, 2>(q, k, v, tq, tk, tv, out, ws, offsets, items, n_items, n_heads, text_len, c2, s);
-    else if (head_dim == 128)
-        launch<128, 1>(q, k, v, tq, tk, tv, out, ws, offsets, items, n_items, n_heads, text_len, c2, s);
-    else if (head_dim == 64 && qb == 2)
-        launch<64, 2>(q, k, v, tq, tk, tv, out, ws, offsets, items, n_items, n_heads, text_len, c2, s);
+    auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
+    if (head_dim == 128)
+        attn_bf16_kernel<128><<<dim3(n_items), dim3(kThreads), 0, s>>>(
+            U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets,
+            items, n_heads, text_len, c2);
     else if (head_dim == 64)
-        launch<64, 1>(q, k, v, tq, tk, tv, out, ws, offsets, items, n_items, n_heads, text_len, c2, s);
+        attn_bf16_kernel<64><<<dim3(n_items), dim3(kThreads), 0, s>>>(
+            U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets,
+            items, n_heads, text_len, c2);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
