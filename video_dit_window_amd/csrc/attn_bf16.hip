@@ -53,6 +53,9 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per work group
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
+// no swizzle, no index stride).
+constexpr int kBufferFlags = 0x00020000;
 
 // Largest per-lane tile sum of probabilities accepted without moving the
 // running maximum: every probability then stays below 2^20, far inside the
@@ -111,6 +114,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const uint16_t *__restrict__ tk, const uint16_t *__restrict__ tv,
     uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
     const Item *__restrict__ items, int H, int Lt, float c2) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     using S_ = Shape<D>;
     // Two stages, each a K tile followed by a V tile.
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * S_::TILE];
@@ -146,17 +150,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     int dchunk[S_::LOADS];
 #pragma unroll
     for (int i = 0; i < S_::LOADS; ++i) dchunk[i] = 8 * (dpc ^ swz<D>(drow0 + S_::ROWS_PER_LOAD * i));
-    const int64_t tile_step = int64_t(kBN) * rs;
-    const int64_t vid_lane_off = (off + drow0) * rs + hd;  // video rows, tile 0, load 0
+    // Tiles made only of video rows load through buffer resources whose base
+    // is the window's first row (scalar registers): the per-lane offset is
+    // loop-invariant and the tile step rides in the scalar offset.  Tiles
+    // that reach the text rows or the padded end load row by row through
+    // joint_off().  The resource's byte range also bounds every access.
+    const uint32_t row_bytes = uint32_t(rs) * 2u;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(k + off * rs + hd), 0, int(uint32_t(Lw) * row_bytes), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(v + off * rs + hd), 0, int(uint32_t(Lw) * row_bytes), kBufferFlags);
+    int dvoff[S_::LOADS];
+#pragma unroll
+    for (int i = 0; i < S_::LOADS; ++i)
+        dvoff[i] = (drow0 + S_::ROWS_PER_LOAD * i) * int(row_bytes) + 2 * dchunk[i];
     auto dma = [&](uint8_t LDS_AS *dst, int j) {
         if ((j + 1) * kBN <= Lw) {
-            const int64_t base = vid_lane_off + int64_t(j) * tile_step;
+            const int soff = j * kBN * int(row_bytes);
 #pragma unroll
             for (int i = 0; i < S_::LOADS; ++i) {
-                const int64_t o = base + int64_t(S_::ROWS_PER_LOAD * i) * rs + dchunk[i];
                 const int lo = (wave * (kBN / kWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
-                __builtin_amdgcn_global_load_lds(k + o, (void LDS_AS *)(dst + lo), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(v + o, (void LDS_AS *)(dst + S_::TILE + lo), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (void LDS_AS *)(dst + lo), 16, dvoff[i], soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + S_::TILE + lo), 16, dvoff[i],
+                                                         soff, 0, 0);
             }
         } else {
 #pragma unroll
@@ -317,6 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     f32x4{O[t][4 * g] * inv, O[t][4 * g + 1] * inv, O[t][4 * g + 2] * inv,
                           O[t][4 * g + 3] * inv};
     }
+#endif
 }
 
 }  // namespace
