@@ -15,7 +15,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;       // rows per work group
-constexpr int kUnroll = 8;      // 16-byte chunks per lane per pass (8 KB per wave)
+constexpr int kUnroll = 4;      // 16-byte chunks per lane per pass (4 KB per wave)
 
 __global__ __launch_bounds__(kWaves * 64) void relayout_kernel(
     const u32x4 *__restrict__ x, u32x4 *__restrict__ y, const int32_t *__restrict__ perm,
