@@ -7,10 +7,11 @@
 // models with USP (text replica)", section "3. Attention with USP": plain
 // SDPA (no mask, no dropout, scale 1/sqrt(D) unless given).
 //
-// Work item = (window w, head h, tile of 128 query rows) of the joint query
+// Work item = (window w, head h, tile of 32*W query rows) of the joint query
 // sequence [q rows of w; txt_q]; the key/value sequence is [k/v rows of w;
-// txt_k/v].  A work group is 4 wavefronts of 32 query rows; two work groups
-// share a compute unit (2 waves per SIMD, < 256 registers each).
+// txt_k/v].  A work group is W = 8 wavefronts of 32 query rows (one work
+// group per CU; W = 4 gives two per CU), 2 waves per SIMD, < 256 registers
+// each.
 //
 // Per 64-key tile and wavefront:
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16 with K from LDS as the A operand
@@ -52,9 +53,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kBN = 64;        // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per work group
 constexpr float kLog2e = 1.4426950408889634f;
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
 // no swizzle, no index stride).
@@ -65,7 +63,7 @@ constexpr int kBufferFlags = 0x00020000;
 // range of float32 accumulation and of bf16 operands.
 constexpr float kMaxTileSum = 1048576.0f;
 
-template <int D>
+template <int D, int kWaves = 4>
 struct Shape {
     static constexpr int KSTEPS = D / 16;        // k-steps of S^T over the head dim
     static constexpr int DT = D / 32;            // 32-row blocks of O^T
@@ -118,15 +116,16 @@ __device__ inline int64_t joint_off(int r, int Lw, int M, int64_t off, int64_t r
     return (vid ? off + r : int64_t(r - Lw)) * rs;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
+template <int D, int kWaves>
+__global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ tq,
     const uint16_t *__restrict__ tk, const uint16_t *__restrict__ tv,
     uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
     const Item *__restrict__ items, int H, int Lt, float c2) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
-    using S_ = Shape<D>;
+    using S_ = Shape<D, kWaves>;
+    constexpr int kBM = 32 * kWaves;  // query rows per work group
     // Two stages, each a K tile followed by a V tile.
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * S_::TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[2 * S_::TILE];
@@ -386,7 +385,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_bf16_pp_kernel(
     uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
     const Item *__restrict__ items, int H, int Lt, float c2) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
-    using S_ = Shape<D>;
+    using S_ = Shape<D, kPPWaves>;
     constexpr int LOADS = kBN / S_::ROWS_PER_LOAD / kPPWaves;  // DMAs per wave per tile
     static_assert(LOADS * S_::ROWS_PER_LOAD * kPPWaves == kBN, "tile must split over the waves");
     // Each stage: K tile, then V tile.  Separate arrays keep the DMA of one
@@ -638,7 +637,18 @@ bool use_pingpong() {
 
 }  // namespace
 
-int attn_bf16_tile_m(int) { return use_pingpong() ? kPPBM : kBM; }
+// Waves per work group of the plain kernel: 8 (default; one work group of
+// 256 query rows per CU, half the K/V DMA per FLOP) or 4 (two work groups of
+// 128 rows per CU), chosen once per process by WSP_ATTN_WAVES.
+int plain_waves() {
+    static const int wv = [] {
+        const char *e = std::getenv("WSP_ATTN_WAVES");
+        return (e && std::atoi(e) == 4) ? 4 : 8;
+    }();
+    return wv;
+}
+
+int attn_bf16_tile_m(int) { return use_pingpong() ? kPPBM : 32 * plain_waves(); }
 
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
@@ -660,16 +670,17 @@ hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const vo
             return hipErrorInvalidValue;
         return hipGetLastError();
     }
-    if (head_dim == 128)
-        attn_bf16_kernel<128><<<dim3(n_items), dim3(kThreads), 0, s>>>(
-            U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets,
-            items, n_heads, text_len, c2);
-    else if (head_dim == 64)
-        attn_bf16_kernel<64><<<dim3(n_items), dim3(kThreads), 0, s>>>(
-            U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets,
-            items, n_heads, text_len, c2);
-    else
-        return hipErrorInvalidValue;
+    const int wv = plain_waves();
+    auto launch = [&](auto kern, int waves) {
+        kern<<<dim3(n_items), dim3(64 * waves), 0, s>>>(U(q), U(k), U(v), U(tq), U(tk), U(tv),
+                                                          static_cast<uint16_t *>(out), ws, offsets,
+                                                          items, n_heads, text_len, c2);
+    };
+    if (head_dim == 128 && wv == 8) launch(attn_bf16_kernel<128, 8>, 8);
+    else if (head_dim == 128) launch(attn_bf16_kernel<128, 4>, 4);
+    else if (head_dim == 64 && wv == 8) launch(attn_bf16_kernel<64, 8>, 8);
+    else if (head_dim == 64) launch(attn_bf16_kernel<64, 4>, 4);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
