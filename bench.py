@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--workload", default="1080p_bf16", choices=["720p_bf16", "1080p_bf16", "4k_bf16"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the side measurement of the pass with relayouts fused into attention")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (a known-size "
                          "reference for HBM byte counters)")
@@ -127,7 +129,7 @@ def main():
     row_bytes = Hh * D * 2
     stream = torch.cuda.current_stream()
 
-    ev = {"attn": [], "relayout": []}
+    ev = {"attn": [], "relayout": [], "fused_attn": []}
 
     def timed(kind, fn, record):
         if record:
@@ -154,24 +156,35 @@ def main():
                 out=outs[li], txt_out=txts[li], workspace=ws), record)
         timed("relayout", lambda: W.relayout(outs[-1], plans[-1], canon, out=out_c), record)
 
+    def step_fused(record):
+        # The same pass with the layout permutations fused into the attention
+        # kernels: q, k, v and outputs stay in canonical order (wsp_window_attn_ex).
+        for li, p in enumerate(plans):
+            timed("fused_attn", lambda li=li, p=p: W.window_attn(
+                p, dev["q"], dev["k"], dev["v"], dev["txt_q"], dev["txt_k"], dev["txt_v"],
+                out=outs[li], txt_out=txts[li], workspace=ws, canonical=True), record)
+
+    def run(fn):
+        for _ in range(args.warmup):
+            fn(False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            fn(True)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step(True)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(stop) / args.steps
+    ms_step, wall = run(step)
+    ms_fused, _ = (None, None) if args.no_fused else run(step_fused)
     attn_ms = [a.elapsed_time(b) for a, b in ev["attn"]]
     rel_ms = [a.elapsed_time(b) for a, b in ev["relayout"]]
     step_flops = sum(flops)
@@ -206,6 +219,14 @@ def main():
                      "flop_per_launch": per_call_flops, "avg_launch_ms": round(attn_avg_ms, 4)},
         "wall_s_timed": round(wall, 3),
     }
+    if ms_fused is not None:
+        f_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["fused_attn"]]))
+        res["fused_pass"] = {
+            "note": "same pass, layout permutations fused into attention (canonical-order I/O)",
+            "ms_per_step": round(ms_fused, 4),
+            "attn_tflops_per_step": round(step_flops / (ms_fused * 1e-3) / 1e12, 3),
+            "attn_kernel_tflops": round(per_call_flops / (f_ms * 1e-3) / 1e12, 2),
+            "avg_launch_ms": round(f_ms, 4)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -184,6 +184,35 @@ int wsp_window_attn(const wsp_plan_t *p, const void *q, const void *k, const voi
                     int head_dim, int text_len, int dtype, float scale, void *out,
                     void *txt_out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Flags of wsp_window_attn_ex. */
+enum wsp_attn_flags {
+    WSP_ATTN_IO_LAYOUT = 0,    /* q, k, v and out rows are in p's layout (as wsp_window_attn) */
+    WSP_ATTN_IO_CANONICAL = 1  /* q, k, v and out rows are in canonical token order */
+};
+
+/*
+ * wsp_window_attn_ex -- wsp_window_attn with the layout permutation fused in.
+ *
+ * "Window-Aligned Sequence Parallelism (SeedVR2)", sections "Motivation" and
+ * "Plan A redistribution": a layout transition in which no token changes
+ * owner is a local permutation.  With WSP_ATTN_IO_CANONICAL the tensors q, k,
+ * v and out hold rows in canonical token order (row c = canonical id c, the
+ * layout WSP_CANONICAL); video row r of window w is read from (and its output
+ * written to) canonical row ids[offsets[w] + r] of p, so no separate
+ * wsp_relayout is needed before or after the call.  The result equals
+ * wsp_relayout(p -> canonical) applied to wsp_window_attn on inputs relayouted
+ * canonical -> p, bit for bit.  txt_* and txt_out are unchanged.
+ *
+ * Arguments, layouts, ownership and errors as wsp_window_attn, plus
+ * flags  WSP_ATTN_IO_LAYOUT or WSP_ATTN_IO_CANONICAL (other bits: WSP_EINVAL).
+ * The first canonical call for a plan on a device uploads its ids table.
+ */
+int wsp_window_attn_ex(const wsp_plan_t *p, const void *q, const void *k, const void *v,
+                       const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                       int head_dim, int text_len, int dtype, float scale, unsigned flags,
+                       void *out, void *txt_out, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
 /*
  * wsp_set_attn_order -- process-wide dispatch order of wsp_window_attn
  * (enum wsp_order; default WSP_ORDER_LPT_XCD).  "Window-Aligned Sequence

@@ -131,6 +131,17 @@ def test_window_attn_argument_errors():
     assert call(tq=None) == -1                     # text needed when Lt > 0
     assert call(wsb=16) == -4                      # workspace too small
     assert call(ws=None) == -4
+    def call_ex(flags, **kw):
+        d = dict(args, **kw)
+        return L.wsp_window_attn_ex(p.handle, d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"],
+                                    d["H"], d["D"], d["Lt"], d["dt"], d["sc"], flags, d["out"],
+                                    d["to"], d["ws"], d["wsb"], None)
+
+    assert call_ex(2) == -1                        # unknown flag bit
+    assert call_ex(0xFFFFFFFF) == -1
+    assert b"flag" in L.wsp_last_error()
+    assert call_ex(W.IO_CANONICAL, D=96) == -1     # same validation as wsp_window_attn
+    assert call_ex(W.IO_CANONICAL, wsb=16) == -4
     need = W.window_attn_workspace(p, 4, 64, 16, W.F32)
     assert need == p.n_windows * 16 * 4 * 64 * 4
     assert W.window_attn_workspace(p, 4, 64, 0, W.BF16) == 0

@@ -4,10 +4,10 @@ relayout and bf16-MFMA window attention behind a C ABI (libwsp.so).
 The Python surface is a thin ctypes binding with the C entry points' names;
 all device work runs in libwsp's HIP kernels.
 """
-from ._lib import (BF16, CANONICAL, F32, ORDER_ID, ORDER_LPT, ORDER_LPT_XCD, REGULAR, SHIFTED,
+from ._lib import (BF16, CANONICAL, F32, IO_CANONICAL, IO_LAYOUT, ORDER_ID, ORDER_LPT, ORDER_LPT_XCD, REGULAR, SHIFTED,
                    LIB_PATH, Plan, WspError, canonical, lib, plan, relayout, set_attn_order,
                    version, window_attn, window_attn_workspace)
 
-__all__ = ["BF16", "CANONICAL", "F32", "ORDER_ID", "ORDER_LPT", "ORDER_LPT_XCD", "REGULAR",
+__all__ = ["BF16", "CANONICAL", "F32", "IO_CANONICAL", "IO_LAYOUT", "ORDER_ID", "ORDER_LPT", "ORDER_LPT_XCD", "REGULAR",
            "SHIFTED", "LIB_PATH", "Plan", "WspError", "canonical", "lib", "plan", "relayout",
            "set_attn_order", "version", "window_attn", "window_attn_workspace"]

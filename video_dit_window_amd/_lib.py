@@ -16,6 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libwsp.so")
 
 REGULAR, SHIFTED, CANONICAL = 0, 1, 2
+IO_LAYOUT, IO_CANONICAL = 0, 1
 F32, BF16 = 0, 1
 ORDER_LPT_XCD, ORDER_LPT, ORDER_ID = 0, 1, 2
 METHODS = {"regular": REGULAR, "shifted": SHIFTED, "canonical": CANONICAL}
@@ -33,6 +34,8 @@ _SIGNATURES = {
     "wsp_window_attn_workspace": (_c_int, [_c_vp, _c_int, _c_int, _c_int, _c_int, _szp]),
     "wsp_window_attn": (_c_int, [_c_vp] * 7 + [_c_int, _c_int, _c_int, _c_int, ctypes.c_float,
                                                 _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "wsp_window_attn_ex": (_c_int, [_c_vp] * 7 + [_c_int, _c_int, _c_int, _c_int, ctypes.c_float,
+                                                   ctypes.c_uint, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "wsp_set_attn_order": (_c_int, [_c_int]),
     "wsp_last_error": (ctypes.c_char_p, []),
     "wsp_version": (_c_int, []),
@@ -169,8 +172,11 @@ def window_attn_workspace(p: Plan, n_heads, head_dim, text_len, dtype) -> int:
 
 
 def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None, out=None, txt_out=None,
-                workspace=None, stream=None):
-    """Joint window attention; returns (out [N,H,D], txt_out [Lt,H,D])."""
+                workspace=None, stream=None, canonical=False):
+    """Joint window attention; returns (out [N,H,D], txt_out [Lt,H,D]).
+
+    canonical=True: q, k, v and out rows are in canonical token order (the
+    layout permutation happens inside the kernel, wsp_window_attn_ex)."""
     torch = _torch()
     N, Hh, D = q.shape
     Lt = txt_q.shape[0]
@@ -193,9 +199,10 @@ def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None, out=None, txt
     ws_bytes = workspace.numel() * workspace.element_size()
     tp = [(_dev_ptr(t, n) if Lt else _c_vp(0)) for n, t in
           (("txt_q", txt_q), ("txt_k", txt_k), ("txt_v", txt_v), ("txt_out", txt_out))]
-    _check("wsp_window_attn", lib().wsp_window_attn(
+    _check("wsp_window_attn_ex", lib().wsp_window_attn_ex(
         p.handle, _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), tp[0], tp[1], tp[2],
         Hh, D, Lt, code, ctypes.c_float(0.0 if scale is None else float(scale)),
+        IO_CANONICAL if canonical else IO_LAYOUT,
         _dev_ptr(out, "out"), tp[3], _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)))
     return out, txt_out
 

@@ -63,6 +63,17 @@ int device_offsets(wsp_plan_t &p, int dev, int32_t **out) {
     return WSP_OK;
 }
 
+int device_ids(wsp_plan_t &p, int dev, int32_t **out) {
+    std::lock_guard<std::mutex> lk(p.mu);
+    DeviceTables &t = p.dev[dev];
+    if (!t.ids) {
+        int rc = upload(p.ids.data(), p.ids.size(), &t.ids);
+        if (rc) return rc;
+    }
+    *out = t.ids;
+    return WSP_OK;
+}
+
 int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out) {
     const auto key = layout_key(src);
     {
@@ -182,6 +193,7 @@ void wsp_plan_free(wsp_plan_t *p) {
         if (hipSetDevice(kv.first) != hipSuccess) continue;
         DeviceTables &t = kv.second;
         if (t.offsets) (void)hipFree(t.offsets);
+        if (t.ids) (void)hipFree(t.ids);
         for (auto &pm : t.perm) (void)hipFree(pm.second);
         for (auto &it : t.items) (void)hipFree(it.second.first);
     }
@@ -231,7 +243,19 @@ int wsp_window_attn(const wsp_plan_t *pc, const void *q, const void *k, const vo
                     const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
                     int head_dim, int text_len, int dtype, float scale, void *out,
                     void *txt_out, void *workspace, size_t workspace_bytes, void *stream) {
+    return wsp_window_attn_ex(pc, q, k, v, txt_q, txt_k, txt_v, n_heads, head_dim, text_len, dtype,
+                              scale, WSP_ATTN_IO_LAYOUT, out, txt_out, workspace, workspace_bytes,
+                              stream);
+}
+
+int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const void *v,
+                       const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                       int head_dim, int text_len, int dtype, float scale, unsigned flags,
+                       void *out, void *txt_out, void *workspace, size_t workspace_bytes,
+                       void *stream) {
     g_last_error.clear();
+    if (flags & ~unsigned(WSP_ATTN_IO_CANONICAL)) return fail(WSP_EINVAL, "unknown attention flags");
+    const bool gather = (flags & WSP_ATTN_IO_CANONICAL) != 0;
     size_t need = 0;
     int rc = wsp_window_attn_workspace(pc, n_heads, head_dim, text_len, dtype, &need);
     if (rc) return rc;
@@ -253,12 +277,14 @@ int wsp_window_attn(const wsp_plan_t *pc, const void *q, const void *k, const vo
     }
     if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
     const int order = g_attn_order.load();
-    const int bm = dtype == WSP_BF16 ? attn_bf16_tile_m(head_dim) : attn_f32_tile_m(head_dim);
+    const int bm = dtype == WSP_BF16 ? attn_bf16_tile_m(head_dim, gather) : attn_f32_tile_m(head_dim);
 
     int dev = 0;
     WSP_HIP(hipGetDevice(&dev));
     int32_t *d_off = nullptr;
     if ((rc = device_offsets(*p, dev, &d_off))) return rc;
+    int32_t *d_ids = nullptr;
+    if (gather && (rc = device_ids(*p, dev, &d_ids))) return rc;
     Item *items = nullptr;
     int n_items = 0;
     if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, &items, &n_items))) return rc;
@@ -266,14 +292,14 @@ int wsp_window_attn(const wsp_plan_t *pc, const void *q, const void *k, const vo
     float *ws = static_cast<float *>(workspace);
     hipError_t e;
     if (dtype == WSP_BF16)
-        e = launch_attn_bf16(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, items,
-                             n_items, n_heads, text_len, scale, s);
+        e = launch_attn_bf16(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, d_ids,
+                             items, n_items, n_heads, text_len, scale, s);
     else
         e = launch_attn_f32(head_dim, static_cast<const float *>(q), static_cast<const float *>(k),
                             static_cast<const float *>(v), static_cast<const float *>(txt_q),
                             static_cast<const float *>(txt_k), static_cast<const float *>(txt_v),
-                            static_cast<float *>(out), ws, d_off, items, n_items, n_heads,
-                            text_len, scale, s);
+                            static_cast<float *>(out), ws, d_off, d_ids, items, n_items,
+                            n_heads, text_len, scale, s);
     if (e != hipSuccess) return hip_fail(e, "window attention kernel launch");
     if (text_len > 0) {
         e = launch_text_mean(ws, txt_out, int64_t(text_len) * n_heads * head_dim, p->nwin, dtype, s);

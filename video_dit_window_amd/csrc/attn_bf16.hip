@@ -116,13 +116,16 @@ __device__ inline int64_t joint_off(int r, int Lw, int M, int64_t off, int64_t r
     return (vid ? off + r : int64_t(r - Lw)) * rs;
 }
 
-template <int D, int kWaves>
+// GATHER: q, k, v and out hold rows in canonical token order; the video row
+// r of window w is canonical row ids[offsets[w] + r] (the plan's table), so
+// the layout permutation happens inside the loads and the output stores.
+template <int D, int kWaves, bool GATHER>
 __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ tq,
     const uint16_t *__restrict__ tk, const uint16_t *__restrict__ tv,
     uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
-    const Item *__restrict__ items, int H, int Lt, float c2) {
+    const int32_t *__restrict__ ids, const Item *__restrict__ items, int H, int Lt, float c2) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     using S_ = Shape<D, kWaves>;
     constexpr int kBM = 32 * kWaves;  // query rows per work group
@@ -140,12 +143,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
 
+    // Tensor row of video row r (< Lw) of this window.
+    const int32_t *const wids = GATHER ? ids + off : nullptr;
+    auto vrow = [&](int r) -> int64_t { return GATHER ? int64_t(wids[r]) : off + r; };
+
     // Query row of this lane (B operand of S^T = K Q^T): 8 dims per k-step.
     bf16x8 Qr[S_::KSTEPS];
     const int qrow = qt * kBM + wave * 32 + l32;
     {
-        bool vid;
-        const int64_t o = joint_off(qrow, Lw, M, off, rs, vid) + hd;
+        const int r = min(qrow, M - 1);
+        const bool vid = r < Lw;
+        const int64_t o = (vid ? vrow(r) : int64_t(r - Lw)) * rs + hd;
         const uint16_t *p = (vid ? q : tq) + o;
 #pragma unroll
         for (int s = 0; s < S_::KSTEPS; ++s)
@@ -174,8 +182,28 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < S_::LOADS; ++i)
         dvoff[i] = (drow0 + S_::ROWS_PER_LOAD * i) * int(row_bytes) + 2 * dchunk[i];
+    // Gather mode: canonical ids of the rows of the next tile to move,
+    // loaded one tile ahead of their DMA.
+    int idp[S_::LOADS];
+    auto load_ids = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < S_::LOADS; ++i)
+            idp[i] = wids[min(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, Lw - 1)];
+    };
     auto dma = [&](uint8_t LDS_AS *dst, int j) {
-        if ((j + 1) * kBN <= Lw) {
+        if constexpr (GATHER) {
+#pragma unroll
+            for (int i = 0; i < S_::LOADS; ++i) {
+                const int r = min(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, M - 1);
+                const bool vid = r < Lw;
+                const int64_t o = (vid ? int64_t(idp[i]) : int64_t(r - Lw)) * rs + hd + dchunk[i];
+                const int lo = (wave * (kBN / kWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
+                __builtin_amdgcn_global_load_lds((vid ? k : tk) + o, (void LDS_AS *)(dst + lo), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((vid ? v : tv) + o, (void LDS_AS *)(dst + S_::TILE + lo),
+                                                 16, 0, 0);
+            }
+            load_ids(j + 1);
+        } else if ((j + 1) * kBN <= Lw) {
             const int soff = j * kBN * int(row_bytes);
 #pragma unroll
             for (int i = 0; i < S_::LOADS; ++i) {
@@ -323,6 +351,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 
     uint8_t LDS_AS *const st0 = (uint8_t LDS_AS *)stage0;
     uint8_t LDS_AS *const st1 = (uint8_t LDS_AS *)stage1;
+    if constexpr (GATHER) load_ids(0);
     dma(st0, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -336,7 +365,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     if (qrow >= M) return;
     const float inv = 1.0f / l;
     if (qrow < Lw) {
-        uint16_t *dst = out + (off + qrow) * rs + hd;
+        uint16_t *dst = out + vrow(qrow) * rs + hd;
 #pragma unroll
         for (int t = 0; t < S_::DT; ++t)
 #pragma unroll
@@ -648,16 +677,17 @@ int plain_waves() {
     return wv;
 }
 
-int attn_bf16_tile_m(int) { return use_pingpong() ? kPPBM : 32 * plain_waves(); }
+int attn_bf16_tile_m(int, bool gather) { return (use_pingpong() && !gather) ? kPPBM : 32 * plain_waves(); }
 
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
-                            float *ws, const int32_t *offsets, const Item *items, int n_items,
-                            int n_heads, int text_len, float scale, hipStream_t s) {
+                            float *ws, const int32_t *offsets, const int32_t *ids,
+                            const Item *items, int n_items, int n_heads, int text_len, float scale,
+                            hipStream_t s) {
     if (n_items <= 0) return hipSuccess;
     const float c2 = scale * kLog2e;
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
-    if (use_pingpong()) {
+    if (use_pingpong() && !ids) {
         if (head_dim == 128)
             attn_bf16_pp_kernel<128><<<dim3(n_items), dim3(kPPThreads), 0, s>>>(
                 U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets,
@@ -674,12 +704,13 @@ hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const vo
     auto launch = [&](auto kern, int waves) {
         kern<<<dim3(n_items), dim3(64 * waves), 0, s>>>(U(q), U(k), U(v), U(tq), U(tk), U(tv),
                                                           static_cast<uint16_t *>(out), ws, offsets,
-                                                          items, n_heads, text_len, c2);
+                                                          ids, items, n_heads, text_len, c2);
     };
-    if (head_dim == 128 && wv == 8) launch(attn_bf16_kernel<128, 8>, 8);
-    else if (head_dim == 128) launch(attn_bf16_kernel<128, 4>, 4);
-    else if (head_dim == 64 && wv == 8) launch(attn_bf16_kernel<64, 8>, 8);
-    else if (head_dim == 64) launch(attn_bf16_kernel<64, 4>, 4);
+    const bool g = ids != nullptr;
+    if (head_dim == 128 && wv == 8) g ? launch(attn_bf16_kernel<128, 8, true>, 8) : launch(attn_bf16_kernel<128, 8, false>, 8);
+    else if (head_dim == 128) g ? launch(attn_bf16_kernel<128, 4, true>, 4) : launch(attn_bf16_kernel<128, 4, false>, 4);
+    else if (head_dim == 64 && wv == 8) g ? launch(attn_bf16_kernel<64, 8, true>, 8) : launch(attn_bf16_kernel<64, 8, false>, 8);
+    else if (head_dim == 64) g ? launch(attn_bf16_kernel<64, 4, true>, 4) : launch(attn_bf16_kernel<64, 4, false>, 4);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -25,12 +25,14 @@ constexpr int kBM = 64;       // queries per work group
 constexpr int kBN = 32;       // keys per LDS tile
 constexpr int kThreads = 256; // 4 lanes per query
 
+// ids != NULL: q, k, v and out rows are in canonical token order and video
+// row r of window w is canonical row ids[offsets[w] + r].
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ tq, const float *__restrict__ tk, const float *__restrict__ tv,
     float *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
-    const Item *__restrict__ items, int H, int Lt, float scale) {
+    const int32_t *__restrict__ ids, const Item *__restrict__ items, int H, int Lt, float scale) {
     constexpr int E = D / 16;  // float4 groups per lane
     __shared__ f32x4 Ks[kBN][D / 4];
     __shared__ f32x4 Vs[kBN][D / 4];
@@ -44,11 +46,12 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     const int64_t rs = int64_t(H) * D;  // row stride (elements)
     const int tid = threadIdx.x, sub = tid & 3, qi = tid >> 2;
     const int qrow = qt * kBM + qi;
+    auto vrow = [&](int r) -> int64_t { return ids ? int64_t(ids[off + r]) : off + r; };
 
     // Query row (zeros past the end of the joint sequence).
     f32x4 qv[E], o[E];
     const float *qp = nullptr;
-    if (qrow < Lw) qp = q + (off + qrow) * rs + int64_t(h) * D;
+    if (qrow < Lw) qp = q + vrow(qrow) * rs + int64_t(h) * D;
     else if (qrow < M) qp = tq + int64_t(qrow - Lw) * rs + int64_t(h) * D;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
             const int kr = j * kBN + r;
             f32x4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
             if (kr < Lw) {
-                const int64_t o_ = (off + kr) * rs + int64_t(h) * D + 4 * col;
+                const int64_t o_ = vrow(kr) * rs + int64_t(h) * D + 4 * col;
                 kk = *reinterpret_cast<const f32x4 *>(k + o_);
                 vv = *reinterpret_cast<const f32x4 *>(v + o_);
             } else if (kr < M) {
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 
     if (qrow >= M) return;
     const float inv = 1.0f / l_run;
-    float *dst = (qrow < Lw) ? out + (off + qrow) * rs + int64_t(h) * D
+    float *dst = (qrow < Lw) ? out + vrow(qrow) * rs + int64_t(h) * D
                              : ws + ((int64_t(w) * Lt + (qrow - Lw)) * H + h) * D;
 #pragma unroll
     for (int e = 0; e < E; ++e) *reinterpret_cast<f32x4 *>(dst + 16 * e + 4 * sub) = o[e] * inv;
@@ -132,15 +135,16 @@ int attn_f32_tile_m(int) { return kBM; }
 
 hipError_t launch_attn_f32(int head_dim, const float *q, const float *k, const float *v,
                            const float *tq, const float *tk, const float *tv, float *out,
-                           float *ws, const int32_t *offsets, const Item *items, int n_items,
-                           int n_heads, int text_len, float scale, hipStream_t s) {
+                           float *ws, const int32_t *offsets, const int32_t *ids,
+                           const Item *items, int n_items, int n_heads, int text_len, float scale,
+                           hipStream_t s) {
     if (n_items <= 0) return hipSuccess;
     if (head_dim == 128)
         attn_f32_kernel<128><<<dim3(n_items), dim3(kThreads), 0, s>>>(
-            q, k, v, tq, tk, tv, out, ws, offsets, items, n_heads, text_len, scale);
+            q, k, v, tq, tk, tv, out, ws, offsets, ids, items, n_heads, text_len, scale);
     else if (head_dim == 64)
         attn_f32_kernel<64><<<dim3(n_items), dim3(kThreads), 0, s>>>(
-            q, k, v, tq, tk, tv, out, ws, offsets, items, n_heads, text_len, scale);
+            q, k, v, tq, tk, tv, out, ws, offsets, ids, items, n_heads, text_len, scale);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -21,6 +21,7 @@ using Item = int2;
 
 struct DeviceTables {
     int32_t *offsets = nullptr;                                 // [n_windows + 1]
+    int32_t *ids = nullptr;                                     // [n_tokens]
     std::map<std::tuple<int, int, int, int>, int32_t *> perm;   // src layout -> perm
     std::map<std::tuple<int, int, int, int>, std::pair<Item *, int>> items;  // (H, Lt, BM, order)
 };
@@ -57,6 +58,7 @@ int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int orde
 
 // ---- device tables (abi.cpp) ----------------------------------------------
 int device_offsets(wsp_plan_t &p, int dev, int32_t **out);
+int device_ids(wsp_plan_t &p, int dev, int32_t **out);
 int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out);
 int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
                  Item **out, int *count);
@@ -65,18 +67,21 @@ int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int 
 // relayout.hip
 hipError_t launch_relayout(const void *x, void *y, const int32_t *perm, int64_t n_rows,
                            int64_t row_bytes, hipStream_t s);
-// attn_bf16.hip: returns the query-tile height used by the bf16 kernel
-int attn_bf16_tile_m(int head_dim);
+// attn_bf16.hip: the query-tile height used by the bf16 kernel.  ids != NULL
+// selects canonical-order q/k/v/out gathered through the plan's ids table.
+int attn_bf16_tile_m(int head_dim, bool gather);
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
-                            float *ws, const int32_t *offsets, const Item *items, int n_items,
-                            int n_heads, int text_len, float scale, hipStream_t s);
+                            float *ws, const int32_t *offsets, const int32_t *ids,
+                            const Item *items, int n_items, int n_heads, int text_len, float scale,
+                            hipStream_t s);
 // attn_f32.hip
 int attn_f32_tile_m(int head_dim);
 hipError_t launch_attn_f32(int head_dim, const float *q, const float *k, const float *v,
                            const float *tq, const float *tk, const float *tv, float *out,
-                           float *ws, const int32_t *offsets, const Item *items, int n_items,
-                           int n_heads, int text_len, float scale, hipStream_t s);
+                           float *ws, const int32_t *offsets, const int32_t *ids,
+                           const Item *items, int n_items, int n_heads, int text_len, float scale,
+                           hipStream_t s);
 // text_mean.hip
 hipError_t launch_text_mean(const float *ws, void *txt_out, int64_t per_window, int n_windows,
                             int dtype, hipStream_t s);
