@@ -142,6 +142,14 @@ def test_window_attn_argument_errors():
     assert b"flag" in L.wsp_last_error()
     assert call_ex(W.IO_CANONICAL, D=96) == -1     # same validation as wsp_window_attn
     assert call_ex(W.IO_CANONICAL, wsb=16) == -4
+    # bf16 windows address rows with 31-bit byte offsets: 32767 heads x 128 x
+    # 2 B = 8 MiB rows, so a window of >= 256 rows (here 5*20*36 = 3600 in one
+    # window) is rejected before anything is launched.
+    big = W.Plan(5, 20, 36, 1, 1, 1, W.REGULAR)
+    for flags in (W.IO_LAYOUT, W.IO_CANONICAL):
+        assert L.wsp_window_attn_ex(big.handle, a, b, c, None, None, None, 32767, 128, 0, W.BF16,
+                                    ctypes.c_float(0), flags, o, None, None, 0, None) == -2
+        assert b"2 GiB" in L.wsp_last_error()
     need = W.window_attn_workspace(p, 4, 64, 16, W.F32)
     assert need == p.n_windows * 16 * 4 * 64 * 4
     assert W.window_attn_workspace(p, 4, 64, 0, W.BF16) == 0

@@ -275,6 +275,16 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
                                             " bytes required, got " + std::to_string(workspace_bytes));
         if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
     }
+    // The bf16 kernel addresses a window's video rows (canonical order: the
+    // rows between its smallest and largest canonical id) and the text rows
+    // with 31-bit byte offsets from per-window buffer bases.
+    if (dtype == WSP_BF16) {
+        const int64_t row_bytes = int64_t(n_heads) * head_dim * 2;
+        const int64_t rows = std::max<int64_t>(gather ? p->max_span : p->max_rows, text_len);
+        if (rows * row_bytes >= (int64_t(1) << 31))
+            return fail(WSP_ERANGE, gather ? "a window's canonical rows span 2 GiB or more"
+                                           : "a window's rows (or the text rows) take 2 GiB or more");
+    }
     if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
     const int order = g_attn_order.load();
     const int bm = dtype == WSP_BF16 ? attn_bf16_tile_m(head_dim, gather) : attn_f32_tile_m(head_dim);

@@ -35,86 +35,11 @@
 #include <cstdlib>
 #include <string>
 
-#include "wsp_internal.h"
+#include "attn_bf16_common.h"
 
 namespace wsp {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr int kBN = 64;        // keys per tile
-constexpr float kLog2e = 1.4426950408889634f;
-// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
-// no swizzle, no index stride).
-constexpr int kBufferFlags = 0x00020000;
-
-// Largest per-lane tile sum of probabilities accepted without moving the
-// running maximum: every probability then stays below 2^20, far inside the
-// range of float32 accumulation and of bf16 operands.
-constexpr float kMaxTileSum = 1048576.0f;
-
-template <int D, int kWaves = 4>
-struct Shape {
-    static constexpr int KSTEPS = D / 16;        // k-steps of S^T over the head dim
-    static constexpr int DT = D / 32;            // 32-row blocks of O^T
-    static constexpr int CH = D / 8;             // 16-byte chunks per row
-    static constexpr int ROW = 2 * D;            // bytes per K/V row in LDS
-    static constexpr int TILE = kBN * ROW;       // one K (or V) tile
-    static constexpr int ROWS_PER_LOAD = 1024 / ROW;            // rows per wave DMA
-    static constexpr int LOADS = kBN / ROWS_PER_LOAD / kWaves;  // DMAs per wave per tile
-    static_assert(LOADS * ROWS_PER_LOAD * kWaves == kBN, "tile must split over the waves");
-};
-
-// XOR swizzle of the 16-byte chunk index within row r (see the file comment).
-template <int D>
-__device__ __host__ constexpr int swz(int r) {
-    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-
-__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// max / sum of a lane's value and the value of the lane 32 apart (the other
-// half of the same query's keys), through ds_bpermute.
-__device__ inline float halves_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
-__device__ inline float halves_sum(float x) { return x + __shfl_xor(x, 32, 64); }
-
-// Two floats to a packed bf16 pair (round to nearest even), one v_cvt_pk.
-__device__ inline bf16x2 to_bf16x2(float lo, float hi) {
-    return __builtin_convertvector(f32x2{lo, hi}, bf16x2);
-}
-__device__ inline uint32_t pack_bf16(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
-}
-
-// Bare work-group barrier (s_barrier, no memory fence).  A fence would drain
-// every outstanding DMA, including those of later stages.  The ping-pong
-// kernel needs none: each wave awaits its own DMAs with an explicit
-// s_waitcnt vmcnt before the barrier that publishes a stage, and every LDS
-// read result is consumed by an MFMA (so has returned) before the barrier
-// after which that stage may be overwritten.
-__device__ inline void lds_barrier() { __builtin_amdgcn_s_barrier(); }
-
-// Element offset of row r of the joint sequence [video rows of the window;
-// text rows] in its tensor, with r clamped to the last row M-1 (rows past
-// the end read real data, discarded by the key mask or the store guard);
-// `vid` tells which tensor.  Branch-free.
-__device__ inline int64_t joint_off(int r, int Lw, int M, int64_t off, int64_t rs, bool &vid) {
-    r = min(r, M - 1);
-    vid = r < Lw;
-    return (vid ? off + r : int64_t(r - Lw)) * rs;
-}
 
 // GATHER: q, k, v and out hold rows in canonical token order; the video row
 // r of window w is canonical row ids[offsets[w] + r] (the plan's table), so
@@ -153,7 +78,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     {
         const int r = min(qrow, M - 1);
         const bool vid = r < Lw;
-        const int64_t o = (vid ? vrow(r) : int64_t(r - Lw)) * rs + hd;
+        const int64_t o = (vid ? vrow(min(r, Lw - 1)) : int64_t(r - Lw)) * rs + hd;
         const uint16_t *p = (vid ? q : tq) + o;
 #pragma unroll
         for (int s = 0; s < S_::KSTEPS; ++s)
@@ -168,16 +93,30 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     int dchunk[S_::LOADS];
 #pragma unroll
     for (int i = 0; i < S_::LOADS; ++i) dchunk[i] = 8 * (dpc ^ swz<D>(drow0 + S_::ROWS_PER_LOAD * i));
-    // Tiles made only of video rows load through buffer resources whose base
-    // is the window's first row (scalar registers): the per-lane offset is
-    // loop-invariant and the tile step rides in the scalar offset.  Tiles
-    // that reach the text rows or the padded end load row by row through
-    // joint_off().  The resource's byte range also bounds every access.
+    // Every DMA is a buffer load (MUBUF): the global/flat DMA forms would
+    // make the compiler wait for all outstanding LDS reads (lgkmcnt(0)) while
+    // a DMA is in flight.  Video rows come through resources based at the
+    // window's first row (gather mode: its smallest canonical row, the first
+    // in row-major order), text rows through resources based at the text
+    // tensors; the host checks that every offset fits 31 bits.  Tiles made
+    // only of video rows (layout order) keep a loop-invariant per-lane offset
+    // and put the tile step in the scalar offset; other tiles load row by row
+    // with rows past the joint sequence clamped to its last row.  A
+    // resource's byte range also bounds every access.
     const uint32_t row_bytes = uint32_t(rs) * 2u;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(k + off * rs + hd), 0, int(uint32_t(Lw) * row_bytes), kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(v + off * rs + hd), 0, int(uint32_t(Lw) * row_bytes), kBufferFlags);
+    // (readfirstlane: the ids are wave-uniform; the resources must sit in
+    // scalar registers, else every DMA becomes a loop over lanes.)
+    const int32_t id_first = GATHER ? __builtin_amdgcn_readfirstlane(wids[0]) : 0;
+    const int32_t id_last = GATHER ? __builtin_amdgcn_readfirstlane(wids[Lw - 1]) : 0;
+    const int64_t vrow0 = GATHER ? int64_t(id_first) : off;
+    const uint32_t vrows = GATHER ? uint32_t(id_last - id_first + 1) : uint32_t(Lw);
+    auto rsrc = [&](const uint16_t *base, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, int(bytes), kBufferFlags);
+    };
+    const __amdgpu_buffer_rsrc_t krs = rsrc(k + vrow0 * rs + hd, vrows * row_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = rsrc(v + vrow0 * rs + hd, vrows * row_bytes);
+    const __amdgpu_buffer_rsrc_t tkrs = rsrc(tk + hd, uint32_t(Lt) * row_bytes);
+    const __amdgpu_buffer_rsrc_t tvrs = rsrc(tv + hd, uint32_t(Lt) * row_bytes);
     int dvoff[S_::LOADS];
 #pragma unroll
     for (int i = 0; i < S_::LOADS; ++i)
@@ -191,19 +130,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             idp[i] = wids[min(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, Lw - 1)];
     };
     auto dma = [&](uint8_t LDS_AS *dst, int j) {
-        if constexpr (GATHER) {
-#pragma unroll
-            for (int i = 0; i < S_::LOADS; ++i) {
-                const int r = min(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, M - 1);
-                const bool vid = r < Lw;
-                const int64_t o = (vid ? int64_t(idp[i]) : int64_t(r - Lw)) * rs + hd + dchunk[i];
-                const int lo = (wave * (kBN / kWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
-                __builtin_amdgcn_global_load_lds((vid ? k : tk) + o, (void LDS_AS *)(dst + lo), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((vid ? v : tv) + o, (void LDS_AS *)(dst + S_::TILE + lo),
-                                                 16, 0, 0);
-            }
-            load_ids(j + 1);
-        } else if ((j + 1) * kBN <= Lw) {
+        if (!GATHER && (j + 1) * kBN <= Lw) {
             const int soff = j * kBN * int(row_bytes);
 #pragma unroll
             for (int i = 0; i < S_::LOADS; ++i) {
@@ -212,18 +139,37 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + S_::TILE + lo), 16, dvoff[i],
                                                          soff, 0, 0);
             }
+        } else if (GATHER && (j + 1) * kBN <= Lw) {
+#pragma unroll
+            for (int i = 0; i < S_::LOADS; ++i) {
+                const int lo = (wave * (kBN / kWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
+                const int o = int(idp[i] - vrow0) * int(row_bytes) + 2 * dchunk[i];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (void LDS_AS *)(dst + lo), 16, o, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + S_::TILE + lo), 16, o, 0, 0, 0);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < S_::LOADS; ++i) {
-                bool vid;
-                const int64_t o = joint_off(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, Lw, M, off,
-                                            rs, vid) + hd + dchunk[i];
+                const int r = min(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, M - 1);
                 const int lo = (wave * (kBN / kWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
-                __builtin_amdgcn_global_load_lds((vid ? k : tk) + o, (void LDS_AS *)(dst + lo), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((vid ? v : tv) + o, (void LDS_AS *)(dst + S_::TILE + lo),
-                                                 16, 0, 0);
+                if (r < Lw) {
+                    const int o = (GATHER ? int(idp[i] - vrow0) : r) * int(row_bytes) + 2 * dchunk[i];
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (void LDS_AS *)(dst + lo), 16, o, 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + S_::TILE + lo), 16, o, 0,
+                                                             0, 0);
+                } else {
+                    const int o = (r - Lw) * int(row_bytes) + 2 * dchunk[i];
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(tkrs, (void LDS_AS *)(dst + lo), 16, o, 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(tvrs, (void LDS_AS *)(dst + S_::TILE + lo), 16, o, 0,
+                                                             0, 0);
+                    // Keeps the compiler from merging the two arms into one
+                    // load with a per-lane resource (issued as a loop over
+                    // lanes).
+                    asm volatile("");
+                }
             }
         }
+        if constexpr (GATHER) load_ids(j + 1);
     };
 
     // LDS byte offsets of this lane's operands inside a stage.
@@ -653,7 +599,7 @@ __global__ __launch_bounds__(kPPThreads) void attn_bf16_pp_kernel(
 #endif
 }
 
-// Kernel variant: the plain 4-wave kernel (default; faster on the measured
+// Kernel variant: the plain kernel (default; faster on the measured
 // workloads) or the ping-pong kernel, chosen once per process by the
 // WSP_ATTN_KERNEL environment variable ("pingpong").
 bool use_pingpong() {

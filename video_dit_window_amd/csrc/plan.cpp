@@ -105,6 +105,14 @@ int build_plan(int T, int H, int W, int nt, int nh, int nw, int method, wsp_plan
                 p.offsets.push_back(int32_t(pos));
             }
     p.nwin = int32_t(nwin);
+    p.max_rows = p.max_span = 0;
+    for (size_t w = 0; w < nwin; ++w) {
+        const int32_t a = p.offsets[w], b = p.offsets[w + 1];
+        p.max_rows = std::max<int64_t>(p.max_rows, b - a);
+        // Rows are in row-major (t, h, w) order: the first has the smallest
+        // canonical id and the last the largest.
+        if (b > a) p.max_span = std::max<int64_t>(p.max_span, int64_t(p.ids[b - 1]) - p.ids[a] + 1);
+    }
     // Largest first, ties by window id.
     std::iota(p.lpt.begin(), p.lpt.end(), 0);
     std::stable_sort(p.lpt.begin(), p.lpt.end(), [&](int32_t a, int32_t b) {

@@ -33,6 +33,8 @@ struct wsp_plan_t {
     int wt = 0, wh = 0, ww = 0;
     int64_t n = 0;
     int32_t nwin = 0;
+    int64_t max_rows = 0;   // largest window (rows)
+    int64_t max_span = 0;   // largest canonical-id span of a window (last id - first id + 1)
     std::vector<int32_t> offsets, ids, inv, boxes, lpt;
     std::mutex mu;                               // guards dev
     std::map<int, wsp::DeviceTables> dev;        // per device ordinal
