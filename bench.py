@@ -40,13 +40,17 @@ METRIC = "window-attn TFLOP/s + video tokens/s/layer at 1080p grid; % MFMA peak"
 # (FETCH_SIZE x2.0, WRITE_SIZE x1.0); the committed summary under profiles/ holds the
 # figures and commands.  Keyed by the sha256 prefix of the attention kernel source the
 # counters were taken on: any later change to the kernel reports null.
-MEASURED_TRAFFIC = {"bc1bc29714423499": {"1080p_bf16": 4.6506e9}}
-ATTN_SRC = os.path.join(ROOT, "video_dit_window_amd", "csrc", "attn_bf16.hip")
+MEASURED_TRAFFIC = {"54467b935b3e9fbe": {"1080p_bf16": 4.5868e9}}
+ATTN_SRCS = [os.path.join(ROOT, "video_dit_window_amd", "csrc", f)
+             for f in ("attn_bf16.hip", "attn_bf16_common.h")]
+
+
+def attn_source_hash():
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in ATTN_SRCS)).hexdigest()[:16]
 
 
 def measured_traffic(workload):
-    h = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
-    return MEASURED_TRAFFIC.get(h, {}).get(workload)
+    return MEASURED_TRAFFIC.get(attn_source_hash(), {}).get(workload)
 
 
 def attn_flops(lengths, heads, head_dim, text_len):
@@ -215,7 +219,7 @@ def main():
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(w.name), "traffic_unit": "B/launch",
-                     "kernel": "attn_bf16_kernel<128> (+ text_mean_kernel in the same call)",
+                     "kernel": "attn_bf16_kernel<128, 8, false> (+ text_mean_kernel in the same call)",
                      "flop_per_launch": per_call_flops, "avg_launch_ms": round(attn_avg_ms, 4)},
         "wall_s_timed": round(wall, 3),
     }
