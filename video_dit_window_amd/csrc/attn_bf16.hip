@@ -259,6 +259,21 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         // Only when some probability would exceed 2^20 (always on the first
         // tile, where m_run = -inf) does the wave take the exact path: tile
         // maximum, rescale of O and l by 2^((m_old - m_new)*c2), recompute.
+        // V^T operands (transpose reads) of one 16-key step; those of the
+        // first step are read while the softmax runs.
+        auto vread = [&](int cs, bf16x8 (&dst)[S_::DT]) {
+#pragma unroll
+            for (int t = 0; t < S_::DT; ++t) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 LDS_AS *)(cur + vaddr[t][0] + cs * 16 * S_::ROW));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 LDS_AS *)(cur + vaddr[t][1] + cs * 16 * S_::ROW));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                dst[t] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+            }
+        };
+        bf16x8 va[2][S_::DT];
+        vread(0, va[0]);
         float tsum = probs();
         if (__builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
             float m = S[0][0];
@@ -276,19 +291,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         }
         l_run += tsum;
 
-        // O^T += V^T P^T over the tile's four 16-key k-steps.
+        // O^T += V^T P^T over the tile's four 16-key k-steps, the operands
+        // of step cs+1 read while step cs multiplies.
 #pragma unroll
-        for (int cs = 0; cs < 4; ++cs)
+        for (int cs = 0; cs < 4; ++cs) {
+            if (cs + 1 < 4) vread(cs + 1, va[(cs + 1) & 1]);
 #pragma unroll
-            for (int t = 0; t < S_::DT; ++t) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (s16x4 LDS_AS *)(cur + vaddr[t][0] + cs * 16 * S_::ROW));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (s16x4 LDS_AS *)(cur + vaddr[t][1] + cs * 16 * S_::ROW));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-                O[t] = mfma(a, P[cs], O[t]);
-            }
+            for (int t = 0; t < S_::DT; ++t) O[t] = mfma(va[cs & 1][t], P[cs], O[t]);
+        }
         // The DMA of tile j+1 has landed (vmcnt) and every wave is done with
         // `cur` before it is overwritten two tiles later.
         __builtin_amdgcn_s_waitcnt(0x0F70);
