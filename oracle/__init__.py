@@ -5,3 +5,4 @@ may import this package.  The product path (``video_dit_window_amd``) never
 imports it and shares no code with it.
 """
 from .wsp_oracle import *  # noqa: F401,F403
+from .wsp_rope import *  # noqa: F401,F403,E402
