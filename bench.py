@@ -133,7 +133,7 @@ def main():
     row_bytes = Hh * D * 2
     stream = torch.cuda.current_stream()
 
-    ev = {"attn": [], "relayout": [], "fused_attn": []}
+    ev = {"attn": [], "relayout": [], "fused_attn": [], "rope": []}
 
     def timed(kind, fn, record):
         if record:
@@ -168,6 +168,15 @@ def main():
                 p, dev["q"], dev["k"], dev["v"], dev["txt_q"], dev["txt_k"], dev["txt_v"],
                 out=outs[li], txt_out=txts[li], workspace=ws, canonical=True), record)
 
+    def step_rope(record):
+        # Window-local RoPE of q and k fused with the entry move (canonical ->
+        # each layer's layout, that layout's positions).
+        for li, p in enumerate(plans):
+            dst = bufs if li % 2 == 0 else bufs2
+            for n in ("q", "k"):
+                timed("rope", lambda n=n, p=p, dst=dst: W.rope_relayout(dev[n], canon, p, p, Lt, out=dst[n]),
+                      record)
+
     def run(fn):
         for _ in range(args.warmup):
             fn(False)
@@ -189,6 +198,7 @@ def main():
         del src, dst
     ms_step, wall = run(step)
     ms_fused, _ = (None, None) if args.no_fused else run(step_fused)
+    run(step_rope)
     attn_ms = [a.elapsed_time(b) for a, b in ev["attn"]]
     rel_ms = [a.elapsed_time(b) for a, b in ev["relayout"]]
     step_flops = sum(flops)
@@ -223,6 +233,12 @@ def main():
                      "flop_per_launch": per_call_flops, "avg_launch_ms": round(attn_avg_ms, 4)},
         "wall_s_timed": round(wall, 3),
     }
+    rope_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["rope"]]))
+    rope_bytes = 2 * N * row_bytes + 12 * N   # rows in + out, perm + id + position per row
+    res["rope_relayout"] = {"note": "q or k moved canonical -> layout with window-local 3D RoPE",
+                            "avg_launch_ms": round(rope_ms, 4),
+                            "gbps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     if ms_fused is not None:
         f_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["fused_attn"]]))
         res["fused_pass"] = {

@@ -214,6 +214,53 @@ int wsp_window_attn_ex(const wsp_plan_t *p, const void *q, const void *k, const 
                        void *stream);
 
 /*
+ * wsp_rope_relayout -- window-local 3D rotary position embedding, fused with
+ * the row move between two layouts (for q and k; v takes wsp_relayout).
+ *
+ * "Window-Aligned Sequence Parallelism (SeedVR2)", section "Reference quirks
+ * reproduced on purpose": a video token at window-local offset (dt, dh, dw)
+ * inside its window uses the axial indices (text_len + dt, dh, dw), and every
+ * window restarts at 0; 3 * (rope_dim // 3) channels are rotated (126 of 128)
+ * and the last two pass through.  Where the page is silent this library
+ * takes: three contiguous 42-channel axis blocks [t | h | w], each rotated in
+ * adjacent pairs (2k, 2k+1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a),
+ * pair i of a block turning by position * theta^(-2i/42).
+ *
+ * y[j] = rotate(x[row of src holding dst's token j], axial indices of that
+ * token in layout `pos`).  With pos == dst this is the rotation a window
+ * layer applies; with src == dst == pos's grid in canonical order it rotates
+ * canonical-order q / k for the layout `pos` (for wsp_window_attn_ex with
+ * canonical I/O).
+ *
+ * x, y       device pointers, [n_tokens, n_heads, head_dim] of dtype,
+ *            16-byte aligned, non-overlapping
+ * head_dim   128 (the only size whose axis blocks pair up); n_heads 1..32767
+ * src, dst, pos  plans of the same grid; pos's window extents <= 1024 (t),
+ *            2048 (h, w)
+ * text_len   text tokens ahead of the video in the temporal index (>= 0)
+ * theta      rotary base (<= 0 or non-finite: 10000)
+ * The first call for a (theta, position count) pair on a device builds a
+ * small (cos, sin) table (double precision, rounded to float32) that lives
+ * until the process ends; the first call for a plan uploads its tables.
+ * Errors: WSP_EINVAL (NULL / misaligned / aliasing pointers, grids differ,
+ * head_dim, dtype, n_heads, text_len), WSP_ERANGE (window extents),
+ * WSP_ENOMEM, WSP_EDEVICE.
+ */
+int wsp_rope_relayout(const void *x, void *y, int n_heads, int head_dim, int dtype,
+                      const wsp_plan_t *src, const wsp_plan_t *dst, const wsp_plan_t *pos,
+                      int text_len, float theta, void *stream);
+
+/*
+ * wsp_rope_text -- rotary embedding of the text rows: text token i uses the
+ * axial indices (i, i, i) (plain 1-D rotary positions; the page places video
+ * temporal indices after text_len, the text takes 0 .. text_len-1).
+ * x, y [text_len, n_heads, head_dim]; arguments and errors as
+ * wsp_rope_relayout.  text_len == 0 is a no-op.
+ */
+int wsp_rope_text(const void *x, void *y, int text_len, int n_heads, int head_dim, int dtype,
+                  float theta, void *stream);
+
+/*
  * wsp_set_attn_order -- process-wide dispatch order of wsp_window_attn
  * (enum wsp_order; default WSP_ORDER_LPT_XCD).  "Window-Aligned Sequence
  * Parallelism (SeedVR2)", section "Planner": ragged windows are balanced by

@@ -155,6 +155,31 @@ def test_window_attn_argument_errors():
     assert W.window_attn_workspace(p, 4, 64, 0, W.BF16) == 0
 
 
+def test_rope_argument_errors():
+    p = W.Plan(5, 20, 36, 2, 3, 3, W.REGULAR)
+    c = W.canonical(5, 20, 36)
+    other = W.Plan(5, 20, 40, 2, 3, 3, W.REGULAR)
+    L = raw()
+    a, b = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
+    f0 = ctypes.c_float(0)
+
+    def call(x=a, y=b, H=4, D=128, dt=W.BF16, src=c, dst=p, pos=p, Lt=16):
+        return L.wsp_rope_relayout(x, y, H, D, dt, src.handle, dst.handle, pos.handle, Lt, f0, None)
+
+    assert call(D=64) == -1 and b"head_dim 128" in L.wsp_last_error()
+    assert call(x=None) == -1
+    assert call(y=a) == -1                      # aliasing
+    assert call(x=ctypes.c_void_p(0x1008)) == -1
+    assert call(dt=7) == -1
+    assert call(H=0) == -1
+    assert call(Lt=-1) == -1
+    assert call(pos=other) == -1                # grids differ
+    assert L.wsp_rope_relayout(a, b, 4, 128, W.BF16, c.handle, None, p.handle, 0, f0, None) == -1
+    assert L.wsp_rope_text(a, b, 16, 4, 64, W.BF16, f0, None) == -1
+    assert L.wsp_rope_text(a, a, 16, 4, 128, W.BF16, f0, None) == -1
+    assert L.wsp_rope_text(a, b, 0, 4, 128, W.BF16, f0, None) == 0      # nothing to do
+
+
 def test_attn_order_option():
     L = raw()
     assert L.wsp_set_attn_order(7) == -1

@@ -36,6 +36,9 @@ _SIGNATURES = {
                                                 _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "wsp_window_attn_ex": (_c_int, [_c_vp] * 7 + [_c_int, _c_int, _c_int, _c_int, ctypes.c_float,
                                                    ctypes.c_uint, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "wsp_rope_relayout": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_int,
+                                   ctypes.c_float, _c_vp]),
+    "wsp_rope_text": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _c_vp]),
     "wsp_set_attn_order": (_c_int, [_c_int]),
     "wsp_last_error": (ctypes.c_char_p, []),
     "wsp_version": (_c_int, []),
@@ -205,6 +208,37 @@ def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None, out=None, txt
         IO_CANONICAL if canonical else IO_LAYOUT,
         _dev_ptr(out, "out"), tp[3], _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)))
     return out, txt_out
+
+
+def rope_relayout(x, src: Plan, dst: Plan, pos: Plan, text_len, theta=None, out=None, stream=None):
+    """Rows of x [N, H, 128] moved from layout src to dst and rotated by the
+    window-local axial indices (text_len + dt, dh, dw) of each token in
+    layout pos (wsp_rope_relayout)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    if x.shape[0] != src.n_tokens or out.shape != x.shape or out.dtype != x.dtype or x.dim() != 3:
+        raise ValueError("x/out shape does not match the plans")
+    _check("wsp_rope_relayout", lib().wsp_rope_relayout(
+        _dev_ptr(x, "x"), _dev_ptr(out, "out"), x.shape[1], x.shape[2], _dtype_code(x.dtype),
+        src.handle, dst.handle, pos.handle, int(text_len), ctypes.c_float(0.0 if theta is None else theta),
+        _stream(stream)))
+    return out
+
+
+def rope_text(x, theta=None, out=None, stream=None):
+    """Text rows x [Lt, H, 128] rotated by the axial indices (i, i, i) (wsp_rope_text)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or x.dim() != 3:
+        raise ValueError("x/out shapes differ")
+    if x.shape[0] == 0:
+        return out
+    _check("wsp_rope_text", lib().wsp_rope_text(
+        _dev_ptr(x, "x"), _dev_ptr(out, "out"), x.shape[0], x.shape[1], x.shape[2], _dtype_code(x.dtype),
+        ctypes.c_float(0.0 if theta is None else theta), _stream(stream)))
+    return out
 
 
 def set_attn_order(order: int):

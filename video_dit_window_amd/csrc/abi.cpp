@@ -4,6 +4,9 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "wsp_internal.h"
 
@@ -71,6 +74,23 @@ int device_ids(wsp_plan_t &p, int dev, int32_t **out) {
         if (rc) return rc;
     }
     *out = t.ids;
+    return WSP_OK;
+}
+
+int device_positions(wsp_plan_t &p, int dev, int32_t **out) {
+    std::lock_guard<std::mutex> lk(p.mu);
+    DeviceTables &t = p.dev[dev];
+    if (!t.pos) {
+        std::vector<int32_t> pos;
+        try {
+            window_positions(p, pos);
+        } catch (const std::bad_alloc &) {
+            return fail(WSP_ENOMEM, "host allocation of a position table failed");
+        }
+        int rc = upload(pos.data(), pos.size(), &t.pos);
+        if (rc) return rc;
+    }
+    *out = t.pos;
     return WSP_OK;
 }
 
@@ -194,6 +214,7 @@ void wsp_plan_free(wsp_plan_t *p) {
         DeviceTables &t = kv.second;
         if (t.offsets) (void)hipFree(t.offsets);
         if (t.ids) (void)hipFree(t.ids);
+        if (t.pos) (void)hipFree(t.pos);
         for (auto &pm : t.perm) (void)hipFree(pm.second);
         for (auto &it : t.items) (void)hipFree(it.second.first);
     }
@@ -315,6 +336,106 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
         e = launch_text_mean(ws, txt_out, int64_t(text_len) * n_heads * head_dim, p->nwin, dtype, s);
         if (e != hipSuccess) return hip_fail(e, "text mean kernel launch");
     }
+    return WSP_OK;
+}
+
+namespace {
+
+constexpr int kRopeHeadDim = 128;
+constexpr int kRopeAxisPairs = 21;
+
+// (cos, sin) of position p times theta^(-2i/42), i < 21, for p < P; one table
+// per (device, theta, P), built in double and kept until the process ends.
+std::mutex g_rope_mu;
+std::map<std::tuple<int, uint32_t, int>, float2 *> g_rope_tables;
+
+int rope_table(int dev, float theta, int P, const float2 **out) {
+    uint32_t tb;
+    std::memcpy(&tb, &theta, sizeof tb);
+    const auto key = std::make_tuple(dev, tb, P);
+    std::lock_guard<std::mutex> lk(g_rope_mu);
+    auto it = g_rope_tables.find(key);
+    if (it != g_rope_tables.end()) {
+        *out = it->second;
+        return WSP_OK;
+    }
+    std::vector<float2> host;
+    try {
+        host.resize(size_t(P) * kRopeAxisPairs);
+    } catch (const std::bad_alloc &) {
+        return fail(WSP_ENOMEM, "host allocation of a rotary table failed");
+    }
+    const int axis = 2 * kRopeAxisPairs;
+    for (int p = 0; p < P; ++p)
+        for (int i = 0; i < kRopeAxisPairs; ++i) {
+            const double a = double(p) * std::pow(double(theta), -2.0 * i / axis);
+            host[size_t(p) * kRopeAxisPairs + i] = float2{float(std::cos(a)), float(std::sin(a))};
+        }
+    float2 *d = nullptr;
+    int rc = upload(host.data(), host.size(), &d);
+    if (rc) return rc;
+    g_rope_tables.emplace(key, d);
+    *out = d;
+    return WSP_OK;
+}
+
+int rope_args(const void *x, const void *y, int n_heads, int head_dim, int dtype, int text_len,
+              float &theta) {
+    if (!x || !y) return fail(WSP_EINVAL, "x or y is NULL");
+    if (!aligned16(x) || !aligned16(y)) return fail(WSP_EINVAL, "x and y must be 16-byte aligned");
+    if (x == y) return fail(WSP_EINVAL, "x and y must not alias");
+    if (head_dim != kRopeHeadDim)
+        return fail(WSP_EINVAL, "rotary embedding needs head_dim 128 (three 42-channel axis blocks), got " +
+                                    std::to_string(head_dim));
+    if (n_heads < 1 || n_heads > 32767) return fail(WSP_EINVAL, "n_heads must be in 1..32767");
+    if (dtype != WSP_F32 && dtype != WSP_BF16) return fail(WSP_EINVAL, "unknown dtype");
+    if (text_len < 0 || text_len > (1 << 20)) return fail(WSP_EINVAL, "text_len must be in 0..2^20");
+    if (!(theta > 0.0f) || !std::isfinite(theta)) theta = 10000.0f;
+    return WSP_OK;
+}
+
+}  // namespace
+
+int wsp_rope_relayout(const void *x, void *y, int n_heads, int head_dim, int dtype,
+                      const wsp_plan_t *src, const wsp_plan_t *dst, const wsp_plan_t *pos,
+                      int text_len, float theta, void *stream) {
+    g_last_error.clear();
+    if (!src || !dst || !pos) return fail(WSP_EINVAL, "plan is NULL");
+    if (src->T != dst->T || src->H != dst->H || src->W != dst->W || pos->T != dst->T ||
+        pos->H != dst->H || pos->W != dst->W)
+        return fail(WSP_EINVAL, "plans of different grids");
+    int rc = rope_args(x, y, n_heads, head_dim, dtype, text_len, theta);
+    if (rc) return rc;
+    if (pos->max_ext[0] > 1024 || pos->max_ext[1] > 2048 || pos->max_ext[2] > 2048)
+        return fail(WSP_ERANGE, "window extents beyond 1024 (t) / 2048 (h, w)");
+    const int P = std::max({text_len + pos->max_ext[0], pos->max_ext[1], pos->max_ext[2]});
+    int dev = 0;
+    WSP_HIP(hipGetDevice(&dev));
+    int32_t *perm = nullptr, *cid = nullptr, *ptab = nullptr;
+    const float2 *cs = nullptr;
+    if ((rc = device_perm(*src, *const_cast<wsp_plan_t *>(dst), dev, &perm))) return rc;
+    if ((rc = device_ids(*const_cast<wsp_plan_t *>(dst), dev, &cid))) return rc;
+    if ((rc = device_positions(*const_cast<wsp_plan_t *>(pos), dev, &ptab))) return rc;
+    if ((rc = rope_table(dev, theta, P, &cs))) return rc;
+    hipError_t e = launch_rope(x, y, perm, cid, ptab, cs, dst->n, n_heads, dtype, text_len,
+                               hipStream_t(stream));
+    if (e != hipSuccess) return hip_fail(e, "rope kernel launch");
+    return WSP_OK;
+}
+
+int wsp_rope_text(const void *x, void *y, int text_len, int n_heads, int head_dim, int dtype,
+                  float theta, void *stream) {
+    g_last_error.clear();
+    int rc = rope_args(x, y, n_heads, head_dim, dtype, text_len, theta);
+    if (rc) return rc;
+    if (text_len == 0) return WSP_OK;
+    int dev = 0;
+    WSP_HIP(hipGetDevice(&dev));
+    const float2 *cs = nullptr;
+    if ((rc = rope_table(dev, theta, text_len, &cs))) return rc;
+    hipError_t e = launch_rope(x, y, nullptr, nullptr, nullptr, cs, text_len, n_heads, dtype, 0,
+                               hipStream_t(stream));
+    if (e != hipSuccess) return hip_fail(e, "rope kernel launch");
     return WSP_OK;
 }
 

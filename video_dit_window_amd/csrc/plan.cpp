@@ -106,6 +106,10 @@ int build_plan(int T, int H, int W, int nt, int nh, int nw, int method, wsp_plan
             }
     p.nwin = int32_t(nwin);
     p.max_rows = p.max_span = 0;
+    p.max_ext[0] = p.max_ext[1] = p.max_ext[2] = 0;
+    for (size_t w = 0; w < nwin; ++w)
+        for (int a = 0; a < 3; ++a)
+            p.max_ext[a] = std::max(p.max_ext[a], p.boxes[6 * w + 2 * a + 1] - p.boxes[6 * w + 2 * a]);
     for (size_t w = 0; w < nwin; ++w) {
         const int32_t a = p.offsets[w], b = p.offsets[w + 1];
         p.max_rows = std::max<int64_t>(p.max_rows, b - a);
@@ -120,6 +124,20 @@ int build_plan(int T, int H, int W, int nt, int nh, int nw, int method, wsp_plan
         return la > lb;
     });
     return WSP_OK;
+}
+
+void window_positions(const wsp_plan_t &p, std::vector<int32_t> &pos) {
+    // "Window-Aligned Sequence Parallelism (SeedVR2)", section "Reference
+    // quirks reproduced on purpose": RoPE positions restart in every window.
+    pos.assign(size_t(p.n), 0);
+    for (int32_t w = 0; w < p.nwin; ++w) {
+        const int32_t *b = &p.boxes[6 * size_t(w)];
+        for (int t = b[0]; t < b[1]; ++t)
+            for (int h = b[2]; h < b[3]; ++h)
+                for (int x = b[4]; x < b[5]; ++x)
+                    pos[size_t((int64_t(t) * p.H + h) * p.W + x)] =
+                        (t - b[0]) | ((h - b[2]) << 10) | ((x - b[4]) << 21);
+    }
 }
 
 void relayout_perm(const wsp_plan_t &src, const wsp_plan_t &dst, std::vector<int32_t> &perm) {

@@ -22,6 +22,7 @@ using Item = int2;
 struct DeviceTables {
     int32_t *offsets = nullptr;                                 // [n_windows + 1]
     int32_t *ids = nullptr;                                     // [n_tokens]
+    int32_t *pos = nullptr;                                     // [n_tokens] window positions
     std::map<std::tuple<int, int, int, int>, int32_t *> perm;   // src layout -> perm
     std::map<std::tuple<int, int, int, int>, std::pair<Item *, int>> items;  // (H, Lt, BM, order)
 };
@@ -35,6 +36,7 @@ struct wsp_plan_t {
     int32_t nwin = 0;
     int64_t max_rows = 0;   // largest window (rows)
     int64_t max_span = 0;   // largest canonical-id span of a window (last id - first id + 1)
+    int32_t max_ext[3] = {0, 0, 0};  // largest window extent along t, h, w
     std::vector<int32_t> offsets, ids, inv, boxes, lpt;
     std::mutex mu;                               // guards dev
     std::map<int, wsp::DeviceTables> dev;        // per device ordinal
@@ -54,6 +56,9 @@ int hip_fail(hipError_t e, const char *what);
 // ---- host planner (plan.cpp) ---------------------------------------------
 int build_plan(int T, int H, int W, int nt, int nh, int nw, int method, wsp_plan_t &p);
 void relayout_perm(const wsp_plan_t &src, const wsp_plan_t &dst, std::vector<int32_t> &perm);
+// Window-local offset (dt, dh, dw) of every canonical token, packed as
+// dt | dh << 10 | dw << 21 (extents checked against 1024 / 2048 by the caller).
+void window_positions(const wsp_plan_t &p, std::vector<int32_t> &pos);
 // Attention work list; returns the grid size (items.size()).
 int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order,
                 std::vector<Item> &items);
@@ -62,6 +67,7 @@ int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int orde
 int device_offsets(wsp_plan_t &p, int dev, int32_t **out);
 int device_ids(wsp_plan_t &p, int dev, int32_t **out);
 int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out);
+int device_positions(wsp_plan_t &p, int dev, int32_t **out);
 int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
                  Item **out, int *count);
 
@@ -84,6 +90,12 @@ hipError_t launch_attn_f32(int head_dim, const float *q, const float *k, const f
                            float *ws, const int32_t *offsets, const int32_t *ids,
                            const Item *items, int n_items, int n_heads, int text_len, float scale,
                            hipStream_t s);
+// rope.hip: rows of x (perm[j], or j) rotated into y[j]; positions from the
+// packed table pos[cid[j]] (+ text_len on t) or, with pos == NULL, (j, j, j);
+// cs = [P][21] (cos, sin) pairs.  Head dim 128 only.
+hipError_t launch_rope(const void *x, void *y, const int32_t *perm, const int32_t *cid,
+                       const int32_t *pos, const float2 *cs, int64_t n_rows, int n_heads, int dtype,
+                       int text_len, hipStream_t s);
 // text_mean.hip
 hipError_t launch_text_mean(const float *ws, void *txt_out, int64_t per_window, int n_windows,
                             int dtype, hipStream_t s);
