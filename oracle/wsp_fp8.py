@@ -41,7 +41,8 @@ _POS_VALS = e4m3_decode(_POS_CODES)
 
 def e4m3_encode(x) -> np.ndarray:
     """Nearest E4M3 code (ties to the even code, i.e. even mantissa), |x|
-    saturated at 448.  x must be finite."""
+    saturated at 448, sign bit from x (so -0.0 and negative values that
+    round to zero give 0x80).  x must be finite."""
     x = np.asarray(x, dtype=np.float64)
     a = np.minimum(np.abs(x), E4M3_MAX)
     # nearest by exhaustive comparison against the 127 non-negative values
@@ -52,7 +53,9 @@ def e4m3_encode(x) -> np.ndarray:
     even = (_POS_CODES % 2 == 0)
     pick = np.where(cand & even, 1, 0) + np.where(cand, 1, 0)
     code = _POS_CODES[np.argmax(pick, axis=-1)]
-    return np.where(x < 0, code | 0x80, code).astype(np.uint8)
+    # the sign bit is kept whatever the magnitude rounds to (E4M3 has a
+    # signed zero, 0x80)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
 
 
 def fp8_amax(*tensors) -> np.ndarray:

@@ -16,8 +16,14 @@ def test_decode_closed_forms():
 
 
 def test_every_finite_code_round_trips():
-    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], dtype=np.uint8)
-    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes)   # 0x80 is -0.0
+
+
+def test_signed_zero():
+    assert O.e4m3_encode(-0.0) == 0x80 and O.e4m3_encode(0.0) == 0x00
+    assert O.e4m3_encode(-1e-12) == 0x80 and O.e4m3_encode(1e-12) == 0x00
+    assert O.e4m3_decode(np.uint8(0x80)) == 0.0 and np.signbit(O.e4m3_decode(np.uint8(0x80)))
 
 
 def test_ties_go_to_even_and_saturate():
