@@ -59,8 +59,11 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 def fp8_amax(*tensors) -> np.ndarray:
-    """Per-head max |x| over [rows, heads, dim] tensors (all of the same head count)."""
-    return np.max(np.stack([np.abs(np.asarray(t, dtype=np.float64)).max(axis=(0, 2)) for t in tensors]), axis=0)
+    """Per-head max |x| over [rows, heads, dim] tensors (all of the same head
+    count); tensors without rows add nothing (0 if all are empty)."""
+    heads = np.asarray(tensors[0]).shape[1]
+    per = [np.abs(np.asarray(t, dtype=np.float64)).max(axis=(0, 2)) for t in tensors if np.asarray(t).shape[0]]
+    return np.max(np.stack(per), axis=0) if per else np.zeros(heads)
 
 
 def fp8_scale(amax) -> np.ndarray:
