@@ -133,7 +133,7 @@ def main():
     row_bytes = Hh * D * 2
     stream = torch.cuda.current_stream()
 
-    ev = {"attn": [], "relayout": [], "fused_attn": [], "rope": []}
+    ev = {"attn": [], "relayout": [], "fused_attn": [], "rope": [], "qk8_attn": []}
 
     def timed(kind, fn, record):
         if record:
@@ -177,6 +177,21 @@ def main():
                 timed("rope", lambda n=n, p=p, dst=dst: W.rope_relayout(dev[n], canon, p, p, Lt, out=dst[n]),
                       record)
 
+    # E4M3 q / k codes (per-head scales), moved into each layout once, outside the timing.
+    amax_q, amax_k = W.fp8_amax(dev["q"], dev["txt_q"]), W.fp8_amax(dev["k"], dev["txt_k"])
+    tq8, tk8 = W.fp8_quantize(dev["txt_q"], amax_q), W.fp8_quantize(dev["txt_k"], amax_k)
+    q8c, k8c = W.fp8_quantize(dev["q"], amax_q), W.fp8_quantize(dev["k"], amax_k)
+    codes = [(W.relayout(q8c, canon, p), W.relayout(k8c, canon, p)) for p in plans]
+    del q8c, k8c
+
+    def step_qk8(record):
+        # The two layers on the FP8 q/k path (v, softmax and outputs bf16).
+        for li, p in enumerate(plans):
+            vv = bufs["v"] if li % 2 == 0 else bufs2["v"]
+            timed("qk8_attn", lambda li=li, p=p, vv=vv: W.window_attn_qk8(
+                p, codes[li][0], codes[li][1], vv, tq8, tk8, dev["txt_v"], amax_q, amax_k,
+                out=outs[li], txt_out=txts[li], workspace=ws), record)
+
     def run(fn):
         for _ in range(args.warmup):
             fn(False)
@@ -199,6 +214,7 @@ def main():
     ms_step, wall = run(step)
     ms_fused, _ = (None, None) if args.no_fused else run(step_fused)
     run(step_rope)
+    run(step_qk8)
     attn_ms = [a.elapsed_time(b) for a, b in ev["attn"]]
     rel_ms = [a.elapsed_time(b) for a, b in ev["relayout"]]
     step_flops = sum(flops)
@@ -239,6 +255,11 @@ def main():
                             "avg_launch_ms": round(rope_ms, 4),
                             "gbps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
                             "hbm_frac": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    q8_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["qk8_attn"]]))
+    res["fp8_qk_attention"] = {
+        "note": "q, k as OCP E4M3 codes (per-head scales) on the FP8 matrix cores; v, P, outputs bf16",
+        "avg_launch_ms": round(q8_ms, 4),
+        "attn_kernel_tflops": round(per_call_flops / (q8_ms * 1e-3) / 1e12, 2)}
     if ms_fused is not None:
         f_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["fused_attn"]]))
         res["fused_pass"] = {

@@ -261,6 +261,50 @@ int wsp_rope_text(const void *x, void *y, int text_len, int n_heads, int head_di
                   float theta, void *stream);
 
 /*
+ * wsp_fp8_amax -- per-head largest |x| of a [n_rows, n_heads, head_dim]
+ * tensor, max-accumulated into amax[n_heads] (float32, device memory; the
+ * caller zeroes it before the first call, then may accumulate several
+ * tensors -- e.g. the video and the text keys -- into one scale).
+ *
+ * Low-precision attention variant: the page "Scaling Video Training with
+ * Parallelism" reports that low precision pays off in a neighbouring system;
+ * the quantisation recipe here (per-head scale 448 / amax, OCP E4M3 codes) is
+ * this library's own.
+ * x  device, 16-byte aligned; dtype WSP_BF16 or WSP_F32; head_dim 64 or
+ *    128; a row may hold at most 32 KiB.
+ * Errors: WSP_EINVAL, WSP_EDEVICE.
+ */
+int wsp_fp8_amax(const void *x, int64_t n_rows, int n_heads, int head_dim, int dtype, float *amax,
+                 void *stream);
+
+/*
+ * wsp_fp8_quantize -- y = OCP E4M3 codes (1 byte each) of x * (448 /
+ * amax[head]): the scale a correctly rounded float32 division, the product
+ * one float32 multiply, then round to nearest even, saturated at +-448
+ * (amax 0 gives scale 1).  x and y [n_rows, n_heads, head_dim]; y holds one
+ * byte per element.  Arguments and errors as wsp_fp8_amax.
+ */
+int wsp_fp8_quantize(const void *x, void *y, int64_t n_rows, int n_heads, int head_dim, int dtype,
+                     const float *amax, void *stream);
+
+/*
+ * wsp_window_attn_qk8 -- wsp_window_attn_ex with E4M3 queries and keys.
+ *
+ * The scores come from the codes q8, k8, txt_q8, txt_k8 (wsp_fp8_quantize
+ * with the per-head amax_q of q and txt_q, amax_k of k and txt_k) on the
+ * gfx950 FP8 matrix cores and are dequantised by (amax_q/448)(amax_k/448);
+ * softmax, probabilities, v and the outputs are as in the bf16 path (v,
+ * txt_v, out, txt_out bfloat16).  Windows, text mean, flags
+ * (WSP_ATTN_IO_CANONICAL), workspace (as for WSP_BF16), stream and errors as
+ * wsp_window_attn_ex; head_dim must be 128.
+ */
+int wsp_window_attn_qk8(const wsp_plan_t *p, const void *q8, const void *k8, const void *v,
+                        const void *txt_q8, const void *txt_k8, const void *txt_v,
+                        const float *amax_q, const float *amax_k, int n_heads, int head_dim,
+                        int text_len, float scale, unsigned flags, void *out, void *txt_out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * wsp_set_attn_order -- process-wide dispatch order of wsp_window_attn
  * (enum wsp_order; default WSP_ORDER_LPT_XCD).  "Window-Aligned Sequence
  * Parallelism (SeedVR2)", section "Planner": ragged windows are balanced by

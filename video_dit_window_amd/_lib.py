@@ -39,6 +39,10 @@ _SIGNATURES = {
     "wsp_rope_relayout": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_int,
                                    ctypes.c_float, _c_vp]),
     "wsp_rope_text": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _c_vp]),
+    "wsp_fp8_amax": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp]),
+    "wsp_fp8_quantize": (_c_int, [_c_vp, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp]),
+    "wsp_window_attn_qk8": (_c_int, [_c_vp] * 9 + [_c_int, _c_int, _c_int, ctypes.c_float, ctypes.c_uint,
+                                                    _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "wsp_set_attn_order": (_c_int, [_c_int]),
     "wsp_last_error": (ctypes.c_char_p, []),
     "wsp_version": (_c_int, []),
@@ -239,6 +243,62 @@ def rope_text(x, theta=None, out=None, stream=None):
         _dev_ptr(x, "x"), _dev_ptr(out, "out"), x.shape[0], x.shape[1], x.shape[2], _dtype_code(x.dtype),
         ctypes.c_float(0.0 if theta is None else theta), _stream(stream)))
     return out
+
+
+def fp8_amax(*tensors, amax=None, stream=None):
+    """Per-head max |x| (float32 [heads]) over [rows, heads, dim] tensors (wsp_fp8_amax)."""
+    torch = _torch()
+    H = tensors[0].shape[1]
+    if amax is None:
+        amax = torch.zeros(H, dtype=torch.float32, device=tensors[0].device)
+    for t in tensors:
+        if t.dim() != 3 or t.shape[1] != H:
+            raise ValueError("tensors must be [rows, heads, dim] with one head count")
+        if t.shape[0] == 0:
+            continue
+        _check("wsp_fp8_amax", lib().wsp_fp8_amax(_dev_ptr(t, "x"), t.shape[0], H, t.shape[2],
+                                                  _dtype_code(t.dtype), _dev_ptr(amax, "amax"), _stream(stream)))
+    return amax
+
+
+def fp8_quantize(x, amax, out=None, stream=None):
+    """E4M3 codes (torch.uint8, same shape) of x * 448/amax[head] (wsp_fp8_quantize)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if x.shape[0]:
+        _check("wsp_fp8_quantize", lib().wsp_fp8_quantize(
+            _dev_ptr(x, "x"), _dev_ptr(out, "out"), x.shape[0], x.shape[1], x.shape[2], _dtype_code(x.dtype),
+            _dev_ptr(amax, "amax"), _stream(stream)))
+    return out
+
+
+def window_attn_qk8(p: Plan, q8, k8, v, txt_q8, txt_k8, txt_v, amax_q, amax_k, scale=None, out=None,
+                    txt_out=None, workspace=None, stream=None, canonical=False):
+    """Window attention with E4M3 q / k codes and bf16 v (wsp_window_attn_qk8)."""
+    torch = _torch()
+    N, Hh, D = v.shape
+    Lt = txt_v.shape[0]
+    if q8.shape != v.shape or k8.shape != v.shape or q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
+        raise ValueError("q8 / k8 must be uint8 codes shaped like v")
+    if v.dtype != torch.bfloat16 or txt_v.dtype != torch.bfloat16:
+        raise ValueError("v and txt_v must be bfloat16")
+    if out is None:
+        out = torch.empty_like(v)
+    if txt_out is None:
+        txt_out = torch.empty_like(txt_v)
+    need = window_attn_workspace(p, Hh, D, Lt, BF16)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=v.device)
+    tp = [(_dev_ptr(t, n) if Lt else _c_vp(0)) for n, t in
+          (("txt_q8", txt_q8), ("txt_k8", txt_k8), ("txt_v", txt_v), ("txt_out", txt_out))]
+    _check("wsp_window_attn_qk8", lib().wsp_window_attn_qk8(
+        p.handle, _dev_ptr(q8, "q8"), _dev_ptr(k8, "k8"), _dev_ptr(v, "v"), tp[0], tp[1], tp[2],
+        _dev_ptr(amax_q, "amax_q"), _dev_ptr(amax_k, "amax_k"), Hh, D, Lt,
+        ctypes.c_float(0.0 if scale is None else float(scale)), IO_CANONICAL if canonical else IO_LAYOUT,
+        _dev_ptr(out, "out"), tp[3], _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, txt_out
 
 
 def set_attn_order(order: int):

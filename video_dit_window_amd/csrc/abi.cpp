@@ -439,6 +439,101 @@ int wsp_rope_text(const void *x, void *y, int text_len, int n_heads, int head_di
     return WSP_OK;
 }
 
+int wsp_fp8_amax(const void *x, int64_t n_rows, int n_heads, int head_dim, int dtype, float *amax,
+                 void *stream) {
+    g_last_error.clear();
+    if (!amax) return fail(WSP_EINVAL, "amax is NULL");
+    if (n_rows < 0) return fail(WSP_EINVAL, "n_rows must be >= 0");
+    if (n_rows > 0 && !x) return fail(WSP_EINVAL, "x is NULL");
+    if (x && !aligned16(x)) return fail(WSP_EINVAL, "x must be 16-byte aligned");
+    if (!aligned16(amax) && (reinterpret_cast<uintptr_t>(amax) & 3u))
+        return fail(WSP_EINVAL, "amax must be 4-byte aligned");
+    if (head_dim != 64 && head_dim != 128) return fail(WSP_EINVAL, "head_dim must be 64 or 128");
+    if (dtype != WSP_F32 && dtype != WSP_BF16) return fail(WSP_EINVAL, "unknown dtype");
+    const int elem = dtype == WSP_BF16 ? 2 : 4;
+    if (n_heads < 1 || int64_t(n_heads) * head_dim * elem / 16 > fp8_max_row_chunks())
+        return fail(WSP_EINVAL, "n_heads out of range (a row may hold at most " +
+                                    std::to_string(fp8_max_row_chunks() * 16) + " bytes)");
+    hipError_t e = launch_fp8_amax(x, amax, n_rows, n_heads, head_dim, dtype, hipStream_t(stream));
+    if (e != hipSuccess) return hip_fail(e, "fp8 amax kernel launch");
+    return WSP_OK;
+}
+
+int wsp_fp8_quantize(const void *x, void *y, int64_t n_rows, int n_heads, int head_dim, int dtype,
+                     const float *amax, void *stream) {
+    g_last_error.clear();
+    if (!amax) return fail(WSP_EINVAL, "amax is NULL");
+    if (n_rows < 0) return fail(WSP_EINVAL, "n_rows must be >= 0");
+    if (n_rows > 0 && (!x || !y)) return fail(WSP_EINVAL, "x or y is NULL");
+    if ((x && !aligned16(x)) || (y && !aligned16(y)))
+        return fail(WSP_EINVAL, "x and y must be 16-byte aligned");
+    if (head_dim != 64 && head_dim != 128) return fail(WSP_EINVAL, "head_dim must be 64 or 128");
+    if (dtype != WSP_F32 && dtype != WSP_BF16) return fail(WSP_EINVAL, "unknown dtype");
+    if (n_heads < 1 || n_heads > 32767) return fail(WSP_EINVAL, "n_heads must be in 1..32767");
+    hipError_t e = launch_fp8_quantize(x, y, amax, n_rows, n_heads, head_dim, dtype, hipStream_t(stream));
+    if (e != hipSuccess) return hip_fail(e, "fp8 quantize kernel launch");
+    return WSP_OK;
+}
+
+int wsp_window_attn_qk8(const wsp_plan_t *pc, const void *q8, const void *k8, const void *v,
+                        const void *txt_q8, const void *txt_k8, const void *txt_v,
+                        const float *amax_q, const float *amax_k, int n_heads, int head_dim,
+                        int text_len, float scale, unsigned flags, void *out, void *txt_out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error.clear();
+    if (flags & ~unsigned(WSP_ATTN_IO_CANONICAL)) return fail(WSP_EINVAL, "unknown attention flags");
+    const bool gather = (flags & WSP_ATTN_IO_CANONICAL) != 0;
+    if (head_dim != 128) return fail(WSP_EINVAL, "the fp8 q/k attention needs head_dim 128");
+    if (!amax_q || !amax_k) return fail(WSP_EINVAL, "amax_q and amax_k must be non-NULL");
+    size_t need = 0;
+    int rc = wsp_window_attn_workspace(pc, n_heads, head_dim, text_len, WSP_BF16, &need);
+    if (rc) return rc;
+    wsp_plan_t *p = const_cast<wsp_plan_t *>(pc);
+    for (const void *ptr : {q8, k8, v, static_cast<const void *>(out)}) {
+        if (!ptr) return fail(WSP_EINVAL, "q, k, v and out must be non-NULL");
+        if (!aligned16(ptr)) return fail(WSP_EINVAL, "q, k, v and out must be 16-byte aligned");
+    }
+    if (out == q8 || out == k8 || out == v) return fail(WSP_EINVAL, "out must not alias q, k or v");
+    if (text_len > 0) {
+        for (const void *ptr : {txt_q8, txt_k8, txt_v, static_cast<const void *>(txt_out)}) {
+            if (!ptr) return fail(WSP_EINVAL, "text tensors and txt_out must be non-NULL when text_len > 0");
+            if (!aligned16(ptr)) return fail(WSP_EINVAL, "text tensors must be 16-byte aligned");
+        }
+        if (!workspace || workspace_bytes < need)
+            return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) +
+                                            " bytes required, got " + std::to_string(workspace_bytes));
+        if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
+    }
+    {
+        const int64_t row_bytes = int64_t(n_heads) * head_dim * 2;
+        const int64_t rows = std::max<int64_t>(gather ? p->max_span : p->max_rows, text_len);
+        if (rows * row_bytes >= (int64_t(1) << 31))
+            return fail(WSP_ERANGE, gather ? "a window's canonical rows span 2 GiB or more"
+                                           : "a window's rows (or the text rows) take 2 GiB or more");
+    }
+    if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
+    const int order = g_attn_order.load();
+    int dev = 0;
+    WSP_HIP(hipGetDevice(&dev));
+    int32_t *d_off = nullptr, *d_ids = nullptr;
+    if ((rc = device_offsets(*p, dev, &d_off))) return rc;
+    if (gather && (rc = device_ids(*p, dev, &d_ids))) return rc;
+    Item *items = nullptr;
+    int n_items = 0;
+    if ((rc = device_items(*p, dev, n_heads, text_len, attn_qk8_tile_m(), order, &items, &n_items)))
+        return rc;
+    hipStream_t s = hipStream_t(stream);
+    float *ws = static_cast<float *>(workspace);
+    hipError_t e = launch_attn_qk8(q8, k8, v, txt_q8, txt_k8, txt_v, out, ws, d_off, d_ids, items,
+                                   n_items, amax_q, amax_k, n_heads, text_len, scale, s);
+    if (e != hipSuccess) return hip_fail(e, "fp8 attention kernel launch");
+    if (text_len > 0) {
+        e = launch_text_mean(ws, txt_out, int64_t(text_len) * n_heads * head_dim, p->nwin, WSP_BF16, s);
+        if (e != hipSuccess) return hip_fail(e, "text mean kernel launch");
+    }
+    return WSP_OK;
+}
+
 int wsp_set_attn_order(int order) {
     g_last_error.clear();
     if (order != WSP_ORDER_LPT_XCD && order != WSP_ORDER_LPT && order != WSP_ORDER_ID)

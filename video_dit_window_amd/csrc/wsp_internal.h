@@ -96,6 +96,19 @@ hipError_t launch_attn_f32(int head_dim, const float *q, const float *k, const f
 hipError_t launch_rope(const void *x, void *y, const int32_t *perm, const int32_t *cid,
                        const int32_t *pos, const float2 *cs, int64_t n_rows, int n_heads, int dtype,
                        int text_len, hipStream_t s);
+// fp8.hip: per-head amax (max-accumulated as float bits) and E4M3 codes.
+int fp8_max_row_chunks();
+hipError_t launch_fp8_amax(const void *x, float *amax, int64_t n_rows, int n_heads, int head_dim,
+                           int dtype, hipStream_t s);
+hipError_t launch_fp8_quantize(const void *x, void *y, const float *amax, int64_t n_rows,
+                               int n_heads, int head_dim, int dtype, hipStream_t s);
+// attn_qk8.hip: attention with E4M3 q / k codes (head dim 128, bf16 v / out).
+int attn_qk8_tile_m();
+hipError_t launch_attn_qk8(const void *q, const void *k, const void *v, const void *tq,
+                           const void *tk, const void *tv, void *out, float *ws,
+                           const int32_t *offsets, const int32_t *ids, const Item *items,
+                           int n_items, const float *amax_q, const float *amax_k, int n_heads,
+                           int text_len, float scale, hipStream_t s);
 // text_mean.hip
 hipError_t launch_text_mean(const float *ws, void *txt_out, int64_t per_window, int n_windows,
                             int dtype, hipStream_t s);
