@@ -18,7 +18,10 @@ constexpr int kAmaxThreads = 256;
 constexpr int kAmaxSlots = 8;  // 16-byte chunks per thread and row: rows up to 32 KiB
 
 // amax[h] = max(amax[h], |x[r, h, :]|) over all rows, as float bits (the bit
-// patterns of non-negative floats order like unsigned integers).
+// patterns of non-negative floats order like unsigned integers).  Each thread
+// keeps the running maximum of fixed chunk columns over a strided set of rows
+// (four rows in flight); the lanes sharing a head then reduce by shuffles and
+// one lane per head and wave issues the atomic.
 template <bool BF16>
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const u32x4 *__restrict__ x,
                                                             unsigned int *__restrict__ amax,
@@ -27,29 +30,40 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const u32x4 *__restr
     uint32_t m[kAmaxSlots];
 #pragma unroll
     for (int s = 0; s < kAmaxSlots; ++s) m[s] = 0;
-    for (int64_t r = blockIdx.x; r < n_rows; r += gridDim.x) {
-        const u32x4 *row = x + r * chunks;
+    auto absmax = [](uint32_t acc, const u32x4 &v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (BF16) {
+                acc = max(acc, max((v[e] & 0x7FFFu) << 16, (v[e] >> 16 & 0x7FFFu) << 16));
+            } else {
+                acc = max(acc, v[e] & 0x7FFFFFFFu);
+            }
+        }
+        return acc;
+    };
+    constexpr int kRowsInFlight = 4;
+    const int64_t stride = int64_t(gridDim.x) * kRowsInFlight;
+    for (int64_t r0 = int64_t(blockIdx.x) * kRowsInFlight; r0 < n_rows; r0 += stride) {
 #pragma unroll
         for (int s = 0; s < kAmaxSlots; ++s) {
             const int c = threadIdx.x + s * kAmaxThreads;
             if (c < chunks) {
-                const u32x4 v = row[c];
+                u32x4 v[kRowsInFlight];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (BF16) {
-                        const uint32_t lo = (v[e] & 0x7FFFu) << 16, hi = (v[e] >> 16 & 0x7FFFu) << 16;
-                        m[s] = max(m[s], max(lo, hi));
-                    } else {
-                        m[s] = max(m[s], v[e] & 0x7FFFFFFFu);
-                    }
-                }
+                for (int i = 0; i < kRowsInFlight; ++i)
+                    v[i] = r0 + i < n_rows ? x[(r0 + i) * chunks + c] : u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < kRowsInFlight; ++i) m[s] = absmax(m[s], v[i]);
             }
         }
     }
+    // Lanes c .. c+cph-1 (consecutive in the wave; cph is 8, 16 or 32) share a head.
 #pragma unroll
     for (int s = 0; s < kAmaxSlots; ++s) {
         const int c = threadIdx.x + s * kAmaxThreads;
-        if (c < chunks) atomicMax(amax + c / chunks_per_head, m[s]);
+        uint32_t v = c < chunks ? m[s] : 0u;
+        for (int d = 1; d < chunks_per_head; d <<= 1) v = max(v, uint32_t(__shfl_xor(int(v), d, 64)));
+        if (c < chunks && c % chunks_per_head == 0) atomicMax(amax + c / chunks_per_head, v);
     }
 }
 
@@ -106,7 +120,7 @@ hipError_t launch_fp8_amax(const void *x, float *amax, int64_t n_rows, int n_hea
     if (n_rows <= 0) return hipSuccess;
     const int elem = dtype == WSP_BF16 ? 2 : 4;
     const int cph = head_dim * elem / 16, chunks = n_heads * cph;
-    const unsigned grid = unsigned(std::min<int64_t>(n_rows, 2048));
+    const unsigned grid = unsigned(std::min<int64_t>((n_rows + 3) / 4, 1024));
     const u32x4 *xs = static_cast<const u32x4 *>(x);
     unsigned int *bits = reinterpret_cast<unsigned int *>(amax);
     if (dtype == WSP_BF16)
