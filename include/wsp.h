@@ -67,6 +67,13 @@ enum wsp_order {
     WSP_ORDER_ID = 2       /* window id order                                    */
 };
 
+/* Schedule of the bf16 attention kernel (wsp_set_attn_schedule). */
+enum wsp_schedule {
+    WSP_SCHED_AUTO = 0,       /* by mean window length (wsp_set_attn_schedule) */
+    WSP_SCHED_PERSISTENT = 1, /* resident work groups walk per-CU item lists   */
+    WSP_SCHED_PER_ITEM = 2    /* one work group per item                       */
+};
+
 /*
  * wsp_plan -- build the window tables of one layout.
  *
@@ -312,6 +319,21 @@ int wsp_window_attn_qk8(const wsp_plan_t *p, const void *q8, const void *k8, con
  * Results do not depend on the order.  Errors: WSP_EINVAL.
  */
 int wsp_set_attn_order(int order);
+
+/*
+ * wsp_set_attn_schedule -- process-wide schedule of the bf16 attention
+ * kernel (enum wsp_schedule; default WSP_SCHED_AUTO).
+ * WSP_SCHED_PERSISTENT: one resident work group per compute unit walks a
+ * host-built list of (window, head, 256-query-row) items, fetching the next
+ * item's first K/V tile and query rows while the current item finishes.
+ * WSP_SCHED_PER_ITEM: one work group per item.  WSP_SCHED_AUTO: persistent
+ * when a window's joint sequence averages fewer than 1024 rows (short items,
+ * where the per-item start-up is a visible share), else per item.  All run
+ * the same per-tile arithmetic in the same order, so results are
+ * bit-identical; the order set by wsp_set_attn_order applies to all.
+ * Errors: WSP_EINVAL.
+ */
+int wsp_set_attn_schedule(int schedule);
 
 /* wsp_last_error -- message of the calling thread's last failed call ("" if none). */
 const char *wsp_last_error(void);

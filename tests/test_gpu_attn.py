@@ -105,6 +105,9 @@ MID = [  # (name, T, H, W, nt, nh, nw, heads, D, Lt)
     ("mid_bf16_text1", 6, 30, 52, 2, 3, 3, 2, 128, 1),
     ("small_windows_bf16", 5, 24, 40, 3, 9, 12, 2, 128, 19),
     ("one_window_bf16", 3, 12, 20, 1, 1, 1, 2, 128, 77),
+    # windows of at most 45 tokens: a joint sequence of one 64-key tile
+    ("tiny_windows_bf16", 4, 20, 36, 4, 9, 9, 2, 128, 0),
+    ("tiny_windows_text_d64", 4, 20, 36, 4, 9, 9, 2, 64, 19),
 ]
 
 
@@ -145,6 +148,64 @@ def test_bf16_order_independent_and_deterministic(gpu):
     for o, t in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
         assert torch.equal(t.view(torch.int16), outs[0][1].view(torch.int16))
+
+
+@pytest.mark.parametrize("case", MID, ids=[c[0] for c in MID])
+@pytest.mark.parametrize("canonical", [False, True], ids=["layout_io", "canonical_io"])
+def test_bf16_schedules_bit_identical(gpu, case, canonical):
+    """The persistent schedule (resident work groups walking per-CU item
+    lists) and one work group per item run the same per-tile
+    arithmetic in the same order: identical bits, for both I/O orders."""
+    import torch
+    w = I.custom(*case, "bf16", index=300 + MID.index(case))
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    d = upload(I.qkv(w), "bf16")
+    res = {}
+    for method in (W.REGULAR, W.SHIFTED):
+        p = W.Plan(*geo, method)
+        for sched in (W.SCHED_PERSISTENT, W.SCHED_PER_ITEM):
+            W.set_attn_schedule(sched)
+            try:
+                o, t = W.window_attn(p, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"],
+                                     canonical=canonical)
+            finally:
+                W.set_attn_schedule(W.SCHED_AUTO)
+            res[(method, sched)] = (o, t)
+    torch.cuda.synchronize()
+    for method in (W.REGULAR, W.SHIFTED):
+        (o1, t1), (o2, t2) = res[(method, W.SCHED_PERSISTENT)], res[(method, W.SCHED_PER_ITEM)]
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"{w.name} method {method}: video"
+        if w.text_len:
+            assert torch.equal(t1.view(torch.int16), t2.view(torch.int16)), f"{w.name} method {method}: text"
+
+
+@pytest.mark.parametrize("canonical", [False, True], ids=["layout_io", "canonical_io"])
+def test_1080p_schedules_bit_identical(gpu, canonical):
+    """Persistent and per-item schedules agree bit for bit on the full 1080p
+    grid (both layouts), in the launch configuration the benchmark times."""
+    import torch
+    w = I.WORKLOADS["1080p_bf16"]
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1080)
+
+    def rnd(rows):
+        return (torch.randn((rows, w.heads, w.head_dim), device="cuda", generator=g) / 11.3).to(torch.bfloat16)
+    q, k, v = (rnd(w.n_tokens) for _ in range(3))
+    tq, tk, tv = (rnd(w.text_len) for _ in range(3))
+    for method in (W.REGULAR, W.SHIFTED):
+        p = W.Plan(*geo, method)
+        outs = []
+        for sched in (W.SCHED_PERSISTENT, W.SCHED_PER_ITEM):
+            W.set_attn_schedule(sched)
+            try:
+                outs.append(W.window_attn(p, q, k, v, tq, tk, tv, canonical=canonical))
+            finally:
+                W.set_attn_schedule(W.SCHED_AUTO)
+        torch.cuda.synchronize()
+        log(f"  1080p method {method} canonical={canonical}: comparing schedules")
+        assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+        assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
 
 
 # ------------------------------------------------------------------ full-size, sampled

@@ -77,6 +77,8 @@ FUSED_BF16 = [  # (name, T, H, W, nt, nh, nw, heads, D, Lt)
     ("fmid_bf16_text1", 6, 30, 52, 2, 3, 3, 2, 128, 1),
     ("fsmall_windows_bf16", 5, 24, 40, 3, 9, 12, 2, 128, 19),
     ("fone_window_bf16", 3, 12, 20, 1, 1, 1, 2, 128, 77),
+    ("ftiny_windows_bf16", 4, 20, 36, 4, 9, 9, 2, 128, 0),
+    ("ftiny_windows_text_d64", 4, 20, 36, 4, 9, 9, 2, 64, 19),
 ]
 
 

@@ -180,6 +180,14 @@ def test_rope_argument_errors():
     assert L.wsp_rope_text(a, b, 0, 4, 128, W.BF16, f0, None) == 0      # nothing to do
 
 
+def test_attn_schedule_option():
+    L = raw()
+    assert L.wsp_set_attn_schedule(3) == -1
+    assert L.wsp_set_attn_schedule(-1) == -1
+    for sc in (W.SCHED_PER_ITEM, W.SCHED_PERSISTENT, W.SCHED_AUTO):
+        W.set_attn_schedule(sc)
+
+
 def test_attn_order_option():
     L = raw()
     assert L.wsp_set_attn_order(7) == -1

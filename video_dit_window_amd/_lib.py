@@ -19,6 +19,7 @@ REGULAR, SHIFTED, CANONICAL = 0, 1, 2
 IO_LAYOUT, IO_CANONICAL = 0, 1
 F32, BF16 = 0, 1
 ORDER_LPT_XCD, ORDER_LPT, ORDER_ID = 0, 1, 2
+SCHED_AUTO, SCHED_PERSISTENT, SCHED_PER_ITEM = 0, 1, 2
 METHODS = {"regular": REGULAR, "shifted": SHIFTED, "canonical": CANONICAL}
 
 _c_int, _c_i64, _c_sz, _c_vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -44,6 +45,7 @@ _SIGNATURES = {
     "wsp_window_attn_qk8": (_c_int, [_c_vp] * 9 + [_c_int, _c_int, _c_int, ctypes.c_float, ctypes.c_uint,
                                                     _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "wsp_set_attn_order": (_c_int, [_c_int]),
+    "wsp_set_attn_schedule": (_c_int, [_c_int]),
     "wsp_last_error": (ctypes.c_char_p, []),
     "wsp_version": (_c_int, []),
 }
@@ -303,6 +305,10 @@ def window_attn_qk8(p: Plan, q8, k8, v, txt_q8, txt_k8, txt_v, amax_q, amax_k, s
 
 def set_attn_order(order: int):
     _check("wsp_set_attn_order", lib().wsp_set_attn_order(order))
+
+
+def set_attn_schedule(schedule: int):
+    _check("wsp_set_attn_schedule", lib().wsp_set_attn_schedule(schedule))
 
 
 def version() -> int:

@@ -15,6 +15,7 @@ namespace wsp {
 namespace {
 thread_local std::string g_last_error;
 std::atomic<int> g_attn_order{WSP_ORDER_LPT_XCD};
+std::atomic<int> g_attn_sched{WSP_SCHED_AUTO};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -123,8 +124,8 @@ int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out) 
 }
 
 int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
-                 Item **out, int *count) {
-    const auto key = std::make_tuple(n_heads, text_len, bm, order);
+                 int n_groups, Item **out, int *count) {
+    const auto key = std::make_tuple(n_heads, text_len, bm, order, n_groups);
     {
         std::lock_guard<std::mutex> lk(p.mu);
         auto &m = p.dev[dev].items;
@@ -138,7 +139,7 @@ int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int 
     std::vector<Item> items;
     int rc;
     try {
-        rc = build_items(p, n_heads, text_len, bm, order, items);
+        rc = build_items(p, n_heads, text_len, bm, order, n_groups, items);
     } catch (const std::bad_alloc &) {
         return fail(WSP_ENOMEM, "host allocation of the attention work list failed");
     }
@@ -308,21 +309,37 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
     }
     if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
     const int order = g_attn_order.load();
-    const int bm = dtype == WSP_BF16 ? attn_bf16_tile_m(head_dim, gather) : attn_f32_tile_m(head_dim);
+    // Persistent work groups pay off when items are short: their per-item
+    // start-up (query rows and first K/V tile) is then a visible share.
+    const int sched = g_attn_sched.load();
+    const bool short_items = (double(p->n) / double(p->nwin) + text_len) < 1024.0;
+    const bool persist =
+        dtype == WSP_BF16 && (sched == WSP_SCHED_PERSISTENT || (sched == WSP_SCHED_AUTO && short_items));
+    const int bm = dtype != WSP_BF16 ? attn_f32_tile_m(head_dim)
+                   : persist        ? attn_bf16_persist_tile_m()
+                                    : attn_bf16_tile_m(head_dim, gather);
 
     int dev = 0;
     WSP_HIP(hipGetDevice(&dev));
+    int n_groups = 0;
+    if (persist) {
+        WSP_HIP(hipDeviceGetAttribute(&n_groups, hipDeviceAttributeMultiprocessorCount, dev));
+        if (n_groups < 1) return fail(WSP_EDEVICE, "device reports no compute units");
+    }
     int32_t *d_off = nullptr;
     if ((rc = device_offsets(*p, dev, &d_off))) return rc;
     int32_t *d_ids = nullptr;
     if (gather && (rc = device_ids(*p, dev, &d_ids))) return rc;
     Item *items = nullptr;
     int n_items = 0;
-    if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, &items, &n_items))) return rc;
+    if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, n_groups, &items, &n_items))) return rc;
     hipStream_t s = hipStream_t(stream);
     float *ws = static_cast<float *>(workspace);
     hipError_t e;
-    if (dtype == WSP_BF16)
+    if (persist)
+        e = launch_attn_bf16_persist(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, d_ids,
+                                     items, n_groups, n_items / n_groups, n_heads, text_len, scale, s);
+    else if (dtype == WSP_BF16)
         e = launch_attn_bf16(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, d_ids,
                              items, n_items, n_heads, text_len, scale, s);
     else
@@ -520,7 +537,7 @@ int wsp_window_attn_qk8(const wsp_plan_t *pc, const void *q8, const void *k8, co
     if (gather && (rc = device_ids(*p, dev, &d_ids))) return rc;
     Item *items = nullptr;
     int n_items = 0;
-    if ((rc = device_items(*p, dev, n_heads, text_len, attn_qk8_tile_m(), order, &items, &n_items)))
+    if ((rc = device_items(*p, dev, n_heads, text_len, attn_qk8_tile_m(), order, 0, &items, &n_items)))
         return rc;
     hipStream_t s = hipStream_t(stream);
     float *ws = static_cast<float *>(workspace);
@@ -539,6 +556,14 @@ int wsp_set_attn_order(int order) {
     if (order != WSP_ORDER_LPT_XCD && order != WSP_ORDER_LPT && order != WSP_ORDER_ID)
         return fail(WSP_EINVAL, "unknown attention order " + std::to_string(order));
     g_attn_order.store(order);
+    return WSP_OK;
+}
+
+int wsp_set_attn_schedule(int schedule) {
+    g_last_error.clear();
+    if (schedule != WSP_SCHED_AUTO && schedule != WSP_SCHED_PERSISTENT && schedule != WSP_SCHED_PER_ITEM)
+        return fail(WSP_EINVAL, "unknown attention schedule");
+    g_attn_sched.store(schedule);
     return WSP_OK;
 }
 

@@ -344,287 +344,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 #endif
 }
 
-
-// ---------------------------------------------------------------------------
-// Ping-pong variant.  A work group is 8 wavefronts in two groups of 4 (one
-// wavefront of each group per SIMD) covering 2 x 128 query rows of the same
-// (window, head); both groups read the same K/V tiles.  Work is split into
-// steps; step j is two phases separated by work-group barriers:
-//     phase 0:  group 0  MFMA:    O += V_{j-1}^T P_{j-1}^T,  S_j = K_j Q^T
-//               group 1  softmax: P_{j-1} from S_{j-1}
-//     phase 1:  group 0  softmax: P_j from S_j
-//               group 1  MFMA:    O += V_{j-1}^T P_{j-1}^T,  S_j = K_j Q^T
-// so on every SIMD one wavefront feeds the matrix cores while the other runs
-// its softmax on the vector ALUs.  The LDS stage of step j holds K_j and
-// V_{j-1}; four stages let the DMA for step j+3 run during step j.
-constexpr int kPPWaves = 8;
-constexpr int kPPThreads = 64 * kPPWaves;
-constexpr int kPPBM = 32 * kPPWaves;  // query rows per work group
-constexpr int kStages = 4;
-
-template <int D>
-__global__ __launch_bounds__(kPPThreads) void attn_bf16_pp_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const uint16_t *__restrict__ tq,
-    const uint16_t *__restrict__ tk, const uint16_t *__restrict__ tv,
-    uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
-    const Item *__restrict__ items, int H, int Lt, float c2) {
-#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
-    using S_ = Shape<D, kPPWaves>;
-    constexpr int LOADS = kBN / S_::ROWS_PER_LOAD / kPPWaves;  // DMAs per wave per tile
-    static_assert(LOADS * S_::ROWS_PER_LOAD * kPPWaves == kBN, "tile must split over the waves");
-    // Each stage: K tile, then V tile.  Separate arrays keep the DMA of one
-    // stage and the LDS reads of another visibly independent.
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * S_::TILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[2 * S_::TILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage2[2 * S_::TILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage3[2 * S_::TILE];
-
-    const Item it = items[blockIdx.x];
-    if (it.x < 0) return;
-    const int w = it.x, h = it.y >> 16, qt = it.y & 0xFFFF;
-    const int64_t off = offsets[w];
-    const int Lw = offsets[w + 1] - int(off);
-    const int M = Lw + Lt;
-    const int64_t rs = int64_t(H) * D, hd = int64_t(h) * D;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int group = wave >> 2, wig = wave & 3;
-    const int l32 = lane & 31, hh = lane >> 5;
-
-    bf16x8 Qr[S_::KSTEPS];
-    const int qrow = qt * kPPBM + group * 128 + wig * 32 + l32;
-    {
-        bool vid;
-        const int64_t o = joint_off(qrow, Lw, M, off, rs, vid) + hd;
-        const uint16_t *p = (vid ? q : tq) + o;
-#pragma unroll
-        for (int s = 0; s < S_::KSTEPS; ++s)
-            Qr[s] = *reinterpret_cast<const bf16x8 *>(p + 16 * s + 8 * hh);
-    }
-
-    // DMA.  Wave `wave` moves rows wave*8 + ROWS_PER_LOAD*i + lane/CH of a
-    // tile; each lane's 16 bytes land at LDS chunk lane%CH of its row and
-    // come from the row's chunk (lane%CH) ^ swz(row).
-    const int drow0 = wave * (kBN / kPPWaves) + lane / S_::CH;
-    const int dpc = lane % S_::CH;
-    int dchunk[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) dchunk[i] = 8 * (dpc ^ swz<D>(drow0 + S_::ROWS_PER_LOAD * i));
-    const uint32_t row_bytes = uint32_t(rs) * 2u;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(k + off * rs + hd), 0, int(uint32_t(Lw) * row_bytes), kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(v + off * rs + hd), 0, int(uint32_t(Lw) * row_bytes), kBufferFlags);
-    int dvoff[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-        dvoff[i] = (drow0 + S_::ROWS_PER_LOAD * i) * int(row_bytes) + 2 * dchunk[i];
-    // One tile of K (or V) rows into dst: buffer loads when the tile holds
-    // only video rows, else row by row (text rows, clamped end).
-    auto dma_tile = [&](uint8_t LDS_AS *dst, const __amdgpu_buffer_rsrc_t &rsrc, const uint16_t *vid_base,
-                        const uint16_t *txt_base, int jt) {
-        if ((jt + 1) * kBN <= Lw) {
-            const int soff = jt * kBN * int(row_bytes);
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int lo = (wave * (kBN / kPPWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void LDS_AS *)(dst + lo), 16, dvoff[i], soff, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                bool vid;
-                const int64_t o = joint_off(jt * kBN + drow0 + S_::ROWS_PER_LOAD * i, Lw, M, off, rs, vid) +
-                                  hd + dchunk[i];
-                const int lo = (wave * (kBN / kPPWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
-                __builtin_amdgcn_global_load_lds((vid ? vid_base : txt_base) + o, (void LDS_AS *)(dst + lo), 16,
-                                                 0, 0);
-            }
-        }
-    };
-    const int ntiles = (M + kBN - 1) / kBN;
-    // The stage of step j: K_j and V_{j-1}.  Every step issues the same number
-    // of DMAs (tiles past either end repeat a valid tile), so one constant
-    // wait count fits every step.
-    auto dma_step = [&](uint8_t LDS_AS *dst, int j) {
-        dma_tile(dst, krs, k, tk, min(j, ntiles - 1));
-        dma_tile(dst + S_::TILE, vrs, v, tv, max(min(j - 1, ntiles - 1), 0));
-    };
-
-    int kaddr[S_::KSTEPS];
-#pragma unroll
-    for (int s = 0; s < S_::KSTEPS; ++s)
-        kaddr[s] = l32 * S_::ROW + 16 * ((2 * s + hh) ^ swz<D>(l32));
-    const int gi = lane & 15, ghalf = (lane >> 4) & 1;
-    int vaddr[S_::DT][2];
-#pragma unroll
-    for (int t = 0; t < S_::DT; ++t)
-#pragma unroll
-        for (int B = 0; B < 2; ++B) {
-            const int row = 8 * B + 4 * hh + (gi >> 2);
-            const int dim = 32 * t + 16 * ghalf + 4 * (gi & 3);
-            vaddr[t][B] = S_::TILE + row * S_::ROW + 16 * ((dim >> 3) ^ swz<D>(row)) + 2 * (dim & 7);
-        }
-
-    f32x16 O[S_::DT];
-#pragma unroll
-    for (int t = 0; t < S_::DT; ++t) O[t] = f32x16{};
-    f32x16 S[2] = {f32x16{}, f32x16{}};
-    bf16x8 P[4];
-    float m_run = -INFINITY, l_run = 0.f;
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-
-    // Matrix phase of step j: PV of tile j-1, then S of tile j.
-    auto mfma_phase = [&](const uint8_t LDS_AS *cur, int j) {
-        if (j >= 1) {
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs)
-#pragma unroll
-                for (int t = 0; t < S_::DT; ++t) {
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (s16x4 LDS_AS *)(cur + vaddr[t][0] + cs * 16 * S_::ROW));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (s16x4 LDS_AS *)(cur + vaddr[t][1] + cs * 16 * S_::ROW));
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-                    O[t] = mfma(a, P[cs], O[t]);
-                }
-        }
-        if (j < ntiles) {
-            S[0] = S[1] = f32x16{};
-#pragma unroll
-            for (int s = 0; s < S_::KSTEPS; ++s)
-#pragma unroll
-                for (int mk = 0; mk < 2; ++mk) {
-                    const bf16x8 a =
-                        *reinterpret_cast<const bf16x8 LDS_AS *>(cur + kaddr[s] + mk * 32 * S_::ROW);
-                    S[mk] = mfma(a, Qr[s], S[mk]);
-                }
-            if ((j + 1) * kBN > M) {
-#pragma unroll
-                for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (j * kBN + 32 * mk + 8 * (r >> 2) + 4 * hh + (r & 3) >= M) S[mk][r] = -INFINITY;
-            }
-        }
-    };
-    auto probs = [&]() {
-        const float mc = m_run * c2;
-        float sum = 0.f;
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-            const int mk = cs >> 1, r0 = 8 * (cs & 1);
-            u32x4 pk;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i], c2, -mc));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i + 1], c2, -mc));
-                const bf16x2 pp = to_bf16x2(p0, p1);
-                sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
-                pk[i] = __builtin_bit_cast(uint32_t, pp);
-            }
-            P[cs] = __builtin_bit_cast(bf16x8, pk);
-        }
-        return sum;
-    };
-    // Softmax phase for tile j (same rule as the plain kernel: the running
-    // maximum moves only when a probability would exceed 2^20).
-    auto softmax_phase = [&](int j) {
-        if (j < 0 || j >= ntiles) return;
-        float tsum = probs();
-        if (__builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
-            float m = S[0][0];
-#pragma unroll
-            for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) m = fmaxf(m, S[mk][r]);
-            const float m_new = fmaxf(m_run, halves_max(m));
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int t = 0; t < S_::DT; ++t) O[t] *= alpha;
-            tsum = probs();
-        }
-        l_run += tsum;
-    };
-    // vmcnt(2 * 2 * LOADS): the DMAs of the two later steps may stay in flight.
-    constexpr int kWait = 0x0F70 | ((4 * LOADS) & 15) | (((4 * LOADS) >> 4) << 14);
-    auto step = [&](const uint8_t LDS_AS *cur, uint8_t LDS_AS *ahead, int j) {
-        if (j > ntiles) return;
-        dma_step(ahead, j + 3);
-        if (group == 0) mfma_phase(cur, j);
-        else softmax_phase(j - 1);
-        lds_barrier();
-        if (group == 0) softmax_phase(j);
-        else mfma_phase(cur, j);
-        __builtin_amdgcn_s_waitcnt(kWait);
-        lds_barrier();
-    };
-
-    uint8_t LDS_AS *const st0 = (uint8_t LDS_AS *)stage0;
-    uint8_t LDS_AS *const st1 = (uint8_t LDS_AS *)stage1;
-    uint8_t LDS_AS *const st2 = (uint8_t LDS_AS *)stage2;
-    uint8_t LDS_AS *const st3 = (uint8_t LDS_AS *)stage3;
-    dma_step(st0, 0);
-    dma_step(st1, 1);
-    dma_step(st2, 2);
-    __builtin_amdgcn_s_waitcnt(kWait);
-    lds_barrier();
-    for (int j = 0; j <= ntiles; j += kStages) {
-        step(st0, st3, j);
-        step(st1, st0, j + 1);
-        step(st2, st1, j + 2);
-        step(st3, st2, j + 3);
-    }
-    // The last steps issued DMAs that are never read; let them land before
-    // the work group's LDS can be reused.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-
-    const float l = halves_sum(l_run);
-    if (qrow >= M) return;
-    const float inv = 1.0f / l;
-    if (qrow < Lw) {
-        uint16_t *dst = out + (off + qrow) * rs + hd;
-#pragma unroll
-        for (int t = 0; t < S_::DT; ++t)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 st;
-                st[0] = pack_bf16(O[t][4 * g] * inv, O[t][4 * g + 1] * inv);
-                st[1] = pack_bf16(O[t][4 * g + 2] * inv, O[t][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2 *>(dst + 32 * t + 8 * g + 4 * hh) = st;
-            }
-    } else {
-        float *dst = ws + ((int64_t(w) * Lt + (qrow - Lw)) * H + h) * D;
-#pragma unroll
-        for (int t = 0; t < S_::DT; ++t)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<f32x4 *>(dst + 32 * t + 8 * g + 4 * hh) =
-                    f32x4{O[t][4 * g] * inv, O[t][4 * g + 1] * inv, O[t][4 * g + 2] * inv,
-                          O[t][4 * g + 3] * inv};
-    }
-#endif
-}
-
-// Kernel variant: the plain kernel (default; faster on the measured
-// workloads) or the ping-pong kernel, chosen once per process by the
-// WSP_ATTN_KERNEL environment variable ("pingpong").
-bool use_pingpong() {
-    static const bool pp = [] {
-        const char *e = std::getenv("WSP_ATTN_KERNEL");
-        return e && std::string(e) == "pingpong";
-    }();
-    return pp;
-}
-
 }  // namespace
 
-// Waves per work group of the plain kernel: 8 (default; one work group of
-// 256 query rows per CU, half the K/V DMA per FLOP) or 4 (two work groups of
-// 128 rows per CU), chosen once per process by WSP_ATTN_WAVES.
+// Waves per work group of the per-item kernel: 8 (default; one work group
+// of 256 query rows per CU, half the K/V DMA per FLOP) or 4 (two work groups
+// of 128 rows per CU), chosen once per process by WSP_ATTN_WAVES.
 int plain_waves() {
     static const int wv = [] {
         const char *e = std::getenv("WSP_ATTN_WAVES");
@@ -633,7 +357,7 @@ int plain_waves() {
     return wv;
 }
 
-int attn_bf16_tile_m(int, bool gather) { return (use_pingpong() && !gather) ? kPPBM : 32 * plain_waves(); }
+int attn_bf16_tile_m(int, bool) { return 32 * plain_waves(); }
 
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
@@ -643,19 +367,6 @@ hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const vo
     if (n_items <= 0) return hipSuccess;
     const float c2 = scale * kLog2e;
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
-    if (use_pingpong() && !ids) {
-        if (head_dim == 128)
-            attn_bf16_pp_kernel<128><<<dim3(n_items), dim3(kPPThreads), 0, s>>>(
-                U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets,
-                items, n_heads, text_len, c2);
-        else if (head_dim == 64)
-            attn_bf16_pp_kernel<64><<<dim3(n_items), dim3(kPPThreads), 0, s>>>(
-                U(q), U(k), U(v), U(tq), U(tk), U(tv), static_cast<uint16_t *>(out), ws, offsets,
-                items, n_heads, text_len, c2);
-        else
-            return hipErrorInvalidValue;
-        return hipGetLastError();
-    }
     const int wv = plain_waves();
     auto launch = [&](auto kern, int waves) {
         kern<<<dim3(n_items), dim3(64 * waves), 0, s>>>(U(q), U(k), U(v), U(tq), U(tk), U(tv),

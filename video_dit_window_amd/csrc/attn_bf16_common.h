@@ -65,23 +65,5 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
 }
 
-// Bare work-group barrier (s_barrier, no memory fence).  A fence would drain
-// every outstanding DMA, including those of later stages.  The ping-pong
-// kernel needs none: each wave awaits its own DMAs with an explicit
-// s_waitcnt vmcnt before the barrier that publishes a stage, and every LDS
-// read result is consumed by an MFMA (so has returned) before the barrier
-// after which that stage may be overwritten.
-__device__ inline void lds_barrier() { __builtin_amdgcn_s_barrier(); }
-
-// Element offset of row r of the joint sequence [video rows of the window;
-// text rows] in its tensor, with r clamped to the last row M-1 (rows past
-// the end read real data, discarded by the key mask or the store guard);
-// `vid` tells which tensor.  Branch-free.
-__device__ inline int64_t joint_off(int r, int Lw, int M, int64_t off, int64_t rs, bool &vid) {
-    r = min(r, M - 1);
-    vid = r < Lw;
-    return (vid ? off + r : int64_t(r - Lw)) * rs;
-}
-
 }  // namespace
 }  // namespace wsp

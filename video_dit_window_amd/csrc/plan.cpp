@@ -146,7 +146,7 @@ void relayout_perm(const wsp_plan_t &src, const wsp_plan_t &dst, std::vector<int
     for (int64_t j = 0; j < dst.n; ++j) perm[size_t(j)] = src.inv[size_t(dst.ids[size_t(j)])];
 }
 
-int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order,
+int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order, int n_groups,
                 std::vector<Item> &items) {
     constexpr int kXcds = 8;
     std::vector<int32_t> worder(size_t(p.nwin));
@@ -161,6 +161,37 @@ int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int orde
     for (int32_t w : worder)
         if (tiles_of(w) > 0xFFFF)
             return fail(WSP_ERANGE, "window " + std::to_string(w) + " needs more than 65535 query tiles");
+    if (n_groups > 0) {
+        // Persistent lists: work group g (on XCD g % 8) runs items[r * n_groups
+        // + g] for r = 0, 1, ...  Each (window, head) group goes whole to the
+        // least-loaded XCD (ORDER_LPT_XCD; any work group otherwise), and each
+        // of its query tiles to the least-loaded work group there; an item
+        // costs its number of 64-key tiles.  Groups are taken in `worder`.
+        const int xcds = (order == WSP_ORDER_LPT_XCD && n_groups >= kXcds) ? kXcds : 1;
+        std::vector<std::vector<Item>> lists(static_cast<size_t>(n_groups));
+        std::vector<int64_t> wg_load(static_cast<size_t>(n_groups), 0), xcd_load(static_cast<size_t>(xcds), 0);
+        for (int32_t w : worder) {
+            const int64_t len = int64_t(p.offsets[w + 1] - p.offsets[w]) + text_len;
+            const int64_t tiles = tiles_of(w), cost = ceil_div(len, 64);
+            for (int h = 0; h < n_heads; ++h) {
+                const int x = int(std::min_element(xcd_load.begin(), xcd_load.end()) - xcd_load.begin());
+                for (int64_t t = 0; t < tiles; ++t) {
+                    int best = -1;
+                    for (int g = x; g < n_groups; g += xcds)
+                        if (best < 0 || wg_load[size_t(g)] < wg_load[size_t(best)]) best = g;
+                    lists[size_t(best)].push_back({w, (h << 16) | int(t)});
+                    wg_load[size_t(best)] += cost;
+                }
+                xcd_load[size_t(x)] += tiles * cost;
+            }
+        }
+        size_t rounds = 0;
+        for (auto &l : lists) rounds = std::max(rounds, l.size());
+        items.assign(rounds * size_t(n_groups), Item{-1, 0});
+        for (int g = 0; g < n_groups; ++g)
+            for (size_t r = 0; r < lists[size_t(g)].size(); ++r) items[r * size_t(n_groups) + size_t(g)] = lists[size_t(g)][r];
+        return int(items.size());
+    }
     if (order != WSP_ORDER_LPT_XCD) {
         for (int32_t w : worder)
             for (int h = 0; h < n_heads; ++h)

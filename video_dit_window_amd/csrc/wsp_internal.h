@@ -24,7 +24,8 @@ struct DeviceTables {
     int32_t *ids = nullptr;                                     // [n_tokens]
     int32_t *pos = nullptr;                                     // [n_tokens] window positions
     std::map<std::tuple<int, int, int, int>, int32_t *> perm;   // src layout -> perm
-    std::map<std::tuple<int, int, int, int>, std::pair<Item *, int>> items;  // (H, Lt, BM, order)
+    // (H, Lt, BM, order, persistent work groups) -> work list
+    std::map<std::tuple<int, int, int, int, int>, std::pair<Item *, int>> items;
 };
 
 }  // namespace wsp
@@ -59,8 +60,10 @@ void relayout_perm(const wsp_plan_t &src, const wsp_plan_t &dst, std::vector<int
 // Window-local offset (dt, dh, dw) of every canonical token, packed as
 // dt | dh << 10 | dw << 21 (extents checked against 1024 / 2048 by the caller).
 void window_positions(const wsp_plan_t &p, std::vector<int32_t> &pos);
-// Attention work list; returns the grid size (items.size()).
-int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order,
+// Attention work list; returns items.size().  n_groups == 0: one item per
+// work group (grid = items.size()); n_groups > 0: persistent lists for that
+// many work groups, items[r * n_groups + g] (padded with x = -1).
+int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order, int n_groups,
                 std::vector<Item> &items);
 
 // ---- device tables (abi.cpp) ----------------------------------------------
@@ -69,20 +72,29 @@ int device_ids(wsp_plan_t &p, int dev, int32_t **out);
 int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out);
 int device_positions(wsp_plan_t &p, int dev, int32_t **out);
 int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
-                 Item **out, int *count);
+                 int n_groups, Item **out, int *count);
 
 // ---- kernel launchers -------------------------------------------------------
 // relayout.hip
 hipError_t launch_relayout(const void *x, void *y, const int32_t *perm, int64_t n_rows,
                            int64_t row_bytes, hipStream_t s);
-// attn_bf16.hip: the query-tile height used by the bf16 kernel.  ids != NULL
-// selects canonical-order q/k/v/out gathered through the plan's ids table.
+// attn_bf16.hip: the per-item bf16 kernel (one work group per item) and its
+// query-tile height.  ids != NULL selects canonical-order q/k/v/out gathered
+// through the plan's ids table.
 int attn_bf16_tile_m(int head_dim, bool gather);
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
                             float *ws, const int32_t *offsets, const int32_t *ids,
                             const Item *items, int n_items, int n_heads, int text_len, float scale,
                             hipStream_t s);
+// attn_bf16_persist.hip: the persistent bf16 kernel (default): n_groups
+// resident work groups walk items[r * n_groups + g], r < rounds.
+int attn_bf16_persist_tile_m();
+hipError_t launch_attn_bf16_persist(int head_dim, const void *q, const void *k, const void *v,
+                                    const void *tq, const void *tk, const void *tv, void *out,
+                                    float *ws, const int32_t *offsets, const int32_t *ids,
+                                    const Item *items, int n_groups, int rounds, int n_heads,
+                                    int text_len, float scale, hipStream_t s);
 // attn_f32.hip
 int attn_f32_tile_m(int head_dim);
 hipError_t launch_attn_f32(int head_dim, const float *q, const float *k, const float *v,
