@@ -7,3 +7,4 @@ imports it and shares no code with it.
 from .wsp_oracle import *  # noqa: F401,F403
 from .wsp_rope import *  # noqa: F401,F403,E402
 from .wsp_fp8 import *  # noqa: F401,F403,E402
+from .wsp_stack import *  # noqa: F401,F403,E402
