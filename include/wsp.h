@@ -335,6 +335,25 @@ int wsp_set_attn_order(int order);
  */
 int wsp_set_attn_schedule(int schedule);
 
+/*
+ * wsp_linear -- y = x w^T (+ r): the bfloat16 projection of the 32-layer
+ * stack workload (q / k / v projections of the hidden state and the output
+ * projection added to the residual stream).  The pages define the attention
+ * layer only; this entry point serves the synthetic multi-layer harness
+ * built around it, with random weights.
+ *
+ * x: [M, K], w: [N, K] (one output feature per row), y and r: [M, N]; all
+ * row-major bfloat16 device arrays owned by the caller; float32 accumulation
+ * and one rounding to bfloat16 after adding r.  r may be NULL (no residual)
+ * or equal to y (in-place residual update); y must not alias x or w.
+ * dtype must be WSP_BF16.  Requirements: M >= 0 (M = 0 does nothing),
+ * N a positive multiple of 256, K a positive multiple of 64, K < 2^20,
+ * 16-byte aligned pointers.  Asynchronous on `stream`; errors: WSP_EINVAL,
+ * WSP_EDEVICE (launch failure); nothing is launched on error.
+ */
+int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, int N, int K,
+               int dtype, void *stream);
+
 /* wsp_last_error -- message of the calling thread's last failed call ("" if none). */
 const char *wsp_last_error(void);
 

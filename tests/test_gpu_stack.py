@@ -1,0 +1,161 @@
+"""GPU parity of the multi-layer stack workload: wsp_linear (bf16 projection)
+and the stack driver against the CPU oracle (oracle/wsp_stack.py).
+
+wsp_linear is compared element by element with the float64 product rounded
+once to bfloat16: at most one bfloat16 ulp apart plus the float32
+accumulation error bound K * 2^-24 * sum|x w| (float32 accumulation can move
+a result across a rounding tie, or matter near zero), on ragged row counts,
+with and without a residual, in place.  The stack runs a few alternating
+layers on the tiny grid in full against the oracle (both the explicit
+permutations and canonical-order I/O, which must agree bit for bit), and one
+layer of the full 1080p, 2560-wide configuration on the largest window's
+rows.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import video_dit_window_amd as W
+import wsp_inputs as I
+from helpers import check_bf16, dev_bits, from_dev, log
+from video_dit_window_amd.stack import Stack
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_dev(a):
+    """float64 array of bf16 values -> device bf16 tensor (exact)."""
+    import torch
+    bits = I.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def rnd_bf16(shape, seed, std=1.0):
+    return O.bf16_round(np.random.default_rng(seed).standard_normal(shape) * std)
+
+
+def ulp_bf16(x):
+    """Spacing of bfloat16 values at |x| (8 significant bits)."""
+    _, e = np.frexp(np.abs(x))
+    return np.ldexp(1.0, e - 8)
+
+
+def check_linear(M, N, K, residual, in_place, seed):
+    import torch
+    x, w = rnd_bf16((M, K), seed), rnd_bf16((N, K), seed + 1, std=0.05)
+    r = rnd_bf16((M, N), seed + 2) if residual else None
+    dx, dw = bf16_dev(x), bf16_dev(w)
+    dr = bf16_dev(r) if residual else None
+    if in_place:
+        y = W.linear(dx, dw, residual=dr, out=dr)
+    else:
+        y = W.linear(dx, dw, residual=dr)
+    torch.cuda.synchronize()
+    got, ref = from_dev(y), O.linear(x, w, r)
+    err = np.abs(got - ref)
+    acc = 2.0 * K * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T + (np.abs(r) if residual else 0.0))
+    bound = ulp_bf16(np.abs(ref) + acc) + acc
+    log(f"  linear M={M} N={N} K={K} res={residual} in_place={in_place}: max|err| = {err.max():.3e}, "
+        f"elements not correctly rounded: {int((err > 0).sum())} of {err.size}")
+    assert np.all(err <= bound), "beyond one bf16 ulp plus the float32 accumulation bound"
+    check_bf16(got, ref, "linear")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 64), (300, 256, 192), (1000, 512, 640), (4099, 768, 2560)])
+def test_linear(gpu, M, N, K):
+    check_linear(M, N, K, residual=False, in_place=False, seed=M + N)
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_linear_residual(gpu, in_place):
+    check_linear(777, 512, 256, residual=True, in_place=in_place, seed=9)
+
+
+def test_linear_rejects_bad_shapes(gpu):
+    """N not a multiple of 256, K not a multiple of 64 and float32 operands
+    are refused with an error (nothing is launched)."""
+    import torch
+    z = lambda *shape, dt=torch.bfloat16: torch.zeros(shape, dtype=dt, device="cuda")
+    for (n, k) in ((128, 64), (256, 96)):
+        with pytest.raises(W.WspError):
+            W.linear(z(8, k), z(n, k))
+    with pytest.raises(W.WspError):
+        W.linear(z(8, 64, dt=torch.float32), z(256, 64, dt=torch.float32))
+    y = W.linear(z(0, 64), z(256, 64))      # no rows: nothing to do
+    assert tuple(y.shape) == (0, 256)
+
+
+def check_update(got, ref, inp, what):
+    """Relative L2 error of the layer updates (stream minus its input)."""
+    du, ru = got - inp, ref - inp
+    rel = float(np.linalg.norm(du - ru) / max(np.linalg.norm(ru), 1e-30))
+    log(f"  {what}: rel-L2 = {rel:.3e} (bar 2e-2)")
+    assert rel <= 2e-2, f"{what}: relative L2 error {rel}"
+
+
+GEO = (5, 20, 36, 2, 3, 3)
+HEADS, HD, LT = 4, 64, 16
+
+
+def stack_inputs(n_layers, seed, wstd=0.06):
+    E = HEADS * HD
+    N = GEO[0] * GEO[1] * GEO[2]
+    x, t = rnd_bf16((N, E), seed), rnd_bf16((LT, E), seed + 1)
+    weights = [tuple(rnd_bf16((E, E), seed + 10 + 4 * l + i, std=wstd) for i in range(4)) for l in range(n_layers)]
+    return x, t, weights
+
+
+@pytest.mark.parametrize("n_layers", [1, 3])
+def test_stack_tiny(gpu, n_layers):
+    """A few alternating layers on the tiny grid (4 heads x 64, 16 text
+    tokens): explicit permutations and canonical-order I/O agree bit for bit
+    and match the oracle."""
+    import torch
+    x, t, weights = stack_inputs(n_layers, seed=40 + n_layers)
+    dw = [tuple(bf16_dev(a) for a in wl) for wl in weights]
+    res = {}
+    for canon in (False, True):
+        st = Stack(*GEO, n_layers, HEADS, HD, LT, canonical_io=canon)
+        res[canon] = st.forward(bf16_dev(x), bf16_dev(t), dw)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_bits(res[False][0]), dev_bits(res[True][0])), "video state: I/O orders differ"
+    assert np.array_equal(dev_bits(res[False][1]), dev_bits(res[True][1])), "text state: I/O orders differ"
+    ref_x, ref_t = O.stack_forward(x, t, GEO, weights, HEADS, HD)
+    check_bf16(from_dev(res[False][0]), ref_x, f"stack {n_layers} layers video")
+    check_bf16(from_dev(res[False][1]), ref_t, f"stack {n_layers} layers text")
+    # The stream is dominated by its input (checked element-wise above); its
+    # update must match too, in relative L2 within the bf16 bar.
+    for got, ref, inp, what in ((res[False][0], ref_x, x, "video"), (res[False][1], ref_t, t, "text")):
+        check_update(from_dev(got), ref, inp, f"stack {n_layers} layers {what} update")
+
+
+def test_stack_1080p_one_layer_sampled(gpu):
+    """One layer of the 1080p, 20 x 128, 256-text-token configuration: the
+    video rows of the largest window (all heads, all 2560 features) against
+    the oracle's projections and window attention of that window."""
+    import torch
+    w = I.WORKLOADS["1080p_bf16"]
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    E, Lt, N = w.heads * w.head_dim, w.text_len, w.n_tokens
+    rng = np.random.default_rng(77)
+    log("  generating 1080p stack inputs")
+    x = O.bf16_round(rng.standard_normal((N, E), dtype=np.float32))
+    t = O.bf16_round(rng.standard_normal((Lt, E), dtype=np.float32))
+    wts = [O.bf16_round(rng.standard_normal((E, E), dtype=np.float32) * 0.02) for _ in range(4)]
+    st = Stack(*geo, 1, w.heads, w.head_dim, Lt)
+    xo, to = st.forward(bf16_dev(x), bf16_dev(t), [tuple(bf16_dev(a) for a in wts)])
+    torch.cuda.synchronize()
+    op = O.plan(*geo, O.REGULAR)
+    win = int(op.lpt[0])
+    ids = op.ids[op.offsets[win]:op.offsets[win + 1]]
+    log(f"  oracle for window {win} ({len(ids)} rows)")
+    X = np.concatenate([x[ids], t], axis=0)
+    q, k, v = (O.linear(X, wm).reshape(-1, w.heads, w.head_dim) for wm in wts[:3])
+    L = len(ids)
+    out = np.empty((L, w.heads, w.head_dim))
+    for h in range(w.heads):
+        out[:, h], _ = O.joint_attention(q[:L, h], k[:L, h], v[:L, h], q[L:, h], k[L:, h], v[L:, h])
+    ref = O.linear(O.bf16_round(out).reshape(L, E), wts[3], r=x[ids])
+    got = from_dev(xo[torch.from_numpy(ids.astype(np.int64)).cuda()])
+    check_bf16(got, ref, f"1080p stack layer, window {win}")
+    check_update(got, ref, x[ids], f"1080p stack layer update, window {win}")

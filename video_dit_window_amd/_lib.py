@@ -44,6 +44,7 @@ _SIGNATURES = {
     "wsp_fp8_quantize": (_c_int, [_c_vp, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp]),
     "wsp_window_attn_qk8": (_c_int, [_c_vp] * 9 + [_c_int, _c_int, _c_int, ctypes.c_float, ctypes.c_uint,
                                                     _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "wsp_linear": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp]),
     "wsp_set_attn_order": (_c_int, [_c_int]),
     "wsp_set_attn_schedule": (_c_int, [_c_int]),
     "wsp_last_error": (ctypes.c_char_p, []),
@@ -169,6 +170,26 @@ def relayout(x, src: Plan, dst: Plan, out=None, stream=None):
         raise ValueError("x/out shape does not match the plans")
     _check("wsp_relayout", lib().wsp_relayout(_dev_ptr(x, "x"), _dev_ptr(out, "out"), row_bytes,
                                               src.handle, dst.handle, _stream(stream)))
+    return out
+
+
+def linear(x, w, residual=None, out=None, stream=None):
+    """y = x w^T (+ residual): x [M, K], w [N, K], y [M, N], bfloat16.
+    residual may be `out` itself (in-place residual update)."""
+    torch = _torch()
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [M, K] and w [N, K]")
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if tuple(out.shape) != (M, N) or out.dtype != x.dtype or w.dtype != x.dtype:
+        raise ValueError("out must be [M, N] with the dtype of x and w")
+    if residual is not None and (tuple(residual.shape) != (M, N) or residual.dtype != x.dtype):
+        raise ValueError("residual must be [M, N] with the dtype of x")
+    rp = None if residual is None else _dev_ptr(residual, "residual")
+    _check("wsp_linear", lib().wsp_linear(_dev_ptr(x, "x"), _dev_ptr(w, "w"), rp, _dev_ptr(out, "out"), M, N, K,
+                                          _dtype_code(x.dtype), _stream(stream)))
     return out
 
 

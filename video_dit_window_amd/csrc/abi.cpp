@@ -551,6 +551,27 @@ int wsp_window_attn_qk8(const wsp_plan_t *pc, const void *q8, const void *k8, co
     return WSP_OK;
 }
 
+int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, int N, int K,
+               int dtype, void *stream) {
+    g_last_error.clear();
+    if (dtype != WSP_BF16) return fail(WSP_EINVAL, "wsp_linear supports WSP_BF16 only");
+    if (M < 0) return fail(WSP_EINVAL, "M must be >= 0");
+    if (N <= 0 || N % gemm_bf16_tile_n() != 0)
+        return fail(WSP_EINVAL, "N must be a positive multiple of " + std::to_string(gemm_bf16_tile_n()));
+    if (K <= 0 || K % gemm_bf16_tile_k() != 0 || K >= (1 << 20))
+        return fail(WSP_EINVAL, "K must be a positive multiple of " + std::to_string(gemm_bf16_tile_k()) +
+                                    " below 2^20");
+    if (M == 0) return WSP_OK;
+    if (M > int64_t(0x7FFFFFFF) - 256) return fail(WSP_ERANGE, "M is too large");
+    if (!x || !w || !y) return fail(WSP_EINVAL, "x, w and y must be non-NULL");
+    for (const void *ptr : {x, w, r, static_cast<const void *>(y)})
+        if (ptr && !aligned16(ptr)) return fail(WSP_EINVAL, "x, w, r and y must be 16-byte aligned");
+    if (y == x || y == w) return fail(WSP_EINVAL, "y must not alias x or w");
+    hipError_t e = launch_gemm_bf16(x, w, y, r, M, N, K, hipStream_t(stream));
+    if (e != hipSuccess) return hip_fail(e, "linear kernel launch");
+    return WSP_OK;
+}
+
 int wsp_set_attn_order(int order) {
     g_last_error.clear();
     if (order != WSP_ORDER_LPT_XCD && order != WSP_ORDER_LPT && order != WSP_ORDER_ID)

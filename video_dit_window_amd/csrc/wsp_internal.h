@@ -121,6 +121,12 @@ hipError_t launch_attn_qk8(const void *q, const void *k, const void *v, const vo
                            const int32_t *offsets, const int32_t *ids, const Item *items,
                            int n_items, const float *amax_q, const float *amax_k, int n_heads,
                            int text_len, float scale, hipStream_t s);
+// gemm_bf16.hip: y[M,N] = x[M,K] w[N,K]^T (+ r), bf16; N % tile_n == 0,
+// K % tile_k == 0 (checked by the caller).
+int gemm_bf16_tile_n();
+int gemm_bf16_tile_k();
+hipError_t launch_gemm_bf16(const void *x, const void *w, void *y, const void *r, int64_t M, int N,
+                            int K, hipStream_t s);
 // text_mean.hip
 hipError_t launch_text_mean(const float *ws, void *txt_out, int64_t per_window, int n_windows,
                             int dtype, hipStream_t s);
