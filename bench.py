@@ -92,6 +92,57 @@ def cpu_baseline(w, budget_s):
             "host_cpus": os.cpu_count()}
 
 
+def stack_measure(w, n_layers, attn_flops_per_layer, reps=2):
+    """The multi-layer stack workload on the same grid: per layer q/k/v and
+    output projections (wsp_linear), window attention and the layout move,
+    layers alternating regular / shifted.  Synthetic inputs from torch's
+    seeded device generator: hidden state N(0,1), weights N(0, 0.02)."""
+    import torch
+    import video_dit_window_amd as W
+    from video_dit_window_amd.stack import Stack
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    N, Lt, E = w.n_tokens, w.text_len, w.heads * w.head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    bf = torch.bfloat16
+    xv = torch.randn((N, E), device="cuda", generator=g).to(bf)
+    xt = torch.randn((Lt, E), device="cuda", generator=g).to(bf)
+    wts = [tuple((torch.randn((E, E), device="cuda", generator=g) * 0.02).to(bf) for _ in range(4))
+           for _ in range(n_layers)]
+    st = Stack(*geo, n_layers, w.heads, w.head_dim, Lt)
+    ov, ot = torch.empty_like(xv), torch.empty_like(xt)
+    stream = torch.cuda.current_stream()
+    # one projection launch on the stack's own buffers, timed alone
+    for _ in range(3):
+        W.linear(st.X[0], wts[0][0], out=st.q)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(10):
+        W.linear(st.X[0], wts[0][0], out=st.q)
+    b.record(stream)
+    st.forward(xv, xt, wts, out_vid=ov, out_txt=ot)      # warm-up pass
+    torch.cuda.synchronize()
+    lin_ms = a.elapsed_time(b) / 10
+    lin_flops = 2 * (N + Lt) * E * E
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(reps):
+        st.forward(xv, xt, wts, out_vid=ov, out_txt=ot)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / reps
+    layer_flops = 4 * lin_flops + attn_flops_per_layer
+    return {"note": f"{n_layers}-layer stack: q/k/v/out projections (wsp_linear) + window attention + "
+                    "layout moves per layer, regular/shifted alternating, entry/exit in canonical order",
+            "layers": n_layers, "hidden": E, "ms_per_pass": round(ms, 3),
+            "ms_per_layer": round(ms / n_layers, 4),
+            "video_tokens_per_s_per_layer": round(n_layers * N / (ms * 1e-3), 1),
+            "tflops_per_pass": round(n_layers * layer_flops / (ms * 1e-3) / 1e12, 2),
+            "linear_avg_ms": round(lin_ms, 4),
+            "linear_kernel_tflops": round(lin_flops / (lin_ms * 1e-3) / 1e12, 2),
+            "flop_per_layer": {"projections": 4 * lin_flops, "attention": attn_flops_per_layer}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +153,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the side measurement of the pass with relayouts fused into attention")
+    ap.add_argument("--stack-layers", type=int, default=32,
+                    help="layers of the multi-layer stack side measurement")
+    ap.add_argument("--no-stack", action="store_true", help="skip the multi-layer stack side measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (a known-size "
                          "reference for HBM byte counters)")
@@ -245,7 +299,8 @@ def main():
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(w.name), "traffic_unit": "B/launch",
-                     "kernel": "attn_bf16_kernel<128, 8, false> (+ text_mean_kernel in the same call)",
+                     "kernel": "attn_bf16_kernel<128, 8, false> (one work group per item; + text_mean_kernel "
+                               "in the same call)",
                      "flop_per_launch": per_call_flops, "avg_launch_ms": round(attn_avg_ms, 4)},
         "wall_s_timed": round(wall, 3),
     }
@@ -268,6 +323,8 @@ def main():
             "attn_tflops_per_step": round(step_flops / (ms_fused * 1e-3) / 1e12, 3),
             "attn_kernel_tflops": round(per_call_flops / (f_ms * 1e-3) / 1e12, 2),
             "avg_launch_ms": round(f_ms, 4)}
+    if not args.no_stack:
+        res["stack"] = stack_measure(w, args.stack_layers, per_call_flops)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(res), flush=True)
