@@ -201,8 +201,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     const int ntiles = (M + kBN - 1) / kBN;
 
     // One tile: cur holds tile j; the DMA of tile j+1 goes to nxt.
+    // A wave whose 32 query rows all lie past the joint sequence (the last
+    // query tile of a window) only moves its share of the K/V tiles and
+    // meets the barriers: the SIMD it shares then runs the other wave alone.
+    const bool active = qt * kBM + wave * 32 < M;
     auto tile = [&](const uint8_t LDS_AS *cur, uint8_t LDS_AS *nxt, int j) {
         if (j + 1 < ntiles) dma(nxt, j + 1);
+        if (active) {
 
         // S^T for 64 keys (two 32-key blocks) x this wave's 32 queries.  The
         // K operands of k-step s+2 are read while step s multiplies.
@@ -298,6 +303,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             if (cs + 1 < 4) vread(cs + 1, va[(cs + 1) & 1]);
 #pragma unroll
             for (int t = 0; t < S_::DT; ++t) O[t] = mfma(va[cs & 1][t], P[cs], O[t]);
+        }
         }
         // The DMA of tile j+1 has landed (vmcnt) and every wave is done with
         // `cur` before it is overwritten two tiles later.

@@ -285,7 +285,9 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
             if constexpr (GATHER) load_ids(nxt, 1);
             q_dma(nxt);
         }
-        if (KIND != kFin || j * kBN < cur.M) {
+        // Waves whose 32 query rows all lie past the joint sequence only move
+        // their share of the tiles and meet the barriers.
+        if ((KIND != kFin || j * kBN < cur.M) && cur.qt * kPkBM + wave * 32 < cur.M) {
 
         // S^T for 64 keys (two 32-key blocks) x this wave's 32 queries; the K
         // operands of k-step s+2 are read while step s multiplies.

@@ -126,13 +126,26 @@ __global__ __launch_bounds__(64 * kGWaves, 2) void gemm_bf16_kernel(
             for (int mb = 0; mb < 2; ++mb) xb[buf][mb] = *reinterpret_cast<const bf16x8 LDS_AS *>(cx + xaddr[mb] + c);
         };
         rd(0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
         for (int ks = 0; ks < kGBK / 16; ++ks) {
+            // The operands of k-step ks+1 are read between the products of
+            // step ks (one read after each of the first six products).
             if (ks + 1 < kGBK / 16) rd(ks + 1, (ks + 1) & 1);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(wa[ks & 1][nb], xb[ks & 1][mb], acc[mb][nb]);
+            if (ks + 1 < kGBK / 16) {
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's DMA of slab s+1 has landed
         __syncthreads();                     // ... every wave's, and all are done with slab s
