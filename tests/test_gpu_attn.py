@@ -258,6 +258,13 @@ def test_720p_regular_sampled(gpu):
     sampled_check(I.WORKLOADS["720p_bf16"], "regular", heads_full_text=[0, 19])
 
 
+def test_720p_shifted_sampled(gpu):
+    """The 720p grid in the shifted layout (64 windows, edge windows of 252
+    rows) -- the workload names the regular layout only; shifted is the
+    other layer kind of the same grid."""
+    sampled_check(I.WORKLOADS["720p_bf16"], "shifted", heads_full_text=[5])
+
+
 @pytest.mark.parametrize("method", ["regular", "shifted"])
 def test_1080p_sampled(gpu, method):
     sampled_check(I.WORKLOADS["1080p_bf16"], method, heads_full_text=[7])
@@ -266,3 +273,10 @@ def test_1080p_sampled(gpu, method):
 @pytest.mark.timeout(900)
 def test_4k_shifted_sampled(gpu):
     sampled_check(I.WORKLOADS["4k_bf16"], "shifted", heads_full_text=[3], text_dtype=np.float32)
+
+
+@pytest.mark.timeout(900)
+def test_4k_regular_sampled(gpu):
+    """4K grid, regular layout (324 windows of 2520-3240 rows; the last
+    temporal window is 7 of the 31 frames deep)."""
+    sampled_check(I.WORKLOADS["4k_bf16"], "regular", heads_full_text=[11], text_dtype=np.float32)
