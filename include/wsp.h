@@ -349,7 +349,8 @@ int wsp_set_attn_schedule(int schedule);
  * dtype must be WSP_BF16.  Requirements: M >= 0 (M = 0 does nothing),
  * N a positive multiple of 256, K a positive multiple of 64, K < 2^20,
  * 16-byte aligned pointers.  Asynchronous on `stream`; errors: WSP_EINVAL,
- * WSP_EDEVICE (launch failure); nothing is launched on error.
+ * WSP_ERANGE (M beyond 2^31 - 257 rows), WSP_EDEVICE (launch failure);
+ * nothing is launched on error.
  */
 int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, int N, int K,
                int dtype, void *stream);
