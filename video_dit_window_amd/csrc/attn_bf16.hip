@@ -7,11 +7,10 @@
 // models with USP (text replica)", section "3. Attention with USP": plain
 // SDPA (no mask, no dropout, scale 1/sqrt(D) unless given).
 //
-// Work item = (window w, head h, tile of 32*W query rows) of the joint query
+// Work item = (window w, head h, tile of 256 query rows) of the joint query
 // sequence [q rows of w; txt_q]; the key/value sequence is [k/v rows of w;
-// txt_k/v].  A work group is W = 8 wavefronts of 32 query rows (one work
-// group per CU; W = 4 gives two per CU), 2 waves per SIMD, < 256 registers
-// each.
+// txt_k/v].  A work group is 8 wavefronts of 32 query rows (one work group
+// per CU), 2 waves per SIMD, < 256 registers each.
 //
 // Per 64-key tile and wavefront:
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16 with K from LDS as the A operand
@@ -23,8 +22,8 @@
 //   O^T += V^T P^T  the probabilities stay in registers as bf16 B operands;
 //                   V^T comes from the row-major V tile through the gfx950
 //                   LDS transpose read (ds_read_b64_tr_b16).
-// K and V tiles travel global -> LDS by direct DMA loads (global_load_lds,
-// 16 bytes per lane, no staging registers), double-buffered: the DMA of tile
+// K and V tiles travel global -> LDS by direct DMA loads (buffer loads to
+// LDS, 16 bytes per lane, no staging registers), double-buffered: the DMA of tile
 // j+1 runs while tile j is multiplied.  Rows are stored unpadded, their
 // 16-byte chunks XOR-swizzled by row so that the K operand reads (16 rows,
 // one chunk) and the transpose reads (4 rows x 4 chunks) hit distinct banks.
@@ -32,14 +31,15 @@
 // float32 output to the workspace, reduced over windows in id order by the
 // text-mean kernel.
 
-#include <cstdlib>
-#include <string>
-
 #include "attn_bf16_common.h"
 
 namespace wsp {
 
 namespace {
+
+// Waves per work group: 8 x 32 query rows, one work group per CU (2 waves
+// per SIMD).
+constexpr int kItemWaves = 8;
 
 // GATHER: q, k, v and out hold rows in canonical token order; the video row
 // r of window w is canonical row ids[offsets[w] + r] (the plan's table), so
@@ -352,18 +352,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 
 }  // namespace
 
-// Waves per work group of the per-item kernel: 8 (default; one work group
-// of 256 query rows per CU, half the K/V DMA per FLOP) or 4 (two work groups
-// of 128 rows per CU), chosen once per process by WSP_ATTN_WAVES.
-int plain_waves() {
-    static const int wv = [] {
-        const char *e = std::getenv("WSP_ATTN_WAVES");
-        return (e && std::atoi(e) == 4) ? 4 : 8;
-    }();
-    return wv;
-}
-
-int attn_bf16_tile_m(int, bool) { return 32 * plain_waves(); }
+int attn_bf16_tile_m(int, bool) { return 32 * kItemWaves; }
 
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
@@ -373,18 +362,18 @@ hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const vo
     if (n_items <= 0) return hipSuccess;
     const float c2 = scale * kLog2e;
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
-    const int wv = plain_waves();
-    auto launch = [&](auto kern, int waves) {
-        kern<<<dim3(n_items), dim3(64 * waves), 0, s>>>(U(q), U(k), U(v), U(tq), U(tk), U(tv),
-                                                          static_cast<uint16_t *>(out), ws, offsets,
-                                                          ids, items, n_heads, text_len, c2);
+    auto launch = [&](auto kern) {
+        kern<<<dim3(n_items), dim3(64 * kItemWaves), 0, s>>>(U(q), U(k), U(v), U(tq), U(tk), U(tv),
+                                                              static_cast<uint16_t *>(out), ws, offsets,
+                                                              ids, items, n_heads, text_len, c2);
     };
     const bool g = ids != nullptr;
-    if (head_dim == 128 && wv == 8) g ? launch(attn_bf16_kernel<128, 8, true>, 8) : launch(attn_bf16_kernel<128, 8, false>, 8);
-    else if (head_dim == 128) g ? launch(attn_bf16_kernel<128, 4, true>, 4) : launch(attn_bf16_kernel<128, 4, false>, 4);
-    else if (head_dim == 64 && wv == 8) g ? launch(attn_bf16_kernel<64, 8, true>, 8) : launch(attn_bf16_kernel<64, 8, false>, 8);
-    else if (head_dim == 64) g ? launch(attn_bf16_kernel<64, 4, true>, 4) : launch(attn_bf16_kernel<64, 4, false>, 4);
-    else return hipErrorInvalidValue;
+    if (head_dim == 128)
+        g ? launch(attn_bf16_kernel<128, kItemWaves, true>) : launch(attn_bf16_kernel<128, kItemWaves, false>);
+    else if (head_dim == 64)
+        g ? launch(attn_bf16_kernel<64, kItemWaves, true>) : launch(attn_bf16_kernel<64, kItemWaves, false>);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
