@@ -3,11 +3,16 @@
 
 A step is one pass of the whole hot path over the 1080p-shaped workload
 (T=21, H=68, W=120 latent grid, 171360 video tokens; windows from
-nt,nh,nw = 4,3,3; 20 heads x 128; 256 text tokens; bf16):
-  entry relayout of q, k, v (canonical -> regular), regular-layout window
-  attention + text mean, relayout of q, k, v (regular -> shifted),
-  shifted-layout window attention + text mean, exit relayout of the video
-  output (shifted -> canonical).
+nt,nh,nw = 4,3,3; 20 heads x 128; 256 text tokens; bf16): q, k, v in
+canonical token order enter the regular-layout window attention + text mean,
+then the shifted-layout window attention + text mean, and the video output
+leaves in canonical order.  The headline step runs the layout permutations
+inside the attention kernels (canonical-order I/O: each layer reads its
+layout's rows through the plan's ids table and scatters its output back);
+the same pass with explicit relayout kernels (entry relayout of q, k, v,
+relayout between the layers, exit relayout of the output) is timed beside it
+and reported as `explicit_pass`, with the relayout's HBM rate.  Both give
+bit-identical outputs.
 Inputs are synthetic (seeded normal samples, N(0,1)/sqrt(128)) and resident in
 HBM before the timed region.  The JSON line reports window-attention TFLOP/s
 over the whole step, video tokens/s/layer, the roofline of the attention
@@ -40,7 +45,7 @@ METRIC = "window-attn TFLOP/s + video tokens/s/layer at 1080p grid; % MFMA peak"
 # (FETCH_SIZE x2.0, WRITE_SIZE x1.0); the committed summary under profiles/ holds the
 # figures and commands.  Keyed by the sha256 prefix of the attention kernel source the
 # counters were taken on: any later change to the kernel reports null.
-MEASURED_TRAFFIC = {"11f38e923ebe92e8": {"1080p_bf16": 4.3842e9}}
+MEASURED_TRAFFIC = {"ab1d21a92f6c3534": {"1080p_bf16": {"layout": 4.3854e9, "canonical": 4.3801e9}}}
 ATTN_SRCS = [os.path.join(ROOT, "video_dit_window_amd", "csrc", f)
              for f in ("attn_bf16.hip", "attn_bf16_common.h")]
 
@@ -49,8 +54,9 @@ def attn_source_hash():
     return hashlib.sha256(b"".join(open(f, "rb").read() for f in ATTN_SRCS)).hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    return MEASURED_TRAFFIC.get(attn_source_hash(), {}).get(workload)
+def measured_traffic(workload, io):
+    """HBM bytes per launch for io = "canonical" or "layout" I/O, or None."""
+    return MEASURED_TRAFFIC.get(attn_source_hash(), {}).get(workload, {}).get(io)
 
 
 def attn_flops(lengths, heads, head_dim, text_len):
@@ -89,13 +95,24 @@ def cpu_baseline(w, budget_s):
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{pairs} (window, head) pairs of the {w.name} regular layout, largest "
                       f"windows first, float64 numpy; {el:.1f} s inside the oracle",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def stack_measure(w, n_layers, attn_flops_per_layer, reps=2):
     """The multi-layer stack workload on the same grid: per layer q/k/v and
-    output projections (wsp_linear), window attention and the layout move,
-    layers alternating regular / shifted.  Synthetic inputs from torch's
+    output projections (wsp_linear) and window attention with canonical-order
+    I/O, layers alternating regular / shifted.  Synthetic inputs from torch's
     seeded device generator: hidden state N(0,1), weights N(0, 0.02)."""
     import torch
     import video_dit_window_amd as W
@@ -109,7 +126,7 @@ def stack_measure(w, n_layers, attn_flops_per_layer, reps=2):
     xt = torch.randn((Lt, E), device="cuda", generator=g).to(bf)
     wts = [tuple((torch.randn((E, E), device="cuda", generator=g) * 0.02).to(bf) for _ in range(4))
            for _ in range(n_layers)]
-    st = Stack(*geo, n_layers, w.heads, w.head_dim, Lt)
+    st = Stack(*geo, n_layers, w.heads, w.head_dim, Lt, canonical_io=True)
     ov, ot = torch.empty_like(xv), torch.empty_like(xt)
     stream = torch.cuda.current_stream()
     # one projection launch on the stack's own buffers, timed alone
@@ -133,7 +150,8 @@ def stack_measure(w, n_layers, attn_flops_per_layer, reps=2):
     ms = s0.elapsed_time(s1) / reps
     layer_flops = 4 * lin_flops + attn_flops_per_layer
     return {"note": f"{n_layers}-layer stack: q/k/v/out projections (wsp_linear) + window attention + "
-                    "layout moves per layer, regular/shifted alternating, entry/exit in canonical order",
+                    "regular/shifted alternating; the stream stays in canonical order and each layer's attention reads "
+                    "and writes through its layout's ids table",
             "layers": n_layers, "hidden": E, "ms_per_pass": round(ms, 3),
             "ms_per_layer": round(ms / n_layers, 4),
             "video_tokens_per_s_per_layer": round(n_layers * N / (ms * 1e-3), 1),
@@ -152,7 +170,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true",
-                    help="skip the side measurement of the pass with relayouts fused into attention")
+                    help="headline = the pass with explicit relayout kernels (skip the fused pass)")
     ap.add_argument("--stack-layers", type=int, default=32,
                     help="layers of the multi-layer stack side measurement")
     ap.add_argument("--no-stack", action="store_true", help="skip the multi-layer stack side measurement")
@@ -266,44 +284,74 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     ms_step, wall = run(step)
-    ms_fused, _ = (None, None) if args.no_fused else run(step_fused)
+    ms_fused, wall_f = (None, None) if args.no_fused else run(step_fused)
     run(step_rope)
     run(step_qk8)
     attn_ms = [a.elapsed_time(b) for a, b in ev["attn"]]
     rel_ms = [a.elapsed_time(b) for a, b in ev["relayout"]]
     step_flops = sum(flops)
-    value = step_flops / (ms_step * 1e-3) / 1e12
     # dominant kernel: window attention (per call = attention kernel + text mean)
     per_call_flops = step_flops / len(plans)
     attn_avg_ms = float(np.mean(attn_ms))
-    attn_tflops = per_call_flops / (attn_avg_ms * 1e-3) / 1e12
     rel_bytes = 2 * N * row_bytes + 4 * N
     rel_avg_ms = float(np.mean(rel_ms))
     rel_gbps = rel_bytes / (rel_avg_ms * 1e-3) / 1e9
+    explicit = {
+        "note": "same pass with explicit relayout kernels (entry relayout of q,k,v, relayout between the "
+                "layers, exit relayout of the output) and layout-order attention I/O",
+        "ms_per_step": round(ms_step, 4),
+        "attn_tflops_per_step": round(step_flops / (ms_step * 1e-3) / 1e12, 3),
+        "attn_kernel_tflops": round(per_call_flops / (attn_avg_ms * 1e-3) / 1e12, 2),
+        "avg_launch_ms": round(attn_avg_ms, 4),
+        "breakdown_ms_per_step": {"attention+text_mean": round(sum(attn_ms) / args.steps, 4),
+                                  "relayout": round(sum(rel_ms) / args.steps, 4)},
+        "traffic_bytes_per_launch": measured_traffic(w.name, "layout")}
+    if ms_fused is not None:
+        f_ms = [a.elapsed_time(b) for a, b in ev["fused_attn"]]
+        head_ms, head_avg, io = ms_fused, float(np.mean(f_ms)), "canonical"
+        kernel = "attn_bf16_kernel<128, 8, true> (canonical-order I/O, one work group per item; + " \
+                 "text_mean_kernel in the same call)"
+        breakdown = {"attention+text_mean": round(sum(f_ms) / args.steps, 4)}
+    else:
+        head_ms, head_avg, io = ms_step, attn_avg_ms, "layout"
+        kernel = "attn_bf16_kernel<128, 8, false> (one work group per item; + text_mean_kernel in the same call)"
+        breakdown = explicit["breakdown_ms_per_step"]
+    value = step_flops / (head_ms * 1e-3) / 1e12
+    attn_tflops = per_call_flops / (head_avg * 1e-3) / 1e12
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "grid_thw": [w.T, w.H, w.W], "n_thw": [w.nt, w.nh, w.nw],
                    "video_tokens": N, "heads": Hh, "head_dim": D, "text_len": Lt,
-                   "layers": list(w.layouts), "windows": [p.n_windows for p in plans]},
-        "video_tokens_per_s_per_layer": round(N / (attn_avg_ms * 1e-3), 1),
+                   "layers": list(w.layouts), "windows": [p.n_windows for p in plans],
+                   "io": "canonical order, layout permutations inside the attention kernels"
+                         if io == "canonical" else "explicit relayout kernels"},
+        "video_tokens_per_s_per_layer": round(N / (head_avg * 1e-3), 1),
         "attn_kernel_tflops": round(attn_tflops, 2),
         "attn_mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "relayout_gbps": round(rel_gbps, 1),
         "relayout_hbm_frac": round(rel_gbps / HBM_PEAK_GBPS, 4),
-        "breakdown_ms_per_step": {"attention+text_mean": round(sum(attn_ms) / args.steps, 4),
-                                  "relayout": round(sum(rel_ms) / args.steps, 4)},
+        "breakdown_ms_per_step": breakdown,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name), "traffic_unit": "B/launch",
-                     "kernel": "attn_bf16_kernel<128, 8, false> (one work group per item; + text_mean_kernel "
-                               "in the same call)",
-                     "flop_per_launch": per_call_flops, "avg_launch_ms": round(attn_avg_ms, 4)},
-        "wall_s_timed": round(wall, 3),
+                     "traffic": measured_traffic(w.name, io), "traffic_unit": "B/launch",
+                     "kernel": kernel, "flop_per_launch": per_call_flops, "avg_launch_ms": round(head_avg, 4)},
+        "wall_s_timed": round(wall if ms_fused is None else wall_f, 3),
     }
+    if ms_fused is not None:
+        res["explicit_pass"] = explicit
+    if ms_fused is not None:
+        # Dispatch-order A/B on the headline pass: window-id order, largest
+        # first, largest first with (window, head) groups kept on one XCD.
+        orders = {}
+        for name, o in (("window_id", W.ORDER_ID), ("lpt", W.ORDER_LPT), ("lpt_xcd", W.ORDER_LPT_XCD)):
+            W.set_attn_order(o)
+            orders[name] = round(run(step_fused)[0], 4)
+        W.set_attn_order(W.ORDER_LPT_XCD)
+        res["dispatch_order_ms_per_step"] = orders
     rope_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["rope"]]))
     rope_bytes = 2 * N * row_bytes + 12 * N   # rows in + out, perm + id + position per row
     res["rope_relayout"] = {"note": "q or k moved canonical -> layout with window-local 3D RoPE",
@@ -315,14 +363,6 @@ def main():
         "note": "q, k as OCP E4M3 codes (per-head scales) on the FP8 matrix cores; v, P, outputs bf16",
         "avg_launch_ms": round(q8_ms, 4),
         "attn_kernel_tflops": round(per_call_flops / (q8_ms * 1e-3) / 1e12, 2)}
-    if ms_fused is not None:
-        f_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["fused_attn"]]))
-        res["fused_pass"] = {
-            "note": "same pass, layout permutations fused into attention (canonical-order I/O)",
-            "ms_per_step": round(ms_fused, 4),
-            "attn_tflops_per_step": round(step_flops / (ms_fused * 1e-3) / 1e12, 3),
-            "attn_kernel_tflops": round(per_call_flops / (f_ms * 1e-3) / 1e12, 2),
-            "avg_launch_ms": round(f_ms, 4)}
     if not args.no_stack:
         res["stack"] = stack_measure(w, args.stack_layers, per_call_flops)
     if not args.no_cpu_baseline:
