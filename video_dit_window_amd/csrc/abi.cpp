@@ -123,6 +123,25 @@ int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out) 
     return WSP_OK;
 }
 
+int device_rel_ids(wsp_plan_t &p, int dev, int32_t **out) {
+    std::lock_guard<std::mutex> lk(p.mu);
+    DeviceTables &t = p.dev[dev];
+    if (!t.rel) {
+        std::vector<int32_t> rel;
+        try {
+            rel.resize(p.ids.size());
+        } catch (const std::bad_alloc &) {
+            return fail(WSP_ENOMEM, "host allocation of the relative id table failed");
+        }
+        for (int32_t w = 0; w < p.nwin; ++w)
+            for (int32_t j = p.offsets[w]; j < p.offsets[w + 1]; ++j) rel[j] = p.ids[j] - p.ids[p.offsets[w]];
+        int rc = upload(rel.data(), rel.size(), &t.rel);
+        if (rc) return rc;
+    }
+    *out = t.rel;
+    return WSP_OK;
+}
+
 int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
                  int n_groups, Item **out, int *count) {
     const auto key = std::make_tuple(n_heads, text_len, bm, order, n_groups);
@@ -150,6 +169,53 @@ int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int 
     std::lock_guard<std::mutex> lk(p.mu);
     auto &m = p.dev[dev].items;
     auto ins = m.emplace(key, std::make_pair(d, int(items.size())));
+    if (!ins.second) (void)hipFree(d);
+    *out = ins.first->second.first;
+    *count = ins.first->second.second;
+    return WSP_OK;
+}
+
+int device_item_descs(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
+                      bool gather, ItemDesc **out, int *count) {
+    const auto key = std::make_tuple(n_heads, text_len, bm, order, int(gather));
+    {
+        std::lock_guard<std::mutex> lk(p.mu);
+        auto &m = p.dev[dev].descs;
+        auto it = m.find(key);
+        if (it != m.end()) {
+            *out = it->second.first;
+            *count = it->second.second;
+            return WSP_OK;
+        }
+    }
+    std::vector<ItemDesc> descs;
+    try {
+        std::vector<Item> items;
+        const int rc = build_items(p, n_heads, text_len, bm, order, 0, items);
+        if (rc < 0) return rc;
+        descs.resize(items.size());
+        for (size_t i = 0; i < items.size(); ++i) {
+            ItemDesc &d = descs[i];
+            d = ItemDesc{};
+            d.w = items[i].x;
+            d.hq = items[i].y;
+            if (d.w < 0) continue;
+            d.off = p.offsets[d.w];
+            d.lw = p.offsets[d.w + 1] - d.off;
+            // a window's rows in canonical order ascend (t, h, w row-major), so
+            // its first id is the smallest and its last the largest
+            d.vrow0 = gather ? p.ids[d.off] : d.off;
+            d.vrows = gather ? p.ids[d.off + d.lw - 1] - p.ids[d.off] + 1 : d.lw;
+        }
+    } catch (const std::bad_alloc &) {
+        return fail(WSP_ENOMEM, "host allocation of the attention work list failed");
+    }
+    ItemDesc *d = nullptr;
+    const int rc = upload(descs.data(), descs.size(), &d);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lk(p.mu);
+    auto &m = p.dev[dev].descs;
+    auto ins = m.emplace(key, std::make_pair(d, int(descs.size())));
     if (!ins.second) (void)hipFree(d);
     *out = ins.first->second.first;
     *count = ins.first->second.second;
@@ -215,9 +281,11 @@ void wsp_plan_free(wsp_plan_t *p) {
         DeviceTables &t = kv.second;
         if (t.offsets) (void)hipFree(t.offsets);
         if (t.ids) (void)hipFree(t.ids);
+        if (t.rel) (void)hipFree(t.rel);
         if (t.pos) (void)hipFree(t.pos);
         for (auto &pm : t.perm) (void)hipFree(pm.second);
         for (auto &it : t.items) (void)hipFree(it.second.first);
+        for (auto &it : t.descs) (void)hipFree(it.second.first);
     }
     if (have_cur) (void)hipSetDevice(cur);
     delete p;
@@ -306,6 +374,9 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
         if (rows * row_bytes >= (int64_t(1) << 31))
             return fail(WSP_ERANGE, gather ? "a window's canonical rows span 2 GiB or more"
                                            : "a window's rows (or the text rows) take 2 GiB or more");
+        // canonical order: row offsets are 24-bit products (relative id x row bytes)
+        if (gather && row_bytes >= (int64_t(1) << 24))
+            return fail(WSP_ERANGE, "q/k/v rows of 16 MiB or more");
     }
     if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
     const int order = g_attn_order.load();
@@ -331,8 +402,15 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
     int32_t *d_ids = nullptr;
     if (gather && (rc = device_ids(*p, dev, &d_ids))) return rc;
     Item *items = nullptr;
+    ItemDesc *descs = nullptr;
     int n_items = 0;
-    if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, n_groups, &items, &n_items))) return rc;
+    int32_t *d_rel = nullptr;
+    if (dtype == WSP_BF16 && !persist) {
+        rc = device_item_descs(*p, dev, n_heads, text_len, bm, order, gather, &descs, &n_items);
+        if (!rc && gather) rc = device_rel_ids(*p, dev, &d_rel);
+    } else
+        rc = device_items(*p, dev, n_heads, text_len, bm, order, n_groups, &items, &n_items);
+    if (rc) return rc;
     hipStream_t s = hipStream_t(stream);
     float *ws = static_cast<float *>(workspace);
     hipError_t e;
@@ -340,8 +418,8 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
         e = launch_attn_bf16_persist(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, d_ids,
                                      items, n_groups, n_items / n_groups, n_heads, text_len, scale, s);
     else if (dtype == WSP_BF16)
-        e = launch_attn_bf16(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, d_ids,
-                             items, n_items, n_heads, text_len, scale, s);
+        e = launch_attn_bf16(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_rel, descs, n_items,
+                             n_heads, text_len, scale, s);
     else
         e = launch_attn_f32(head_dim, static_cast<const float *>(q), static_cast<const float *>(k),
                             static_cast<const float *>(v), static_cast<const float *>(txt_q),

@@ -42,15 +42,16 @@ namespace {
 constexpr int kItemWaves = 8;
 
 // GATHER: q, k, v and out hold rows in canonical token order; the video row
-// r of window w is canonical row ids[offsets[w] + r] (the plan's table), so
-// the layout permutation happens inside the loads and the output stores.
+// r of window w is canonical row vrow0 + rel[offsets[w] + r] (the plan's ids
+// relative to the window's smallest id), so the layout permutation happens
+// inside the loads and the output stores.
 template <int D, int kWaves, bool GATHER>
 __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ tq,
     const uint16_t *__restrict__ tk, const uint16_t *__restrict__ tv,
-    uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ ids, const Item *__restrict__ items, int H, int Lt, float c2) {
+    uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ rel,
+    const ItemDesc *__restrict__ items, int H, int Lt, float c2) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     using S_ = Shape<D, kWaves>;
     constexpr int kBM = 32 * kWaves;  // query rows per work group
@@ -58,28 +59,33 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * S_::TILE];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[2 * S_::TILE];
 
-    const Item it = items[blockIdx.x];
-    if (it.x < 0) return;
-    const int w = it.x, h = it.y >> 16, qt = it.y & 0xFFFF;
-    const int64_t off = offsets[w];
-    const int Lw = offsets[w + 1] - int(off);
+    // One scalar load: window, head, query tile and the window's rows.
+    const ItemDesc it = items[blockIdx.x];
+    if (it.w < 0) return;
+    const int w = it.w, h = it.hq >> 16, qt = it.hq & 0xFFFF;
+    const int64_t off = it.off;
+    const int Lw = it.lw;
     const int M = Lw + Lt;
     const int64_t rs = int64_t(H) * D, hd = int64_t(h) * D;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
 
     // Tensor row of video row r (< Lw) of this window.
-    const int32_t *const wids = GATHER ? ids + off : nullptr;
-    auto vrow = [&](int r) -> int64_t { return GATHER ? int64_t(wids[r]) : off + r; };
+    const int64_t vrow0 = it.vrow0;
+    const int32_t *const wrel = GATHER ? rel + off : nullptr;
+    auto vrow = [&](int r) -> int64_t { return GATHER ? vrow0 + wrel[r] : off + r; };
 
     // Query row of this lane (B operand of S^T = K Q^T): 8 dims per k-step.
+    // Its tensor row (video rows: through the ids table) also addresses the
+    // output store.
     bf16x8 Qr[S_::KSTEPS];
     const int qrow = qt * kBM + wave * 32 + l32;
+    int64_t qtrow;
     {
         const int r = min(qrow, M - 1);
         const bool vid = r < Lw;
-        const int64_t o = (vid ? vrow(min(r, Lw - 1)) : int64_t(r - Lw)) * rs + hd;
-        const uint16_t *p = (vid ? q : tq) + o;
+        qtrow = vid ? vrow(min(r, Lw - 1)) : int64_t(r - Lw);
+        const uint16_t *p = (vid ? q : tq) + qtrow * rs + hd;
 #pragma unroll
         for (int s = 0; s < S_::KSTEPS; ++s)
             Qr[s] = *reinterpret_cast<const bf16x8 *>(p + 16 * s + 8 * hh);
@@ -104,12 +110,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     // with rows past the joint sequence clamped to its last row.  A
     // resource's byte range also bounds every access.
     const uint32_t row_bytes = uint32_t(rs) * 2u;
-    // (readfirstlane: the ids are wave-uniform; the resources must sit in
-    // scalar registers, else every DMA becomes a loop over lanes.)
-    const int32_t id_first = GATHER ? __builtin_amdgcn_readfirstlane(wids[0]) : 0;
-    const int32_t id_last = GATHER ? __builtin_amdgcn_readfirstlane(wids[Lw - 1]) : 0;
-    const int64_t vrow0 = GATHER ? int64_t(id_first) : off;
-    const uint32_t vrows = GATHER ? uint32_t(id_last - id_first + 1) : uint32_t(Lw);
+    // (The window's row range comes with the work item, in scalar
+    // registers: a resource held in vector registers would turn every DMA
+    // into a loop over lanes.)
+    const uint32_t vrows = uint32_t(it.vrows);
     auto rsrc = [&](const uint16_t *base, uint32_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, int(bytes), kBufferFlags);
     };
@@ -121,13 +125,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < S_::LOADS; ++i)
         dvoff[i] = (drow0 + S_::ROWS_PER_LOAD * i) * int(row_bytes) + 2 * dchunk[i];
-    // Gather mode: canonical ids of the rows of the next tile to move,
-    // loaded one tile ahead of their DMA.
+    // Gather mode: relative ids of the rows of the next tile to move, loaded
+    // one tile ahead of their DMA by buffer loads whose per-lane offset holds
+    // the row (the range check covers it: rows past the window read 0, and
+    // such rows only reach the DMA as masked keys).  The DMA offset is then
+    // one 24-bit multiply-add (the host keeps row_bytes < 2^24 and every
+    // offset < 2^31).
+    const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t *>(GATHER ? wrel : rel), 0, GATHER ? 4 * Lw : 0, kBufferFlags);
     int idp[S_::LOADS];
     auto load_ids = [&](int j) {
 #pragma unroll
         for (int i = 0; i < S_::LOADS; ++i)
-            idp[i] = wids[min(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, Lw - 1)];
+            idp[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (j * kBN + drow0 + S_::ROWS_PER_LOAD * i),
+                                                          0, 0);
     };
     auto dma = [&](uint8_t LDS_AS *dst, int j) {
         if (!GATHER && (j + 1) * kBN <= Lw) {
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < S_::LOADS; ++i) {
                 const int lo = (wave * (kBN / kWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
-                const int o = int(idp[i] - vrow0) * int(row_bytes) + 2 * dchunk[i];
+                const int o = int(__umul24(uint32_t(idp[i]), row_bytes)) + 2 * dchunk[i];
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (void LDS_AS *)(dst + lo), 16, o, 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + S_::TILE + lo), 16, o, 0, 0, 0);
             }
@@ -153,7 +164,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                 const int r = min(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, M - 1);
                 const int lo = (wave * (kBN / kWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
                 if (r < Lw) {
-                    const int o = (GATHER ? int(idp[i] - vrow0) : r) * int(row_bytes) + 2 * dchunk[i];
+                    const int o = (GATHER ? int(__umul24(uint32_t(idp[i]), row_bytes)) : r * int(row_bytes)) +
+                                  2 * dchunk[i];
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (void LDS_AS *)(dst + lo), 16, o, 0, 0, 0);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + S_::TILE + lo), 16, o, 0,
                                                              0, 0);
@@ -327,7 +339,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     if (qrow >= M) return;
     const float inv = 1.0f / l;
     if (qrow < Lw) {
-        uint16_t *dst = out + vrow(qrow) * rs + hd;
+        uint16_t *dst = out + qtrow * rs + hd;
 #pragma unroll
         for (int t = 0; t < S_::DT; ++t)
 #pragma unroll
@@ -356,18 +368,17 @@ int attn_bf16_tile_m(int, bool) { return 32 * kItemWaves; }
 
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
-                            float *ws, const int32_t *offsets, const int32_t *ids,
-                            const Item *items, int n_items, int n_heads, int text_len, float scale,
-                            hipStream_t s) {
+                            float *ws, const int32_t *rel, const ItemDesc *items, int n_items,
+                            int n_heads, int text_len, float scale, hipStream_t s) {
     if (n_items <= 0) return hipSuccess;
     const float c2 = scale * kLog2e;
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
     auto launch = [&](auto kern) {
         kern<<<dim3(n_items), dim3(64 * kItemWaves), 0, s>>>(U(q), U(k), U(v), U(tq), U(tk), U(tv),
-                                                              static_cast<uint16_t *>(out), ws, offsets,
-                                                              ids, items, n_heads, text_len, c2);
+                                                              static_cast<uint16_t *>(out), ws, rel, items,
+                                                              n_heads, text_len, c2);
     };
-    const bool g = ids != nullptr;
+    const bool g = rel != nullptr;
     if (head_dim == 128)
         g ? launch(attn_bf16_kernel<128, kItemWaves, true>) : launch(attn_bf16_kernel<128, kItemWaves, false>);
     else if (head_dim == 64)

@@ -19,13 +19,30 @@ namespace wsp {
 // y = (head << 16) | query tile.
 using Item = int2;
 
+// Work item of the per-item bf16 kernel with its window resolved on the host,
+// so that a work group starts with one scalar load instead of a chain of
+// dependent table loads.
+struct alignas(32) ItemDesc {
+    int32_t w;      // window id (-1: nothing to do)
+    int32_t hq;     // (head << 16) | query tile
+    int32_t off;    // first layout row of the window
+    int32_t lw;     // video rows of the window
+    int32_t vrow0;  // tensor row the window's video rows are addressed from
+                    // (layout order: off; canonical order: its smallest id)
+    int32_t vrows;  // tensor rows from vrow0 that the window's rows span
+    int32_t pad[2];
+};
+
 struct DeviceTables {
     int32_t *offsets = nullptr;                                 // [n_windows + 1]
     int32_t *ids = nullptr;                                     // [n_tokens]
+    int32_t *rel = nullptr;                                     // [n_tokens] ids - first id of the window
     int32_t *pos = nullptr;                                     // [n_tokens] window positions
     std::map<std::tuple<int, int, int, int>, int32_t *> perm;   // src layout -> perm
     // (H, Lt, BM, order, persistent work groups) -> work list
     std::map<std::tuple<int, int, int, int, int>, std::pair<Item *, int>> items;
+    // (H, Lt, BM, order, canonical-order I/O) -> resolved work list
+    std::map<std::tuple<int, int, int, int, int>, std::pair<ItemDesc *, int>> descs;
 };
 
 }  // namespace wsp
@@ -73,21 +90,24 @@ int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out);
 int device_positions(wsp_plan_t &p, int dev, int32_t **out);
 int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
                  int n_groups, Item **out, int *count);
+int device_rel_ids(wsp_plan_t &p, int dev, int32_t **out);
+int device_item_descs(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
+                      bool gather, ItemDesc **out, int *count);
 
 // ---- kernel launchers -------------------------------------------------------
 // relayout.hip
 hipError_t launch_relayout(const void *x, void *y, const int32_t *perm, int64_t n_rows,
                            int64_t row_bytes, hipStream_t s);
 // attn_bf16.hip: the per-item bf16 kernel (one work group per item) and its
-// query-tile height.  ids != NULL selects canonical-order q/k/v/out gathered
-// through the plan's ids table.
+// query-tile height.  rel != NULL selects canonical-order q/k/v/out: video
+// row r of window w is tensor row vrow0(w) + rel[offsets[w] + r] (the plan's
+// ids relative to the window's smallest id; items resolved to match).
 int attn_bf16_tile_m(int head_dim, bool gather);
 hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
-                            float *ws, const int32_t *offsets, const int32_t *ids,
-                            const Item *items, int n_items, int n_heads, int text_len, float scale,
-                            hipStream_t s);
-// attn_bf16_persist.hip: the persistent bf16 kernel (default): n_groups
+                            float *ws, const int32_t *rel, const ItemDesc *items, int n_items,
+                            int n_heads, int text_len, float scale, hipStream_t s);
+// attn_bf16_persist.hip: the persistent bf16 kernel (short windows): n_groups
 // resident work groups walk items[r * n_groups + g], r < rounds.
 int attn_bf16_persist_tile_m();
 hipError_t launch_attn_bf16_persist(int head_dim, const void *q, const void *k, const void *v,
