@@ -213,8 +213,7 @@ enum wsp_attn_flags {
  * Arguments, layouts, ownership and errors as wsp_window_attn, plus
  * flags  WSP_ATTN_IO_LAYOUT or WSP_ATTN_IO_CANONICAL (other bits: WSP_EINVAL).
  * bf16 with WSP_ATTN_IO_CANONICAL also returns WSP_ERANGE when a window's
- * canonical rows span 2 GiB or more of q/k/v, or a q/k/v row (n_heads *
- * head_dim * 2 bytes) is 16 MiB or more.
+ * canonical rows (smallest to largest id) span 2 GiB or more of q/k/v.
  * The first canonical call for a plan on a device uploads its ids table (and,
  * for bf16, the same ids relative to each window's smallest id).
  */

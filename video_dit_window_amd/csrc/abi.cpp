@@ -374,9 +374,10 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
         if (rows * row_bytes >= (int64_t(1) << 31))
             return fail(WSP_ERANGE, gather ? "a window's canonical rows span 2 GiB or more"
                                            : "a window's rows (or the text rows) take 2 GiB or more");
-        // canonical order: row offsets are 24-bit products (relative id x row bytes)
-        if (gather && row_bytes >= (int64_t(1) << 24))
-            return fail(WSP_ERANGE, "q/k/v rows of 16 MiB or more");
+        // Canonical order: the kernel forms row offsets as 24-bit products
+        // (relative id x row bytes).  Exact: row_bytes <= 32767 * 128 * 2 < 2^24
+        // (n_heads and head_dim checked above), and relative id < span <
+        // 2^31 / row_bytes <= 2^24 because row_bytes >= 128.
     }
     if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
     const int order = g_attn_order.load();

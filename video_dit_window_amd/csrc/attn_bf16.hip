@@ -129,8 +129,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     // one tile ahead of their DMA by buffer loads whose per-lane offset holds
     // the row (the range check covers it: rows past the window read 0, and
     // such rows only reach the DMA as masked keys).  The DMA offset is then
-    // one 24-bit multiply-add (the host keeps row_bytes < 2^24 and every
-    // offset < 2^31).
+    // one 24-bit multiply-add, exact because the host's limits keep row_bytes
+    // and the relative ids below 2^24 and every offset below 2^31.
     const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int32_t *>(GATHER ? wrel : rel), 0, GATHER ? 4 * Lw : 0, kBufferFlags);
     int idp[S_::LOADS];
