@@ -179,7 +179,7 @@ def main():
                          "reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}); "
               "the multi-GPU window-parallel path is not built.", file=sys.stderr)
         sys.exit(2)
 
