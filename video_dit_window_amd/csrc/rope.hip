@@ -13,8 +13,8 @@
 // to the tensor's dtype.
 //
 // One wavefront per destination row, 16 bytes per lane per step (8 bf16 or
-// 4 float32 channels = 4 or 2 pairs, never straddling a head), non-temporal
-// loads and stores as in the plain relayout.
+// 4 float32 channels = 4 or 2 pairs, never straddling a head), four steps'
+// non-temporal loads issued before their stores as in the plain relayout.
 
 #include "wsp_internal.h"
 
@@ -23,6 +23,7 @@ namespace wsp {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kUnroll = 4;      // 16-byte chunks per lane loaded before their stores
 constexpr int kHeadDim = 128;
 constexpr int kSpan = 126;      // 3 * (128 / 3)
 constexpr int kAxisPairs = 21;  // 42 channels per axis block
@@ -51,35 +52,54 @@ __global__ __launch_bounds__(64 * kWaves) void rope_kernel(
     }
     constexpr int EL = BF16 ? 8 : 4;         // channels per 16-byte chunk
     constexpr int CPH = kHeadDim / EL;       // chunks per head
+    static_assert(64 % CPH == 0, "a lane must see the same channels in every head");
+    // The lane's chunks all start at channel d0 of their head, so its pairs
+    // and their (cos, sin) are the same for every chunk of the row.
+    const int d0 = (lane % CPH) * EL;
+    float2 t[EL / 2];
+#pragma unroll
+    for (int e = 0; e < EL / 2; ++e) {
+        const int k = d0 / 2 + e;
+        t[e] = float2{1.f, 0.f};             // pass-through pairs (not applied)
+        if (2 * k < kSpan) {
+            const int axis = k / kAxisPairs;
+            t[e] = cs[p[axis] * kAxisPairs + (k - axis * kAxisPairs)];
+        }
+    }
     const u32x4 *src = x + srow * chunks_per_row;
     u32x4 *dst = y + row * chunks_per_row;
-    for (int ch = lane; ch < chunks_per_row; ch += 64) {
-        const u32x4 raw = __builtin_nontemporal_load(src + ch);
-        const int d0 = (ch % CPH) * EL;      // first channel of the chunk in its head
-        uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-        uint32_t o[4];
+    for (int base = 0; base < chunks_per_row; base += 64 * kUnroll) {
+        u32x4 raw[kUnroll];
 #pragma unroll
-        for (int e = 0; e < EL / 2; ++e) {   // pair index k = d0/2 + e
-            const int k = d0 / 2 + e;
-            f32x2 v;
-            if constexpr (BF16) {
-                v = __builtin_convertvector(__builtin_bit_cast(bf16x2, w[e]), f32x2);
-            } else {
-                v = f32x2{__uint_as_float(w[2 * e]), __uint_as_float(w[2 * e + 1])};
-            }
-            if (2 * k < kSpan) {
-                const int axis = k / kAxisPairs;
-                const float2 t = cs[p[axis] * kAxisPairs + (k - axis * kAxisPairs)];
-                v = f32x2{fmaf(v.x, t.x, -v.y * t.y), fmaf(v.x, t.y, v.y * t.x)};
-            }
-            if constexpr (BF16) {
-                o[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-            } else {
-                o[2 * e] = __float_as_uint(v.x);
-                o[2 * e + 1] = __float_as_uint(v.y);
-            }
+        for (int i = 0; i < kUnroll; ++i) {
+            const int ch = base + lane + 64 * i;
+            if (ch < chunks_per_row) raw[i] = __builtin_nontemporal_load(src + ch);
         }
-        __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, dst + ch);
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            const int ch = base + lane + 64 * i;
+            if (ch >= chunks_per_row) continue;
+            uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < EL / 2; ++e) {   // pair index k = d0/2 + e
+                f32x2 v;
+                if constexpr (BF16) {
+                    v = __builtin_convertvector(__builtin_bit_cast(bf16x2, w[e]), f32x2);
+                } else {
+                    v = f32x2{__uint_as_float(w[2 * e]), __uint_as_float(w[2 * e + 1])};
+                }
+                if (2 * (d0 / 2 + e) < kSpan)
+                    v = f32x2{fmaf(v.x, t[e].x, -v.y * t[e].y), fmaf(v.x, t[e].y, v.y * t[e].x)};
+                if constexpr (BF16) {
+                    o[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+                } else {
+                    o[2 * e] = __float_as_uint(v.x);
+                    o[2 * e + 1] = __float_as_uint(v.y);
+                }
+            }
+            __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, dst + ch);
+        }
     }
 }
 
