@@ -53,8 +53,8 @@ CANONICAL = 2
 # capped at 30 frames.
 MAX_TEMPORAL_WINDOW = 30
 
-# [WSP] "Window layouts": "moves every cut by half a window".  For an odd
-# window w half a window is not an integer; this oracle reads it as
+# [WSP] "Window layouts": the shifted tiling moves each cut by half a window.
+# For an odd window w that is not an integer; this oracle reads it as
 # floor(w / 2).  (Unpinned by the pages; see the module docstring.)
 SHIFT_FLOOR = True
 
