@@ -128,19 +128,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     // Gather mode: relative ids of the rows of the next tile to move, loaded
     // one tile ahead of their DMA by buffer loads whose per-lane offset holds
     // the row (the range check covers it: rows past the window read 0, and
-    // such rows only reach the DMA as masked keys).  The DMA offset is then
-    // one 24-bit multiply-add, exact because the host's limits keep row_bytes
-    // and the relative ids below 2^24 and every offset below 2^31.
+    // such rows only reach the DMA as masked keys).  Two register sets
+    // alternate: the next tile's ids are requested before the current tile's
+    // DMA, so the tile's closing vmcnt wait does not end on them.  The DMA
+    // offset is one 24-bit multiply-add, exact because the host's limits keep
+    // row_bytes and the relative ids below 2^24 and every offset below 2^31.
     const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int32_t *>(GATHER ? wrel : rel), 0, GATHER ? 4 * Lw : 0, kBufferFlags);
-    int idp[S_::LOADS];
-    auto load_ids = [&](int j) {
+    int idA[S_::LOADS], idB[S_::LOADS];
+    auto load_ids = [&](int (&idp)[S_::LOADS], int j) {
 #pragma unroll
         for (int i = 0; i < S_::LOADS; ++i)
             idp[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (j * kBN + drow0 + S_::ROWS_PER_LOAD * i),
                                                           0, 0);
     };
-    auto dma = [&](uint8_t LDS_AS *dst, int j) {
+    auto dma = [&](uint8_t LDS_AS *dst, int j, int (&idp)[S_::LOADS], int (&idn)[S_::LOADS]) {
+        if constexpr (GATHER) load_ids(idn, j + 1);
         if (!GATHER && (j + 1) * kBN <= Lw) {
             const int soff = j * kBN * int(row_bytes);
 #pragma unroll
@@ -181,7 +184,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                 }
             }
         }
-        if constexpr (GATHER) load_ids(j + 1);
     };
 
     // LDS byte offsets of this lane's operands inside a stage.
@@ -217,8 +219,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     // query tile of a window) only moves its share of the K/V tiles and
     // meets the barriers: the SIMD it shares then runs the other wave alone.
     const bool active = qt * kBM + wave * 32 < M;
-    auto tile = [&](const uint8_t LDS_AS *cur, uint8_t LDS_AS *nxt, int j) {
-        if (j + 1 < ntiles) dma(nxt, j + 1);
+    auto tile = [&](const uint8_t LDS_AS *cur, uint8_t LDS_AS *nxt, int j, int (&idu)[S_::LOADS],
+                    int (&idn)[S_::LOADS]) {
+        if (j + 1 < ntiles) dma(nxt, j + 1, idu, idn);
         if (active) {
 
         // S^T for 64 keys (two 32-key blocks) x this wave's 32 queries.  The
@@ -325,13 +328,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 
     uint8_t LDS_AS *const st0 = (uint8_t LDS_AS *)stage0;
     uint8_t LDS_AS *const st1 = (uint8_t LDS_AS *)stage1;
-    if constexpr (GATHER) load_ids(0);
-    dma(st0, 0);
+    if constexpr (GATHER) load_ids(idA, 0);
+    dma(st0, 0, idA, idB);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     for (int j = 0; j < ntiles; j += 2) {
-        tile(st0, st1, j);
-        if (j + 1 < ntiles) tile(st1, st0, j + 1);
+        tile(st0, st1, j, idB, idA);
+        if (j + 1 < ntiles) tile(st1, st0, j + 1, idA, idB);
     }
 
     // Normalise and store: lane holds query qrow, dims 32t + 8g + 4hh + 0..3.
