@@ -126,6 +126,33 @@ def test_bf16_unscaled_inputs(gpu):
     run_full(w, "regular", check_bf16)
 
 
+@pytest.mark.parametrize("std", [4.0, 8.0])
+@pytest.mark.parametrize("sched", ["per_item", "persistent"])
+def test_bf16_large_scores(gpu, std, sched):
+    """q, k, v of standard deviation 4 or 8: logits of standard deviation
+    ~16 or ~64 (nearly one-hot softmax with near-tied keys in some rows).
+    A work item's first tile overflows float32 before its maximum is known
+    (std 8), and later tiles raise the maximum often (the exact path of the
+    lazy online softmax).  Both schedules, element by element against the
+    oracle; canonical-order I/O gives the same bits."""
+    import torch
+    w = I.custom(f"mid_large_{int(std)}", 6, 30, 52, 2, 3, 3, 2, 128, 40, "bf16", std=std,
+                 index=322 + int(std))
+    W.set_attn_schedule(W.SCHED_PERSISTENT if sched == "persistent" else W.SCHED_PER_ITEM)
+    try:
+        out, txt = run_full(w, "shifted", check_bf16)
+        geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+        wp, wc = W.Plan(*geo, W.SHIFTED), W.canonical(*geo[:3])
+        d = upload(I.qkv(w), "bf16")
+        oc, tc = W.window_attn(wp, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"],
+                               canonical=True)
+    finally:
+        W.set_attn_schedule(W.SCHED_AUTO)
+    torch.cuda.synchronize()
+    assert torch.equal(oc.view(torch.int16), W.relayout(out, wp, wc).view(torch.int16))
+    assert torch.equal(tc.view(torch.int16), txt.view(torch.int16))
+
+
 def test_bf16_explicit_scale(gpu):
     w = I.custom("mid_scale", 6, 30, 52, 2, 3, 3, 2, 128, 40, "bf16", std=1.0, index=321)
     run_full(w, "shifted", check_bf16, scale=0.05)

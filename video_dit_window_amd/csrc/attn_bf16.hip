@@ -16,13 +16,9 @@
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16 with K from LDS as the A operand
 //                   and Q in registers as B.  The transposed product leaves
 //                   each lane with ONE query column and 32 of its keys.
-//   softmax         float32 in log2 units: the queries are pre-scaled by
-//                   scale * log2(e) (rounded to bf16) and every S product
-//                   starts from the negated running maximum, so exp2 takes
-//                   the product as it leaves the matrix core; the running
-//                   maximum moves only on a work item's first tile and when
-//                   a tile's probabilities would exceed 2^20 (detected from
-//                   the row sum).
+//   softmax         float32, exp2 with the scale folded into one FMA; the
+//                   running maximum moves only when a tile's probabilities
+//                   would exceed 2^20 (detected from the row sum).
 //   O^T += V^T P^T  the probabilities stay in registers as bf16 B operands;
 //                   V^T comes from the row-major V tile through the gfx950
 //                   LDS transpose read (ds_read_b64_tr_b16).
@@ -94,10 +90,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         for (int s = 0; s < S_::KSTEPS; ++s)
             Qr[s] = *reinterpret_cast<const bf16x8 *>(p + 16 * s + 8 * hh);
     }
-    // Queries pre-scaled by c2 = scale * log2(e): scores leave the matrix
-    // cores in log2 units.
-#pragma unroll
-    for (int s = 0; s < S_::KSTEPS; ++s) Qr[s] = scale_bf16x8(Qr[s], c2);
 
     // DMA of one K/V tile.  Wave `wave` moves rows wave*16 + ROWS_PER_LOAD*i
     // + lane/CH (i < LOADS); lane's 16 bytes land at LDS chunk lane%CH of its
@@ -218,10 +210,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     f32x16 O[S_::DT];
 #pragma unroll
     for (int t = 0; t < S_::DT; ++t) O[t] = f32x16{};
-    // Running maximum (log2 units) and its negation broadcast as the
-    // accumulator every S product starts from; running row sum.
-    float mcs = 0.f, l_run = 0.f;
-    f32x16 Cneg = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     const int ntiles = (M + kBN - 1) / kBN;
 
@@ -250,7 +239,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 #pragma unroll
         for (int s = 0; s < S_::KSTEPS; ++s) {
 #pragma unroll
-            for (int mk = 0; mk < 2; ++mk) S[mk] = mfma(ka[s][mk], Qr[s], s == 0 ? Cneg : S[mk]);
+            for (int mk = 0; mk < 2; ++mk) S[mk] = mfma(ka[s][mk], Qr[s], S[mk]);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             if (s + 2 < S_::KSTEPS) {
                 kread(s + 2);
@@ -265,10 +254,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                     if (j * kBN + 32 * mk + 8 * (r >> 2) + 4 * hh + (r & 3) >= M) S[mk][r] = -INFINITY;
         }
 
-        // p = 2^(S - running max) packed to bf16 pairs (P^T B operands, one
+        // p = 2^(s*c2 - m_run*c2) packed to bf16 pairs (P^T B operands, one
         // per 16-key k-step); the row sum adds the same rounded values.
         bf16x8 P[4];
         auto probs = [&]() {
+            const float mc = m_run * c2;
             float sum = 0.f;
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) {
@@ -276,8 +266,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                 u32x4 pk;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p0 = __builtin_amdgcn_exp2f(S[mk][r0 + 2 * i]);
-                    const float p1 = __builtin_amdgcn_exp2f(S[mk][r0 + 2 * i + 1]);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i], c2, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i + 1], c2, -mc));
                     const bf16x2 pp = to_bf16x2(p0, p1);
                     sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
                     pk[i] = __builtin_bit_cast(uint32_t, pp);
@@ -286,9 +276,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             }
             return sum;
         };
-        // Only on the first tile and when some probability would exceed 2^20
-        // does the wave take the exact path: tile maximum tm (relative to the
-        // running one), rescale of O and l by 2^-tm, recompute.
+        // Only when some probability would exceed 2^20 (always on the first
+        // tile, where m_run = -inf) does the wave take the exact path: tile
+        // maximum, rescale of O and l by 2^((m_old - m_new)*c2), recompute.
         // V^T operands (transpose reads) of one 16-key step; those of the
         // first step are read while the softmax runs.
         auto vread = [&](int cs, bf16x8 (&dst)[S_::DT]) {
@@ -305,8 +295,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         bf16x8 va[2][S_::DT];
         vread(0, va[0]);
         float tsum = probs();
-        if (__builtin_amdgcn_ballot_w64(j == 0 || !(tsum <= kMaxTileSum)))
-            tsum = new_max(j == 0, S, O, mcs, l_run, Cneg, probs);
+        if (__builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
+            float m = S[0][0];
+#pragma unroll
+            for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) m = fmaxf(m, S[mk][r]);
+            const float m_new = fmaxf(m_run, halves_max(m));
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < S_::DT; ++t) O[t] *= alpha;
+            tsum = probs();
+        }
         l_run += tsum;
 
         // O^T += V^T P^T over the tile's four 16-key k-steps, the operands

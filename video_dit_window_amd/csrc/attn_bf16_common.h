@@ -65,42 +65,5 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, to_bf16x2(lo, hi));
 }
 
-// Eight bf16 values times c, rounded back to bf16 (nearest even).
-__device__ inline bf16x8 scale_bf16x8(bf16x8 x, float c) {
-    typedef float f32x8 __attribute__((ext_vector_type(8)));
-    return __builtin_convertvector(__builtin_convertvector(x, f32x8) * c, bf16x8);
-}
-
-// Exact path of the lazy online softmax, in log2 units.  S holds the tile's
-// scores relative to the running maximum mcs (keys past the sequence -inf);
-// tm is the tile maximum over both lane halves (all keys of the query).  On
-// an item's first tile (O and l still zero) the reference moves to tm; later
-// it moves up by max(tm, 0) (the path is taken wave-wide, so a lane's own
-// maximum may not have grown), O and l scaling by 2^-shift.  S shifts with
-// the reference, the broadcast -mcs follows, the probabilities are recomputed.
-template <int DT, class Probs>
-__device__ inline float new_max(bool first, f32x16 (&S)[2], f32x16 (&O)[DT], float &mcs,
-                                float &l_run, f32x16 &Cneg, Probs &&probs) {
-    float m = S[0][0];
-#pragma unroll
-    for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, S[mk][r]);
-    const float tm = halves_max(m);
-    const float shift = first ? tm : fmaxf(tm, 0.f);
-    const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-shift);
-    mcs += shift;
-    l_run *= alpha;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) O[t] *= alpha;
-#pragma unroll
-    for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[mk][r] -= shift;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Cneg[r] = -mcs;
-    return probs();
-}
-
 }  // namespace
 }  // namespace wsp

@@ -229,9 +229,6 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
         for (int s2 = 0; s2 < S_::KSTEPS; ++s2)
             Qr[s2] = *reinterpret_cast<const bf16x8 LDS_AS *>(qb + 16 * ((2 * s2 + hh) ^ swz<D>(l32)));
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        // pre-scaled by c2 = scale * log2(e): scores in log2 units
-#pragma unroll
-        for (int s2 = 0; s2 < S_::KSTEPS; ++s2) Qr[s2] = scale_bf16x8(Qr[s2], c2);
     };
     // Tensor row of this lane's query (video rows; -1 for text rows).
     auto q_tensor_row = [&](const PkItem &t) -> int64_t {
@@ -262,10 +259,7 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
 
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     f32x16 O[S_::DT];
-    // Running maximum (log2 units), its negation broadcast as the accumulator
-    // every S product starts from, running row sum.
-    float mcs, l_run;
-    f32x16 Cneg;
+    float m_run, l_run;
 
     PkItem cur = load_item(0);
     if (!cur.valid) return;
@@ -310,7 +304,7 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
 #pragma unroll
         for (int s = 0; s < S_::KSTEPS; ++s) {
 #pragma unroll
-            for (int mk = 0; mk < 2; ++mk) S[mk] = mfma(ka[s][mk], Qr[s], s == 0 ? Cneg : S[mk]);
+            for (int mk = 0; mk < 2; ++mk) S[mk] = mfma(ka[s][mk], Qr[s], S[mk]);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             if (s + 2 < S_::KSTEPS) {
                 kread(s + 2);
@@ -327,10 +321,11 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
             }
         }
 
-        // p = 2^(S - running max) packed to bf16 pairs (P^T B operands, one
+        // p = 2^(s*c2 - m_run*c2) packed to bf16 pairs (P^T B operands, one
         // per 16-key k-step); the row sum adds the same rounded values.
         bf16x8 P[4];
         auto probs = [&]() {
+            const float mc = m_run * c2;
             float sum = 0.f;
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) {
@@ -338,8 +333,8 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
                 u32x4 pk;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p0 = __builtin_amdgcn_exp2f(S[mk][r0 + 2 * i]);
-                    const float p1 = __builtin_amdgcn_exp2f(S[mk][r0 + 2 * i + 1]);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i], c2, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i + 1], c2, -mc));
                     const bf16x2 pp = to_bf16x2(p0, p1);
                     sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
                     pk[i] = __builtin_bit_cast(uint32_t, pp);
@@ -362,10 +357,23 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
         bf16x8 va[2][S_::DT];
         vread(0, va[0]);
         float tsum = probs();
-        // Only on an item's first tile and when some probability would
-        // exceed 2^20 does the wave take the exact path (new_max).
-        if (__builtin_amdgcn_ballot_w64(j == 0 || !(tsum <= kMaxTileSum)))
-            tsum = new_max(j == 0, S, O, mcs, l_run, Cneg, probs);
+        // Only when some probability would exceed 2^20 (always on an item's
+        // first tile, where m_run = -inf) does the wave take the exact path:
+        // tile maximum, rescale of O and l by 2^((m_old - m_new)*c2), recompute.
+        if (__builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
+            float m = S[0][0];
+#pragma unroll
+            for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) m = fmaxf(m, S[mk][r]);
+            const float m_new = fmaxf(m_run, halves_max(m));
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < S_::DT; ++t) O[t] *= alpha;
+            tsum = probs();
+        }
         l_run += tsum;
 
         // O^T += V^T P^T over the tile's four 16-key k-steps, the operands of
@@ -400,9 +408,8 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
         read_q();
 #pragma unroll
         for (int t = 0; t < S_::DT; ++t) O[t] = f32x16{};
-        mcs = 0.f;
+        m_run = -INFINITY;
         l_run = 0.f;
-        Cneg = f32x16{};
         int j = 0;
         for (; j + 2 < cur.np; j += 2) {
             tile(st0, st1, j, KindC<kMid>{});
