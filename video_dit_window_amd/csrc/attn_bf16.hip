@@ -276,9 +276,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             }
             return sum;
         };
-        // Only when some probability would exceed 2^20 (always on the first
-        // tile, where m_run = -inf) does the wave take the exact path: tile
-        // maximum, rescale of O and l by 2^((m_old - m_new)*c2), recompute.
+        // Only on the first tile (m_run = -inf) and when some probability
+        // would exceed 2^20 does the wave take the exact path: tile maximum,
+        // rescale of O and l by 2^((m_old - m_new)*c2), recompute.  The first
+        // tile goes there directly.
         // V^T operands (transpose reads) of one 16-key step; those of the
         // first step are read while the softmax runs.
         auto vread = [&](int cs, bf16x8 (&dst)[S_::DT]) {
@@ -294,8 +295,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         };
         bf16x8 va[2][S_::DT];
         vread(0, va[0]);
-        float tsum = probs();
-        if (__builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
+        float tsum = j == 0 ? 0.f : probs();
+        if (j == 0 || __builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
             float m = S[0][0];
 #pragma unroll
             for (int mk = 0; mk < 2; ++mk)

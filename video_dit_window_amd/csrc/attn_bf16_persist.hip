@@ -356,11 +356,12 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
         };
         bf16x8 va[2][S_::DT];
         vread(0, va[0]);
-        float tsum = probs();
-        // Only when some probability would exceed 2^20 (always on an item's
-        // first tile, where m_run = -inf) does the wave take the exact path:
-        // tile maximum, rescale of O and l by 2^((m_old - m_new)*c2), recompute.
-        if (__builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
+        // Only on an item's first tile (m_run = -inf; it goes there directly)
+        // and when some probability would exceed 2^20 does the wave take the
+        // exact path: tile maximum, rescale of O and l by
+        // 2^((m_old - m_new)*c2), recompute.
+        float tsum = j == 0 ? 0.f : probs();
+        if (j == 0 || __builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
             float m = S[0][0];
 #pragma unroll
             for (int mk = 0; mk < 2; ++mk)
