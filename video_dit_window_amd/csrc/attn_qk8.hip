@@ -217,11 +217,14 @@ __global__ __launch_bounds__(64 * kQ8Waves, 1) void attn_qk8_kernel(
 #pragma unroll
             for (int mk = 0; mk < 2; ++mk) S[mk] = mfma8(ka[s][mk], Qr[s], S[mk]);
         if ((j + 1) * kBN > M) {  // keys past the end of the joint sequence
+            // element r of S[mk] is key 32mk + 8(r/4) + (r%4) of the tile
+            // counted from this lane's first, j*kBN + 4hh
+            const int lim = M - j * kBN - 4 * hh;
 #pragma unroll
             for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (j * kBN + 32 * mk + 8 * (r >> 2) + 4 * hh + (r & 3) >= M) S[mk][r] = -INFINITY;
+                    if (32 * mk + 8 * (r >> 2) + (r & 3) >= lim) S[mk][r] = -INFINITY;
         }
 
         // Softmax and O^T += V^T P^T exactly as attn_bf16.hip.
@@ -258,8 +261,9 @@ __global__ __launch_bounds__(64 * kQ8Waves, 1) void attn_qk8_kernel(
         };
         bf16x8 va[2][S_::DT];
         vread(0, va[0]);
-        float tsum = probs();
-        if (__builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
+        // The first tile (m_run = -inf) goes straight to the exact path.
+        float tsum = j == 0 ? 0.f : probs();
+        if (j == 0 || __builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
             float m = S[0][0];
 #pragma unroll
             for (int mk = 0; mk < 2; ++mk)
@@ -268,9 +272,11 @@ __global__ __launch_bounds__(64 * kQ8Waves, 1) void attn_qk8_kernel(
             const float m_new = fmaxf(m_run, halves_max(m));
             const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
             m_run = m_new;
-            l_run *= alpha;
+            if (j != 0) {  // on the first tile O and l are still zero
+                l_run *= alpha;
 #pragma unroll
-            for (int t = 0; t < S_::DT; ++t) O[t] *= alpha;
+                for (int t = 0; t < S_::DT; ++t) O[t] *= alpha;
+            }
             tsum = probs();
         }
         l_run += tsum;
