@@ -406,17 +406,17 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
     ItemDesc *descs = nullptr;
     int n_items = 0;
     int32_t *d_rel = nullptr;
-    if (dtype == WSP_BF16 && !persist) {
+    if (dtype == WSP_BF16 && !persist)
         rc = device_item_descs(*p, dev, n_heads, text_len, bm, order, gather, &descs, &n_items);
-        if (!rc && gather) rc = device_rel_ids(*p, dev, &d_rel);
-    } else
+    else
         rc = device_items(*p, dev, n_heads, text_len, bm, order, n_groups, &items, &n_items);
+    if (!rc && dtype == WSP_BF16 && gather) rc = device_rel_ids(*p, dev, &d_rel);
     if (rc) return rc;
     hipStream_t s = hipStream_t(stream);
     float *ws = static_cast<float *>(workspace);
     hipError_t e;
     if (persist)
-        e = launch_attn_bf16_persist(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, d_ids,
+        e = launch_attn_bf16_persist(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, d_ids, d_rel,
                                      items, n_groups, n_items / n_groups, n_heads, text_len, scale, s);
     else if (dtype == WSP_BF16)
         e = launch_attn_bf16(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_rel, descs, n_items,

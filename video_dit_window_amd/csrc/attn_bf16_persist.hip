@@ -64,7 +64,8 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ tq,
     const uint16_t *__restrict__ tk, const uint16_t *__restrict__ tv,
     uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ ids, const Item *__restrict__ items, int rounds, int H, int Lt,
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ rel, const Item *__restrict__ items,
+    int rounds, int H, int Lt,
     float c2) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     using S_ = Shape<D, kPkWaves>;
@@ -121,14 +122,22 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
     auto rsrc = [&](const uint16_t *base, uint32_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, int(bytes), kBufferFlags);
     };
-    // Canonical-order I/O: canonical ids of the rows the next DMA moves,
-    // loaded one DMA ahead (idp_ok false: not loaded, fetch at the DMA).
+    // Canonical-order I/O: ids, relative to the item's smallest id, of the
+    // rows the next DMA moves, loaded one DMA ahead (idp_ok false: not
+    // loaded, fetch at the DMA) by buffer loads over the window's entries
+    // (rows past the window read 0 and reach the DMA only as masked keys).
+    // A row's DMA offset is then one 24-bit multiply-add, exact because the
+    // host's limits keep row_bytes and the relative ids below 2^24.
     int idp[S_::LOADS];
     bool idp_ok = false;
+    auto rel_rsrc = [&](const PkItem &t) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(rel + t.off), 0, 4 * t.Lw, kBufferFlags);
+    };
     auto load_ids = [&](const PkItem &t, int j) {
+        const __amdgpu_buffer_rsrc_t irs = rel_rsrc(t);
 #pragma unroll
         for (int i = 0; i < S_::LOADS; ++i)
-            idp[i] = ids[t.off + min(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, t.Lw - 1)];
+            idp[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (j * kBN + drow0 + S_::ROWS_PER_LOAD * i), 0, 0);
         idp_ok = true;
     };
     // Tile j of item t into dst (K tile, then V tile).  Every DMA is a buffer
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
 #pragma unroll
             for (int i = 0; i < S_::LOADS; ++i) {
                 const int lo = (wave * (kBN / kPkWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
-                const int o = int(idp[i] - t.vrow0) * int(row_bytes) + 2 * dchunk[i];
+                const int o = int(__umul24(uint32_t(idp[i]), row_bytes)) + 2 * dchunk[i];
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (void LDS_AS *)(dst + lo), 16, o, 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + S_::TILE + lo), 16, o, 0, 0, 0);
             }
@@ -169,7 +178,8 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
                 const int r = min(j * kBN + drow0 + S_::ROWS_PER_LOAD * i, t.M - 1);
                 const int lo = (wave * (kBN / kPkWaves) + S_::ROWS_PER_LOAD * i) * S_::ROW;
                 if (r < t.Lw) {
-                    const int o = (GATHER ? int(idp[i] - t.vrow0) : r) * int(row_bytes) + 2 * dchunk[i];
+                    const int o = (GATHER ? int(__umul24(uint32_t(idp[i]), row_bytes)) : r * int(row_bytes)) +
+                                  2 * dchunk[i];
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (void LDS_AS *)(dst + lo), 16, o, 0, 0, 0);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + S_::TILE + lo), 16, o, 0,
                                                              0, 0);
@@ -197,9 +207,11 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
     auto q_row = [&](const PkItem &t) { return t.qt * kPkBM + wave * 32 + l32; };
     int qid[QLOADS];
     auto load_qids = [&](const PkItem &t) {
+        const __amdgpu_buffer_rsrc_t irs = rel_rsrc(t);
 #pragma unroll
         for (int i = 0; i < QLOADS; ++i)
-            qid[i] = ids[t.off + min(t.qt * kPkBM + wave * 32 + S_::ROWS_PER_LOAD * i + lane / S_::CH, t.Lw - 1)];
+            qid[i] = __builtin_amdgcn_raw_buffer_load_b32(
+                irs, 4 * (t.qt * kPkBM + wave * 32 + S_::ROWS_PER_LOAD * i + lane / S_::CH), 0, 0);
     };
     auto q_dma = [&](const PkItem &t) {
         const __amdgpu_buffer_rsrc_t qrs = rsrc(q + t.vrow0 * rs + t.hd, t.vrows * row_bytes);
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
             const int chunk = 16 * (dpc ^ swz<D>(rr));
             uint8_t LDS_AS *dst = (uint8_t LDS_AS *)qbuf + (wave * 32 + S_::ROWS_PER_LOAD * i) * S_::ROW;
             if (r < t.Lw) {
-                const int o = (GATHER ? int(qid[i] - t.vrow0) : r) * int(row_bytes) + chunk;
+                const int o = (GATHER ? int(__umul24(uint32_t(qid[i]), row_bytes)) : r * int(row_bytes)) + chunk;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (void LDS_AS *)dst, 16, o, 0, 0, 0);
             } else {
                 const int o = (r - t.Lw) * int(row_bytes) + chunk;
@@ -472,15 +484,15 @@ __global__ __launch_bounds__(64 * kPkWaves, 2) void attn_bf16_persist_kernel(
 hipError_t launch_attn_bf16_persist(int head_dim, const void *q, const void *k, const void *v,
                                     const void *tq, const void *tk, const void *tv, void *out,
                                     float *ws, const int32_t *offsets, const int32_t *ids,
-                                    const Item *items, int n_groups, int rounds, int n_heads,
-                                    int text_len, float scale, hipStream_t s) {
+                                    const int32_t *rel, const Item *items, int n_groups, int rounds,
+                                    int n_heads, int text_len, float scale, hipStream_t s) {
     if (n_groups <= 0 || rounds <= 0) return hipSuccess;
     const float c2 = scale * kLog2e;
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
     auto launch = [&](auto kern) {
         kern<<<dim3(n_groups), dim3(64 * kPkWaves), 0, s>>>(U(q), U(k), U(v), U(tq), U(tk), U(tv),
                                                              static_cast<uint16_t *>(out), ws, offsets, ids,
-                                                             items, rounds, n_heads, text_len, c2);
+                                                             rel, items, rounds, n_heads, text_len, c2);
     };
     const bool g = ids != nullptr;
     if (head_dim == 128) g ? launch(attn_bf16_persist_kernel<128, true>) : launch(attn_bf16_persist_kernel<128, false>);

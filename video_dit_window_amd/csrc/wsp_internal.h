@@ -113,8 +113,8 @@ int attn_bf16_persist_tile_m();
 hipError_t launch_attn_bf16_persist(int head_dim, const void *q, const void *k, const void *v,
                                     const void *tq, const void *tk, const void *tv, void *out,
                                     float *ws, const int32_t *offsets, const int32_t *ids,
-                                    const Item *items, int n_groups, int rounds, int n_heads,
-                                    int text_len, float scale, hipStream_t s);
+                                    const int32_t *rel, const Item *items, int n_groups, int rounds,
+                                    int n_heads, int text_len, float scale, hipStream_t s);
 // attn_f32.hip
 int attn_f32_tile_m(int head_dim);
 hipError_t launch_attn_f32(int head_dim, const float *q, const float *k, const float *v,
