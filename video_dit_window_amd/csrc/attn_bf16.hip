@@ -17,8 +17,9 @@
 //                   and Q in registers as B.  The transposed product leaves
 //                   each lane with ONE query column and 32 of its keys.
 //   softmax         float32, exp2 with the scale folded into one FMA; the
-//                   running maximum moves only when a tile's probabilities
-//                   would exceed 2^20 (detected from the row sum).
+//                   running maximum is set on a work item's first tile and
+//                   moves only when a tile's probabilities would exceed 2^20
+//                   (detected from the row sum).
 //   O^T += V^T P^T  the probabilities stay in registers as bf16 B operands;
 //                   V^T comes from the row-major V tile through the gfx950
 //                   LDS transpose read (ds_read_b64_tr_b16).
