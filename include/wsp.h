@@ -69,9 +69,10 @@ enum wsp_order {
 
 /* Schedule of the bf16 attention kernel (wsp_set_attn_schedule). */
 enum wsp_schedule {
-    WSP_SCHED_AUTO = 0,       /* by mean window length (wsp_set_attn_schedule) */
-    WSP_SCHED_PERSISTENT = 1, /* resident work groups walk per-CU item lists   */
-    WSP_SCHED_PER_ITEM = 2    /* one work group per item                       */
+    WSP_SCHED_AUTO = 0,         /* by mean window length (wsp_set_attn_schedule) */
+    WSP_SCHED_PERSISTENT = 1,   /* resident work groups walk per-CU item lists   */
+    WSP_SCHED_PER_ITEM = 2,     /* one work group per 256-query-row item         */
+    WSP_SCHED_PER_ITEM_128 = 3  /* one work group per 128-query-row item         */
 };
 
 /*
@@ -329,10 +330,12 @@ int wsp_set_attn_order(int order);
  * WSP_SCHED_PERSISTENT: one resident work group per compute unit walks a
  * host-built list of (window, head, 256-query-row) items, fetching the next
  * item's first K/V tile and query rows while the current item finishes.
- * WSP_SCHED_PER_ITEM: one work group per item.  WSP_SCHED_AUTO: persistent
- * when a window's joint sequence averages fewer than 1024 rows (short items,
- * where the per-item start-up is a visible share), else per item.  All run
- * the same per-tile arithmetic in the same order, so results are
+ * WSP_SCHED_PER_ITEM: one work group (8 wavefronts) per 256-query-row item.
+ * WSP_SCHED_PER_ITEM_128: one work group (4 wavefronts, two per compute
+ * unit) per 128-query-row item: less of a window's last query tile is
+ * empty.  WSP_SCHED_AUTO: WSP_SCHED_PER_ITEM_128 when a window's joint
+ * sequence averages fewer than 1024 rows, else WSP_SCHED_PER_ITEM.  All run
+ * the same per-wavefront arithmetic in the same order, so results are
  * bit-identical; the order set by wsp_set_attn_order applies to all.
  * Errors: WSP_EINVAL.
  */

@@ -127,18 +127,19 @@ def test_bf16_unscaled_inputs(gpu):
 
 
 @pytest.mark.parametrize("std", [4.0, 8.0])
-@pytest.mark.parametrize("sched", ["per_item", "persistent"])
+@pytest.mark.parametrize("sched", ["per_item", "per_item_128", "persistent"])
 def test_bf16_large_scores(gpu, std, sched):
     """q, k, v of standard deviation 4 or 8: logits of standard deviation
     ~16 or ~64 (nearly one-hot softmax with near-tied keys in some rows).
     A work item's first tile overflows float32 before its maximum is known
     (std 8), and later tiles raise the maximum often (the exact path of the
-    lazy online softmax).  Both schedules, element by element against the
+    lazy online softmax).  Every schedule, element by element against the
     oracle; canonical-order I/O gives the same bits."""
     import torch
     w = I.custom(f"mid_large_{int(std)}", 6, 30, 52, 2, 3, 3, 2, 128, 40, "bf16", std=std,
                  index=322 + int(std))
-    W.set_attn_schedule(W.SCHED_PERSISTENT if sched == "persistent" else W.SCHED_PER_ITEM)
+    W.set_attn_schedule({"per_item": W.SCHED_PER_ITEM, "per_item_128": W.SCHED_PER_ITEM_128,
+                         "persistent": W.SCHED_PERSISTENT}[sched])
     try:
         out, txt = run_full(w, "shifted", check_bf16)
         geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
@@ -181,8 +182,9 @@ def test_bf16_order_independent_and_deterministic(gpu):
 @pytest.mark.parametrize("canonical", [False, True], ids=["layout_io", "canonical_io"])
 def test_bf16_schedules_bit_identical(gpu, case, canonical):
     """The persistent schedule (resident work groups walking per-CU item
-    lists) and one work group per item run the same per-tile
-    arithmetic in the same order: identical bits, for both I/O orders."""
+    lists), one work group per 256-row item and one per 128-row item run the
+    same per-wavefront arithmetic in the same order: identical bits, for both
+    I/O orders."""
     import torch
     w = I.custom(*case, "bf16", index=300 + MID.index(case))
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
@@ -190,7 +192,7 @@ def test_bf16_schedules_bit_identical(gpu, case, canonical):
     res = {}
     for method in (W.REGULAR, W.SHIFTED):
         p = W.Plan(*geo, method)
-        for sched in (W.SCHED_PERSISTENT, W.SCHED_PER_ITEM):
+        for sched in (W.SCHED_PERSISTENT, W.SCHED_PER_ITEM, W.SCHED_PER_ITEM_128):
             W.set_attn_schedule(sched)
             try:
                 o, t = W.window_attn(p, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"],
@@ -200,16 +202,19 @@ def test_bf16_schedules_bit_identical(gpu, case, canonical):
             res[(method, sched)] = (o, t)
     torch.cuda.synchronize()
     for method in (W.REGULAR, W.SHIFTED):
-        (o1, t1), (o2, t2) = res[(method, W.SCHED_PERSISTENT)], res[(method, W.SCHED_PER_ITEM)]
-        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"{w.name} method {method}: video"
-        if w.text_len:
-            assert torch.equal(t1.view(torch.int16), t2.view(torch.int16)), f"{w.name} method {method}: text"
+        o1, t1 = res[(method, W.SCHED_PER_ITEM)]
+        for sched in (W.SCHED_PERSISTENT, W.SCHED_PER_ITEM_128):
+            o2, t2 = res[(method, sched)]
+            assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"{w.name} {method} {sched}: video"
+            if w.text_len:
+                assert torch.equal(t1.view(torch.int16), t2.view(torch.int16)), f"{w.name} {method} {sched}: text"
 
 
 @pytest.mark.parametrize("canonical", [False, True], ids=["layout_io", "canonical_io"])
 def test_1080p_schedules_bit_identical(gpu, canonical):
-    """Persistent and per-item schedules agree bit for bit on the full 1080p
-    grid (both layouts), in the launch configuration the benchmark times."""
+    """Persistent, 256-row and 128-row per-item schedules agree bit for bit on
+    the full 1080p grid (both layouts), in the launch configuration the
+    benchmark times."""
     import torch
     w = I.WORKLOADS["1080p_bf16"]
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
@@ -223,7 +228,7 @@ def test_1080p_schedules_bit_identical(gpu, canonical):
     for method in (W.REGULAR, W.SHIFTED):
         p = W.Plan(*geo, method)
         outs = []
-        for sched in (W.SCHED_PERSISTENT, W.SCHED_PER_ITEM):
+        for sched in (W.SCHED_PER_ITEM, W.SCHED_PERSISTENT, W.SCHED_PER_ITEM_128):
             W.set_attn_schedule(sched)
             try:
                 outs.append(W.window_attn(p, q, k, v, tq, tk, tv, canonical=canonical))
@@ -231,8 +236,9 @@ def test_1080p_schedules_bit_identical(gpu, canonical):
                 W.set_attn_schedule(W.SCHED_AUTO)
         torch.cuda.synchronize()
         log(f"  1080p method {method} canonical={canonical}: comparing schedules")
-        assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
-        assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+        for o, t in outs[1:]:
+            assert torch.equal(outs[0][0].view(torch.int16), o.view(torch.int16))
+            assert torch.equal(outs[0][1].view(torch.int16), t.view(torch.int16))
 
 
 # ------------------------------------------------------------------ full-size, sampled

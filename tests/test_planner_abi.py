@@ -182,9 +182,9 @@ def test_rope_argument_errors():
 
 def test_attn_schedule_option():
     L = raw()
-    assert L.wsp_set_attn_schedule(3) == -1
+    assert L.wsp_set_attn_schedule(4) == -1
     assert L.wsp_set_attn_schedule(-1) == -1
-    for sc in (W.SCHED_PER_ITEM, W.SCHED_PERSISTENT, W.SCHED_AUTO):
+    for sc in (W.SCHED_PER_ITEM, W.SCHED_PER_ITEM_128, W.SCHED_PERSISTENT, W.SCHED_AUTO):
         W.set_attn_schedule(sc)
 
 

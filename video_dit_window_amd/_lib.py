@@ -19,7 +19,7 @@ REGULAR, SHIFTED, CANONICAL = 0, 1, 2
 IO_LAYOUT, IO_CANONICAL = 0, 1
 F32, BF16 = 0, 1
 ORDER_LPT_XCD, ORDER_LPT, ORDER_ID = 0, 1, 2
-SCHED_AUTO, SCHED_PERSISTENT, SCHED_PER_ITEM = 0, 1, 2
+SCHED_AUTO, SCHED_PERSISTENT, SCHED_PER_ITEM, SCHED_PER_ITEM_128 = 0, 1, 2, 3
 METHODS = {"regular": REGULAR, "shifted": SHIFTED, "canonical": CANONICAL}
 
 _c_int, _c_i64, _c_sz, _c_vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p

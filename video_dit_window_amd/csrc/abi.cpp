@@ -381,15 +381,16 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
     }
     if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
     const int order = g_attn_order.load();
-    // Persistent work groups pay off when items are short: their per-item
-    // start-up (query rows and first K/V tile) is then a visible share.
+    // Short windows (joint sequences averaging < 1024 rows) take 128-row
+    // query tiles: a window's partly empty last tile then wastes less.
     const int sched = g_attn_sched.load();
     const bool short_items = (double(p->n) / double(p->nwin) + text_len) < 1024.0;
-    const bool persist =
-        dtype == WSP_BF16 && (sched == WSP_SCHED_PERSISTENT || (sched == WSP_SCHED_AUTO && short_items));
+    const bool persist = dtype == WSP_BF16 && sched == WSP_SCHED_PERSISTENT;
+    const bool small =
+        sched == WSP_SCHED_PER_ITEM_128 || (sched == WSP_SCHED_AUTO && short_items);
     const int bm = dtype != WSP_BF16 ? attn_f32_tile_m(head_dim)
                    : persist        ? attn_bf16_persist_tile_m()
-                                    : attn_bf16_tile_m(head_dim, gather);
+                                    : attn_bf16_tile_m(small);
 
     int dev = 0;
     WSP_HIP(hipGetDevice(&dev));
@@ -419,8 +420,8 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
         e = launch_attn_bf16_persist(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, d_ids, d_rel,
                                      items, n_groups, n_items / n_groups, n_heads, text_len, scale, s);
     else if (dtype == WSP_BF16)
-        e = launch_attn_bf16(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_rel, descs, n_items,
-                             n_heads, text_len, scale, s);
+        e = launch_attn_bf16(head_dim, small, q, k, v, txt_q, txt_k, txt_v, out, ws, d_rel, descs,
+                             n_items, n_heads, text_len, scale, s);
     else
         e = launch_attn_f32(head_dim, static_cast<const float *>(q), static_cast<const float *>(k),
                             static_cast<const float *>(v), static_cast<const float *>(txt_q),
@@ -661,7 +662,8 @@ int wsp_set_attn_order(int order) {
 
 int wsp_set_attn_schedule(int schedule) {
     g_last_error.clear();
-    if (schedule != WSP_SCHED_AUTO && schedule != WSP_SCHED_PERSISTENT && schedule != WSP_SCHED_PER_ITEM)
+    if (schedule != WSP_SCHED_AUTO && schedule != WSP_SCHED_PERSISTENT && schedule != WSP_SCHED_PER_ITEM &&
+        schedule != WSP_SCHED_PER_ITEM_128)
         return fail(WSP_EINVAL, "unknown attention schedule");
     g_attn_sched.store(schedule);
     return WSP_OK;

@@ -10,7 +10,8 @@
 // Work item = (window w, head h, tile of 256 query rows) of the joint query
 // sequence [q rows of w; txt_q]; the key/value sequence is [k/v rows of w;
 // txt_k/v].  A work group is 8 wavefronts of 32 query rows (one work group
-// per CU), 2 waves per SIMD, < 256 registers each.
+// per CU), 2 waves per SIMD, < 256 registers each (or, for short windows, 4
+// wavefronts and 128 rows, two work groups per CU).
 //
 // Per 64-key tile and wavefront:
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16 with K from LDS as the A operand
@@ -39,8 +40,9 @@ namespace wsp {
 namespace {
 
 // Waves per work group: 8 x 32 query rows, one work group per CU (2 waves
-// per SIMD).
-constexpr int kItemWaves = 8;
+// per SIMD); or 4 x 32 rows, two work groups per CU (short windows: less of
+// a window's last query tile is empty).  Same per-wave arithmetic.
+constexpr int kItemWaves = 8, kSmallItemWaves = 4;
 
 // GATHER: q, k, v and out hold rows in canonical token order; the video row
 // r of window w is canonical row vrow0 + rel[offsets[w] + r] (the plan's ids
@@ -374,27 +376,34 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 
 }  // namespace
 
-int attn_bf16_tile_m(int, bool) { return 32 * kItemWaves; }
+int attn_bf16_tile_m(bool small) { return 32 * (small ? kSmallItemWaves : kItemWaves); }
 
-hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
+hipError_t launch_attn_bf16(int head_dim, bool small, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
                             float *ws, const int32_t *rel, const ItemDesc *items, int n_items,
                             int n_heads, int text_len, float scale, hipStream_t s) {
     if (n_items <= 0) return hipSuccess;
     const float c2 = scale * kLog2e;
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
-    auto launch = [&](auto kern) {
-        kern<<<dim3(n_items), dim3(64 * kItemWaves), 0, s>>>(U(q), U(k), U(v), U(tq), U(tk), U(tv),
-                                                              static_cast<uint16_t *>(out), ws, rel, items,
-                                                              n_heads, text_len, c2);
+    auto launch = [&](auto kern, int waves) {
+        kern<<<dim3(n_items), dim3(64 * waves), 0, s>>>(U(q), U(k), U(v), U(tq), U(tk), U(tv),
+                                                         static_cast<uint16_t *>(out), ws, rel, items, n_heads,
+                                                         text_len, c2);
     };
-    const bool g = rel != nullptr;
-    if (head_dim == 128)
-        g ? launch(attn_bf16_kernel<128, kItemWaves, true>) : launch(attn_bf16_kernel<128, kItemWaves, false>);
-    else if (head_dim == 64)
-        g ? launch(attn_bf16_kernel<64, kItemWaves, true>) : launch(attn_bf16_kernel<64, kItemWaves, false>);
-    else
-        return hipErrorInvalidValue;
+    auto dispatch = [&](auto waves_c) {
+        constexpr int NW = decltype(waves_c)::value;
+        const bool g = rel != nullptr;
+        if (head_dim == 128)
+            g ? launch(attn_bf16_kernel<128, NW, true>, NW) : launch(attn_bf16_kernel<128, NW, false>, NW);
+        else if (head_dim == 64)
+            g ? launch(attn_bf16_kernel<64, NW, true>, NW) : launch(attn_bf16_kernel<64, NW, false>, NW);
+        else
+            return hipErrorInvalidValue;
+        return hipSuccess;
+    };
+    const hipError_t e = small ? dispatch(std::integral_constant<int, kSmallItemWaves>{})
+                               : dispatch(std::integral_constant<int, kItemWaves>{});
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -99,11 +99,12 @@ int device_item_descs(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm,
 hipError_t launch_relayout(const void *x, void *y, const int32_t *perm, int64_t n_rows,
                            int64_t row_bytes, hipStream_t s);
 // attn_bf16.hip: the per-item bf16 kernel (one work group per item) and its
-// query-tile height.  rel != NULL selects canonical-order q/k/v/out: video
+// query-tile height: 256 rows, or 128 with `small` (4-wave work groups, two
+// per CU).  rel != NULL selects canonical-order q/k/v/out: video
 // row r of window w is tensor row vrow0(w) + rel[offsets[w] + r] (the plan's
 // ids relative to the window's smallest id; items resolved to match).
-int attn_bf16_tile_m(int head_dim, bool gather);
-hipError_t launch_attn_bf16(int head_dim, const void *q, const void *k, const void *v,
+int attn_bf16_tile_m(bool small);
+hipError_t launch_attn_bf16(int head_dim, bool small, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out,
                             float *ws, const int32_t *rel, const ItemDesc *items, int n_items,
                             int n_heads, int text_len, float scale, hipStream_t s);
