@@ -137,7 +137,7 @@ def test_bf16_large_scores(gpu, std, sched):
     oracle; canonical-order I/O gives the same bits."""
     import torch
     w = I.custom(f"mid_large_{int(std)}", 6, 30, 52, 2, 3, 3, 2, 128, 40, "bf16", std=std,
-                 index=322 + int(std))
+                 index=340 + int(std))
     W.set_attn_schedule({"per_item": W.SCHED_PER_ITEM, "per_item_128": W.SCHED_PER_ITEM_128,
                          "persistent": W.SCHED_PERSISTENT}[sched])
     try:
