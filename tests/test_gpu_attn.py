@@ -242,10 +242,12 @@ def test_1080p_schedules_bit_identical(gpu, canonical):
 
 
 # ------------------------------------------------------------------ full-size, sampled
-def sampled_check(w, method, heads_full_text, n_samples=3, text_dtype=np.float64, q=None):
+def sampled_check(w, method, heads_full_text, n_samples=3, text_dtype=np.float64, q=None, canonical=False):
     """Run the whole layer of workload w on the GPU; compare sampled
     (window, head) video outputs and the complete text mean of the given
-    heads with the oracle computed window by window."""
+    heads with the oracle computed window by window.  canonical: q, k, v
+    and out stay in canonical token order (the layout permutation inside
+    the attention kernel)."""
     import torch
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
     om, wm = METH[method]
@@ -254,9 +256,13 @@ def sampled_check(w, method, heads_full_text, n_samples=3, text_dtype=np.float64
     log(f"  generating {w.name} inputs")
     inp = I.qkv(w, bits_only=True)
     d = upload(inp, "bf16")
-    qq, kk, vv = (W.relayout(d[n], wc, wp) for n in "qkv")
-    del d["q"], d["k"], d["v"]
-    out, txt = W.window_attn(wp, qq, kk, vv, d["txt_q"], d["txt_k"], d["txt_v"])
+    if canonical:
+        out, txt = W.window_attn(wp, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"],
+                                 canonical=True)
+    else:
+        qq, kk, vv = (W.relayout(d[n], wc, wp) for n in "qkv")
+        del d["q"], d["k"], d["v"]
+        out, txt = W.window_attn(wp, qq, kk, vv, d["txt_q"], d["txt_k"], d["txt_v"])
     torch.cuda.synchronize()
     bits = {n: inp[n][1] for n in I.QKV_NAMES}
 
@@ -273,7 +279,9 @@ def sampled_check(w, method, heads_full_text, n_samples=3, text_dtype=np.float64
             ov, _ = O.joint_attention(rows("q", ids, h), rows("k", ids, h), rows("v", ids, h),
                                       rows("txt_q", slice(None), h), rows("txt_k", slice(None), h),
                                       rows("txt_v", slice(None), h))
-            check_bf16(from_dev(out[a:b, h]), ov, f"{w.name} {method} window {win} (L={b - a}) head {h}")
+            got = out[torch.from_numpy(ids.astype(np.int64)).cuda(), h] if canonical else out[a:b, h]
+            check_bf16(from_dev(got), ov, f"{w.name} {method} window {win} (L={b - a}) head {h}"
+                       + (" canonical I/O" if canonical else ""))
     for h in heads_full_text:
         acc = np.zeros((w.text_len, w.head_dim), dtype=text_dtype)
         tq, tk, tv = (rows(n, slice(None), h) for n in ("txt_q", "txt_k", "txt_v"))
@@ -301,6 +309,14 @@ def test_720p_shifted_sampled(gpu):
 @pytest.mark.parametrize("method", ["regular", "shifted"])
 def test_1080p_sampled(gpu, method):
     sampled_check(I.WORKLOADS["1080p_bf16"], method, heads_full_text=[7])
+
+
+@pytest.mark.parametrize("method", ["regular", "shifted"])
+def test_1080p_canonical_io_sampled(gpu, method):
+    """The launch the benchmark times: the full 1080p layer with q, k, v and
+    out in canonical token order, against the oracle on sampled windows and
+    the complete text mean of one head."""
+    sampled_check(I.WORKLOADS["1080p_bf16"], method, heads_full_text=[12], canonical=True)
 
 
 @pytest.mark.timeout(900)
