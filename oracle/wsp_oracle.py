@@ -86,10 +86,11 @@ def window_size(T: int, H: int, W: int, nt: int, nh: int, nw: int):
 def axis_intervals(n: int, w: int, method: int):
     """Half-open intervals [a, b) that cut one axis of length n.
 
-    [WSP] "Window layouts": the regular method takes slice(i*w, min((i+1)*w, n));
-    the shifted method moves every cut by half a window and clips it to the
-    axis with max(.., 0) / min(.., n).  It is not a cyclic roll: no interval
-    wraps around.  Empty intervals are not produced.
+    [WSP] "Window layouts": regular cuts sit at the multiples of w, the last
+    interval ending at n.  Shifted cuts sit half a window earlier, and each
+    interval is clamped to [0, n], so the first and last ones are shorter;
+    nothing wraps from one end of the axis to the other (unlike a cyclic
+    roll).  Empty intervals are not produced.
     """
     if method == REGULAR:
         s = 0
@@ -145,9 +146,10 @@ class Plan:
 def plan(T: int, H: int, W: int, nt: int, nh: int, nw: int, method: int) -> Plan:
     """Window tables of one layout.
 
-    [WSP] "Window layouts": windows are enumerated with the w axis outermost
-    and the t axis innermost; inside a window tokens are row-major in
-    (t, h, w); the canonical id of token (t, h, w) is (t*H + h)*W + w.
+    [WSP] "Window layouts": window ids count the w intervals in the outer
+    loop and the t intervals in the inner loop; a window lists its tokens
+    with t varying slowest and w fastest; token (t, h, w) has canonical id
+    (t*H + h)*W + w.
     [WSP] "Planner": the largest-first order sorts windows by
     (-video_token_count, original_window_id).
     """
@@ -214,8 +216,8 @@ def relayout(x: np.ndarray, src: Plan, dst: Plan) -> np.ndarray:
 # layer schedule
 # ---------------------------------------------------------------------------
 def layer_schedule(num_layers: int):
-    """[WSP] "Motivation": regular and shifted layouts alternate at every
-    layer, starting with the regular one."""
+    """[WSP] "Motivation": consecutive layers switch between the regular and
+    the shifted layout; layer 0 is regular."""
     return [REGULAR if l % 2 == 0 else SHIFTED for l in range(num_layers)]
 
 

@@ -6,11 +6,11 @@ it and shares no code or table with it.  float64 throughout.
 
 Source: "Window-Aligned Sequence Parallelism (SeedVR2)", section "Reference
 quirks reproduced on purpose":
-  * RoPE positions are window-local: a video token at window-local offset
-    (dt, dh, dw) inside its window uses the axial indices
-    (text_len + dt, dh, dw); every window restarts at 0;
-  * the rotary span is 3 * (rope_dim // 3) channels (126 of 128 for a head
-    dim of 128); the remaining channels pass through unrotated.
+  * positions count from each window's own corner: a video token whose
+    offset from that corner is (dt, dh, dw) is rotated as if it sat at
+    (text_len + dt, dh, dw), so two windows use the same indices;
+  * only 3 * (head_dim // 3) channels are rotated (126 for a 128-wide head),
+    and the channels beyond that width are copied unchanged.
 
 Readings where the page is silent (listed in the design notes; parity
 unpinned for these three, every other step is pinned by

@@ -1,15 +1,21 @@
 """Pins of the RoPE oracle (oracle/wsp_rope.py) against what the page fixes
 and what rotations must satisfy, independent of the oracle's own formulas.
 
-Page-fixed ("Window-Aligned Sequence Parallelism (SeedVR2)", section
-"Reference quirks reproduced on purpose"): window-local axial indices
-(text_len + dt, dh, dw) restarting in every window; 3 * (rope_dim // 3)
-rotated channels, the rest passed through.  Mathematical invariants of any
+Fixed by the page ("Window-Aligned Sequence Parallelism (SeedVR2)", section
+"Reference quirks reproduced on purpose"): a video token's rotary indices
+are its offsets from its own window's corner, with the temporal one moved up
+by the text length; the rotated width is the largest multiple of three not
+above the head dimension, and the leftover channels are copied.  Mathematical invariants of any
 axial rotary embedding: identity at position 0, norm preservation,
 composition of rotations, dependence of q.k on the position difference only,
-axis separation.  Parity unpinned: the frequency base, the adjacent-pair
-layout and the text positions (readings R1-R3 of the oracle).
+axis separation.  The readings on the frequency base, the adjacent-pair
+layout and the text positions (R1-R3 of the oracle) are pinned to their
+stated form by hand-derived angles in tests/golden/rope_angles.json; the page
+itself does not fix them.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -23,7 +29,7 @@ def rng(seed):
 
 
 def test_span_and_axis_block():
-    assert O.rope_span(128) == 126          # "126 of 128 channels for the 3B"
+    assert O.rope_span(128) == 126          # 3 * (128 // 3): two channels are left unrotated
     assert O.rope_axis_dim(128) == 42
     with pytest.raises(ValueError):
         O.rope_axis_dim(64)                 # 3 * 21 = 63: axis blocks of 21 cannot pair
@@ -109,3 +115,57 @@ def test_rope_relayout_matches_rotation_after_move():
     # moving between layouts does not change a token's rotation, only its row
     y2 = O.rope_relayout(x, c, s, r, Lt)
     assert np.allclose(O.relayout(y2, s, r), y)
+
+
+# ---------------------------------------------------------------- hand-derived goldens
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "rope_angles.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def check_pairs(axial, pairs):
+    """Rotate unit vectors through O.rope at the given axial indices and
+    compare every listed pair with the hand-derived (cos, sin); every other
+    channel of a one-hot input must stay where it is."""
+    pos = np.asarray([axial], dtype=np.int64)
+    ang = O.rope_angles(pos, D)[0]
+    for p in pairs:
+        c0, c1 = p["channels"]
+        assert abs(ang[c0 // 2] - p["angle"]) <= 1e-12 * max(1.0, abs(p["angle"])), p
+        for src, want in ((c0, (p["cos"], p["sin"])), (c1, (-p["sin"], p["cos"]))):
+            x = np.zeros((1, 1, D))
+            x[0, 0, src] = 1.0
+            y = O.rope(x, pos)[0, 0]
+            assert abs(y[c0] - want[0]) <= 1e-12 and abs(y[c1] - want[1]) <= 1e-12, (p, src, y[c0], y[c1])
+            others = np.delete(y, [c0, c1])
+            assert np.all(others == 0.0)
+
+
+@pytest.mark.parametrize("case", golden()["cases"], ids=lambda c: c["name"])
+def test_rope_angles_match_hand_derivation(case):
+    """Pins the readings on the frequency base and exponent (10000^(-2i/42)),
+    the block order [t | h | w] with adjacent pairs, and the rotation
+    direction: a wrong exponent, interleaved axes, half-split pairs or the
+    opposite sign each move at least one listed value."""
+    check_pairs(case["axial"], case["pairs"])
+
+
+def test_rope_text_positions_match_hand_derivation():
+    """Text token i sits at (i, i, i) (reading on text positions)."""
+    case = [c for c in golden()["cases"] if c["name"] == "text token 5"][0]
+    assert tuple(O.text_positions(6)[5]) == tuple(case["axial"])
+    check_pairs(O.text_positions(6)[5], case["pairs"])
+
+
+@pytest.mark.parametrize("entry", golden()["window_positions"], ids=lambda e: e["method"])
+def test_window_positions_and_angles_match_hand_derivation(entry):
+    T, H, W = entry["grid"]
+    p = O.plan(T, H, W, *entry["n"], O.SHIFTED if entry["method"] == "shifted" else O.REGULAR)
+    t, h, w = entry["token"]
+    cid = (t * H + h) * W + w
+    assert cid == entry["canonical_id"]
+    assert tuple(O.window_positions(p, entry["text_len"])[cid]) == tuple(entry["axial"])
+    check_pairs(entry["axial"], entry["pairs"])
