@@ -55,16 +55,19 @@ def linear(x, w, r=None) -> np.ndarray:
     return bf16_round(y)
 
 
-def stack_forward(x_vid, x_txt, geo, weights, heads: int, head_dim: int, scale=None):
+def stack_forward(x_vid, x_txt, geo, weights, heads: int, head_dim: int, scale=None, first_layer: int = 0):
     """One pass of the stack.
 
     x_vid: [N, E] video hidden state in canonical token order, x_txt: [Lt, E]
     text hidden state (both bfloat16 values held in float64); geo = (T, H, W,
     nt, nh, nw); weights: one (Wq, Wk, Wv, Wo) tuple per layer, each [E, E].
+    first_layer: schedule index of weights[0] (the layers run are
+    first_layer .. first_layer + len(weights) - 1 of the alternating
+    schedule, so a pass can be resumed from any layer's state).
     Returns the video state back in canonical order and the text state."""
     T, H, W = geo[:3]
     n_layers = len(weights)
-    layouts = [plan(*geo, m) for m in layer_schedule(n_layers)]
+    layouts = [plan(*geo, m) for m in layer_schedule(first_layer + n_layers)[first_layer:]]
     canon = canonical_plan(T, H, W)
     N, E = x_vid.shape
     Lt = x_txt.shape[0]

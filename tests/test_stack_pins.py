@@ -91,3 +91,26 @@ def test_uniform_attention_gives_window_means(n_layers):
         te = O.bf16_round(te + O.bf16_round(np.broadcast_to(means.mean(axis=0), te.shape)))
     np.testing.assert_allclose(xo, xe, rtol=0, atol=1e-12)
     np.testing.assert_allclose(to, te, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("first_layer", [1, 2, 5])
+def test_resumed_layer_uses_its_schedule_layout(first_layer):
+    """first_layer resumes the schedule: one layer at index l runs in the
+    regular layout for even l and the shifted one for odd l (window means of
+    the closed-form membership, as above), and layers 0..2 in one pass equal
+    layer 0 followed by a pass resumed at layer 1."""
+    x, t = inputs(6)
+    z, eye = np.zeros((E, E)), np.eye(E)
+    xo, to = O.stack_forward(x, t, GEO, [(z, z, eye, eye)], HEADS, HD, first_layer=first_layer)
+    method = O.REGULAR if first_layer % 2 == 0 else O.SHIFTED
+    _, win, nwin = membership(*GEO, method)
+    means = np.stack([np.concatenate([x[win == wi], t], axis=0).mean(axis=0) for wi in range(nwin)])
+    np.testing.assert_allclose(xo, O.bf16_round(x + O.bf16_round(means[win])), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(to, O.bf16_round(t + O.bf16_round(np.broadcast_to(means.mean(axis=0), t.shape))),
+                               rtol=0, atol=1e-12)
+    rng = np.random.default_rng(8)
+    w = [tuple(O.bf16_round(rng.standard_normal((E, E)) * 0.05) for _ in range(4)) for _ in range(3)]
+    full = O.stack_forward(x, t, GEO, w, HEADS, HD)
+    x1, t1 = O.stack_forward(x, t, GEO, w[:1], HEADS, HD)
+    rest = O.stack_forward(x1, t1, GEO, w[1:], HEADS, HD, first_layer=1)
+    assert np.array_equal(full[0], rest[0]) and np.array_equal(full[1], rest[1])
