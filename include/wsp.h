@@ -67,10 +67,10 @@ enum wsp_order {
     WSP_ORDER_ID = 2       /* window id order                                    */
 };
 
-/* Schedule of the bf16 attention kernel (wsp_set_attn_schedule). */
+/* Schedule of the bf16 attention kernel (wsp_set_attn_schedule).  Value 1
+ * (a persistent schedule of earlier versions) is no longer accepted. */
 enum wsp_schedule {
     WSP_SCHED_AUTO = 0,         /* by mean window length (wsp_set_attn_schedule) */
-    WSP_SCHED_PERSISTENT = 1,   /* resident work groups walk per-CU item lists   */
     WSP_SCHED_PER_ITEM = 2,     /* one work group per 256-query-row item         */
     WSP_SCHED_PER_ITEM_128 = 3  /* one work group per 128-query-row item         */
 };
@@ -83,9 +83,10 @@ enum wsp_schedule {
  *   wh = ceil(round(H*scale) / nh), ww = ceil(round(W*scale) / nw) with
  *   round() ties-to-even; wt = ceil(min(T, 30) / nt).  Regular cuts at
  *   multiples of the window; shifted cuts at k*w - floor(w/2), clipped to the
- *   axis (empty windows are not produced).  Windows are numbered with the w
- *   axis outermost and t innermost; tokens inside a window are row-major in
- *   (t, h, w); the canonical id of (t, h, w) is (t*H + h)*W + w.
+ *   axis (empty windows are not produced).  Window ids run over the w
+ *   intervals in the outer loop, then h, then t in the inner loop; a window's
+ *   tokens are listed with t slowest and w fastest; token (t, h, w) has the
+ *   canonical id (t*H + h)*W + w.
  *   Section "Planner": the largest-first order sorts windows by
  *   (-video token count, window id).
  *
@@ -144,8 +145,11 @@ int wsp_relayout(const void *x, void *y, int64_t row_bytes, const wsp_plan_t *sr
 
 /*
  * wsp_window_attn_workspace -- device workspace (bytes) wsp_window_attn needs:
- * n_windows * text_len * n_heads * head_dim * 4 (one float32 text output per
- * window, reduced in window order).  0 when text_len == 0.
+ * G * text_len * n_heads * head_dim * 4 with G = min(n_windows, 16): one
+ * float32 partial text sum per chunk of consecutive windows (the windows
+ * split into G runs of ids, run c starting at floor(c * n_windows / G)).
+ * 0 when text_len == 0.  1080p-shaped layer (20 x 128, 256 text tokens):
+ * 42 MB; 4K-shaped (512 text tokens): 84 MB.
  * Errors: WSP_EINVAL (bad plan/shape/dtype), WSP_ERANGE.
  */
 int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, int text_len,
@@ -167,8 +171,10 @@ int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, in
  *   Q = [q[a:b, h]; txt_q[:, h]],  K = [k[a:b, h]; txt_k[:, h]],
  *   V = [v[a:b, h]; txt_v[:, h]],  O = softmax(Q K^T * scale) V;
  *   out[a:b, h] = the first b-a rows of O; T_w = the last text_len rows.
- *   txt_out[:, h] = (sum_w T_w) / n_windows (float32 sum in window order,
- *   rounded once to dtype).
+ *   txt_out[:, h] = (sum_w T_w) / n_windows, summed in float32 in a fixed
+ *   order -- window order inside each of G = min(n_windows, 16) chunks of
+ *   consecutive windows, then the chunk sums in chunk order -- and rounded
+ *   once to dtype (bit-identical from run to run and across dispatch orders).
  *
  * p                 plan; q/k/v/out rows are in its layout
  * q, k, v           device, [n_tokens, n_heads, head_dim] of dtype
@@ -182,7 +188,10 @@ int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, in
  * txt_out           device, [text_len, n_heads, head_dim] of dtype (NULL
  *                   allowed when text_len == 0)
  * workspace         device, >= wsp_window_attn_workspace() bytes, 16-byte
- *                   aligned; contents on entry are ignored
+ *                   aligned; contents on entry are ignored; it holds the
+ *                   chunk sums until the text-mean kernel of the same call
+ *                   has read them (calls sharing a workspace must be ordered
+ *                   on one stream)
  * Errors: WSP_EINVAL (pointer NULL or not 16-byte aligned, unsupported
  * head_dim/dtype, n_heads out of range), WSP_ERANGE (a window longer than
  * the kernel's tile index range), WSP_EWORKSPACE, WSP_ENOMEM, WSP_EDEVICE.
@@ -229,10 +238,11 @@ int wsp_window_attn_ex(const wsp_plan_t *p, const void *q, const void *k, const 
  * the row move between two layouts (for q and k; v takes wsp_relayout).
  *
  * "Window-Aligned Sequence Parallelism (SeedVR2)", section "Reference quirks
- * reproduced on purpose": a video token at window-local offset (dt, dh, dw)
- * inside its window uses the axial indices (text_len + dt, dh, dw), and every
- * window restarts at 0; 3 * (rope_dim // 3) channels are rotated (126 of 128)
- * and the last two pass through.  Where the page is silent this library
+ * reproduced on purpose": a video token is rotated by its offset (dt, dh, dw)
+ * from the corner of its own window, the temporal index raised by text_len
+ * (tokens of different windows may share indices); the rotated width is
+ * 3 * (head_dim / 3) channels (126 for head_dim 128) and the rest are
+ * copied unchanged.  Where the page is silent this library
  * takes: three contiguous 42-channel axis blocks [t | h | w], each rotated in
  * adjacent pairs (2k, 2k+1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a),
  * pair i of a block turning by position * theta^(-2i/42).
@@ -327,16 +337,13 @@ int wsp_set_attn_order(int order);
 /*
  * wsp_set_attn_schedule -- process-wide schedule of the bf16 attention
  * kernel (enum wsp_schedule; default WSP_SCHED_AUTO).
- * WSP_SCHED_PERSISTENT: one resident work group per compute unit walks a
- * host-built list of (window, head, 256-query-row) items, fetching the next
- * item's first K/V tile and query rows while the current item finishes.
  * WSP_SCHED_PER_ITEM: one work group (8 wavefronts) per 256-query-row item.
  * WSP_SCHED_PER_ITEM_128: one work group (4 wavefronts, two per compute
  * unit) per 128-query-row item: less of a window's last query tile is
  * empty.  WSP_SCHED_AUTO: WSP_SCHED_PER_ITEM_128 when a window's joint
- * sequence averages fewer than 1024 rows, else WSP_SCHED_PER_ITEM.  All run
+ * sequence averages fewer than 1024 rows, else WSP_SCHED_PER_ITEM.  Both run
  * the same per-wavefront arithmetic in the same order, so results are
- * bit-identical; the order set by wsp_set_attn_order applies to all.
+ * bit-identical; the order set by wsp_set_attn_order applies to both.
  * Errors: WSP_EINVAL.
  */
 int wsp_set_attn_schedule(int schedule);
@@ -367,7 +374,7 @@ const char *wsp_last_error(void);
 /* wsp_version -- ABI version of this header (major*10000 + minor*100 + patch). */
 int wsp_version(void);
 
-#define WSP_VERSION 100
+#define WSP_VERSION 20000
 
 #ifdef __cplusplus
 }

@@ -123,9 +123,22 @@ def test_fp8_quantisation_error(gpu, std):
     assert rel <= 6e-2 and rel_t <= 6e-2
 
 
-def test_qk8_1080p_sampled(gpu):
-    """Full 1080p shifted layer on the fp8 path; sampled (window, head) pairs
-    against the oracle on the same codes."""
+def host_amax(bits, heads, rows_per_chunk=1 << 14):
+    """Per-head max |x| of a bf16 [rows, heads, D] tensor, from its bits on
+    the host (the oracle's amax over row chunks, then the max of those)."""
+    amax = np.zeros(heads)
+    for lo in range(0, bits.shape[0], rows_per_chunk):
+        amax = np.maximum(amax, O.fp8_amax(I.bf16_bits_to_f32(bits[lo:lo + rows_per_chunk])))
+    return amax
+
+
+@pytest.mark.parametrize("canonical", [False, True], ids=["layout_io", "canonical_io"])
+def test_qk8_1080p_sampled(gpu, canonical):
+    """Full 1080p shifted layer on the fp8 path.  The per-head amax of the
+    whole q and k (video and text rows) and the codes of the sampled rows are
+    computed on the host from the input bits and must equal the GPU's; the
+    sampled (window, head) outputs are compared with the oracle run on those
+    host codes."""
     import torch
     w = I.WORKLOADS["1080p_bf16"]
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
@@ -134,24 +147,40 @@ def test_qk8_1080p_sampled(gpu):
     inp = I.qkv(w, bits_only=True)
     d = {n: to_dev(None, b, "bf16") for n, (_, b) in inp.items()}
     aq, ak = W.fp8_amax(d["q"], d["txt_q"]), W.fp8_amax(d["k"], d["txt_k"])
-    q8 = W.relayout(W.fp8_quantize(d["q"], aq), wc, wp)
-    k8 = W.relayout(W.fp8_quantize(d["k"], ak), wc, wp)
+    q8c, k8c = W.fp8_quantize(d["q"], aq), W.fp8_quantize(d["k"], ak)
     tq8, tk8 = W.fp8_quantize(d["txt_q"], aq), W.fp8_quantize(d["txt_k"], ak)
-    v = W.relayout(d["v"], wc, wp)
-    out, _ = W.window_attn_qk8(wp, q8, k8, v, tq8, tk8, d["txt_v"], aq, ak)
+    if canonical:
+        out, _ = W.window_attn_qk8(wp, q8c, k8c, d["v"], tq8, tk8, d["txt_v"], aq, ak, canonical=True)
+    else:
+        v = W.relayout(d["v"], wc, wp)
+        out_l, _ = W.window_attn_qk8(wp, W.relayout(q8c, wc, wp), W.relayout(k8c, wc, wp), v, tq8, tk8,
+                                     d["txt_v"], aq, ak)
+        out = W.relayout(out_l, wp, wc)
     torch.cuda.synchronize()
-    raq, rak = aq.cpu().numpy(), ak.cpu().numpy()
     bits = {n: inp[n][1] for n in I.QKV_NAMES}
-    cq, ck = codes(q8), codes(k8)                      # layout order; checked bit-exact at mid sizes
+    log("  host amax of q and k (171360 + 256 rows each)")
+    raq = np.maximum(host_amax(bits["q"], w.heads), host_amax(bits["txt_q"], w.heads)).astype(np.float32)
+    rak = np.maximum(host_amax(bits["k"], w.heads), host_amax(bits["txt_k"], w.heads)).astype(np.float32)
+    assert np.array_equal(aq.cpu().numpy(), raq), "per-head amax of q differs from the host's"
+    assert np.array_equal(ak.cpu().numpy(), rak), "per-head amax of k differs from the host's"
+    gq, gk = codes(q8c), codes(k8c)                    # canonical row order
     for win in sorted({int(op.lpt[0]), int(op.lpt[len(op.lpt) // 2]), int(op.lpt[-1])}):
         a, b = int(op.offsets[win]), int(op.offsets[win + 1])
-        for h in (0, w.heads - 1):
-            deq = lambda c, am, hh=h: O.e4m3_decode(c) * (am[hh] / 448.0)
-            tq = O.fp8_quantize(I.bf16_bits_to_f32(bits["txt_q"][:, h:h + 1]), raq[h:h + 1])[:, 0]
-            tk = O.fp8_quantize(I.bf16_bits_to_f32(bits["txt_k"][:, h:h + 1]), rak[h:h + 1])[:, 0]
-            ids = op.ids[a:b]
-            ov, _ = O.joint_attention(deq(cq[a:b, h], raq), deq(ck[a:b, h], rak),
-                                      I.bf16_bits_to_f32(bits["v"][ids, h]).astype(np.float64),
-                                      deq(tq, raq), deq(tk, rak),
-                                      I.bf16_bits_to_f32(bits["txt_v"][:, h]).astype(np.float64))
-            check_bf16(from_dev(out[a:b, h]), ov, f"1080p fp8 window {win} head {h}")
+        ids = op.ids[a:b]
+        for h in (0, 7, w.heads - 1):
+            f32 = lambda n, rows, hh=h: I.bf16_bits_to_f32(bits[n][rows, hh:hh + 1])
+            cq = O.fp8_quantize(f32("q", ids), raq[h:h + 1])
+            ck = O.fp8_quantize(f32("k", ids), rak[h:h + 1])
+            assert np.array_equal(gq[ids, h:h + 1], cq), f"q codes of window {win} head {h}"
+            assert np.array_equal(gk[ids, h:h + 1], ck), f"k codes of window {win} head {h}"
+            tq = O.fp8_quantize(f32("txt_q", slice(None)), raq[h:h + 1])
+            tk = O.fp8_quantize(f32("txt_k", slice(None)), rak[h:h + 1])
+            assert np.array_equal(codes(tq8)[:, h:h + 1], tq) and np.array_equal(codes(tk8)[:, h:h + 1], tk)
+            deq = lambda c, am: O.fp8_dequantize(c, am)[:, 0]
+            ov, _ = O.joint_attention(deq(cq, raq[h:h + 1]), deq(ck, rak[h:h + 1]),
+                                      f32("v", ids)[:, 0].astype(np.float64),
+                                      deq(tq, raq[h:h + 1]), deq(tk, rak[h:h + 1]),
+                                      f32("txt_v", slice(None))[:, 0].astype(np.float64))
+            got = out[torch.from_numpy(ids.astype(np.int64)).cuda(), h]
+            check_bf16(from_dev(got), ov, f"1080p fp8 window {win} head {h}"
+                       + (" canonical I/O" if canonical else ""))

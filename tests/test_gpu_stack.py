@@ -5,11 +5,15 @@ wsp_linear is compared element by element with the float64 product rounded
 once to bfloat16: at most one bfloat16 ulp apart plus the float32
 accumulation error bound K * 2^-24 * sum|x w| (float32 accumulation can move
 a result across a rounding tie, or matter near zero), on ragged row counts,
-with and without a residual, in place.  The stack runs a few alternating
-layers on the tiny grid in full against the oracle (both the explicit
-permutations and canonical-order I/O, which must agree bit for bit), and one
-layer of the full 1080p, 2560-wide configuration on the largest window's
-rows.
+with and without a residual, in place.  The stack runs 1, 3 and all 32 alternating
+layers (31 layout transitions, a text mean per layer) on the tiny grid and
+32 layers on a mid grid in full against the oracle, with the explicit
+permutations and canonical-order I/O agreeing bit for bit; at 32 layers
+every layer is also checked from the GPU's own state before it (so rounding
+differences of earlier layers do not compound into the comparison), and the
+end state against the oracle run from the input.  At the full 1080p,
+2560-wide configuration one layer is checked on the largest window's rows
+and the second (shifted) layer on the largest shifted window's rows.
 """
 import numpy as np
 import pytest
@@ -129,6 +133,85 @@ def test_stack_tiny(gpu, n_layers):
         check_update(from_dev(got), ref, inp, f"stack {n_layers} layers {what} update")
 
 
+STACK32 = [  # (name, geometry, heads, head_dim, text_len, weight std, seed)
+    ("tiny", GEO, HEADS, HD, LT, 0.03, 60),
+    ("mid", (6, 30, 52, 2, 3, 3), 2, 128, 40, 0.03, 70),
+]
+
+
+def oracle_layer_attention(xi, ti, geo, wl, heads, hd, layer):
+    """Attention output of one stack layer computed by the oracle from the
+    stream state (xi canonical order, ti text rows): q/k/v projections,
+    window attention in the layer's layout and the text mean, returned with
+    the video rows in canonical order."""
+    N, E = xi.shape
+    lt = ti.shape[0]
+    lay = O.plan(*geo, O.REGULAR if layer % 2 == 0 else O.SHIFTED)
+    can = O.canonical_plan(*geo[:3])
+    X = np.concatenate([O.relayout(xi, can, lay), ti], axis=0)
+    q, k, v = (O.linear(X, wm) for wm in wl[:3])
+    split = lambda a: (a[:N].reshape(N, heads, hd), a[N:].reshape(lt, heads, hd))
+    (qv, qt), (kv, kt), (vv, vt) = split(q), split(k), split(v)
+    out, mean = O.window_attn(lay, qv, kv, vv, qt, kt, vt)
+    return O.relayout(out.reshape(N, E), lay, can), mean.reshape(lt, E)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", STACK32, ids=[c[0] for c in STACK32])
+def test_stack_32_layers(gpu, case):
+    """The 32-layer alternating stack (layer 0 regular, 31 transitions).
+    Weight std 0.03 at width 256 keeps the stream bounded over 32 layers (the
+    tiny tests' 0.06 makes it grow ~200-fold, where float32 and float64
+    arithmetic part ways whatever the implementation).  Every layer is
+    checked from the GPU's own state before it: its attention output (video
+    rows and text mean) at the attention bar, and the stream after its
+    residual update.  A layer's update is then only a few bf16 steps of the
+    stream, too fine to compare as a difference of two rounded streams, so the
+    attention output stands in for it (the projection with its residual add
+    is checked on its own by test_linear_residual)."""
+    import torch
+    name, geo, heads, hd, lt, wstd, seed = case
+    E, N = heads * hd, geo[0] * geo[1] * geo[2]
+    rng = np.random.default_rng(seed)
+    x, t = O.bf16_round(rng.standard_normal((N, E))), O.bf16_round(rng.standard_normal((lt, E)))
+    weights = [tuple(O.bf16_round(rng.standard_normal((E, E)) * wstd) for _ in range(4)) for _ in range(32)]
+    dw = [tuple(bf16_dev(a) for a in wl) for wl in weights]
+    dx, dt = bf16_dev(x), bf16_dev(t)
+    # GPU state after every prefix of layers and the last layer's attention
+    # output, canonical-order I/O
+    states, attn = [(x, t)], []
+    for n in range(1, 33):
+        st = Stack(*geo, n, heads, hd, lt, canonical_io=True)
+        xo, to = st.forward(dx, dt, dw[:n])
+        torch.cuda.synchronize()
+        states.append((from_dev(xo), from_dev(to)))
+        attn.append(from_dev(st.A))
+    # the whole pass with explicit permutations: same bits
+    xe, te = Stack(*geo, 32, heads, hd, lt, canonical_io=False).forward(dx, dt, dw)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(xe), states[32][0]), "video state: I/O orders differ"
+    assert np.array_equal(from_dev(te), states[32][1]), "text state: I/O orders differ"
+    log(f"  {name}: every layer from the GPU's own state before it")
+    for l in range(32):
+        (xi, ti), (xg, tg) = states[l], states[l + 1]
+        ra, rm = oracle_layer_attention(xi, ti, geo, weights[l], heads, hd, l)
+        check_bf16(attn[l][:N], ra, f"{name} layer {l} attention, video rows")
+        check_bf16(attn[l][N:], rm, f"{name} layer {l} text mean")
+        rx, rt = O.stack_forward(xi, ti, geo, weights[l:l + 1], heads, hd, first_layer=l)
+        check_bf16(xg, rx, f"{name} layer {l} video state")
+        check_bf16(tg, rt, f"{name} layer {l} text state")
+    # End to end, 32 roundings of the stream apart: the relative L2 part of
+    # the bf16 bar (the element bar is applied per layer above, where one
+    # layer's arithmetic is compared; over 32 layers single elements drift by
+    # rounding-boundary crossings that compound).
+    rx, rt = O.stack_forward(x, t, geo, weights, heads, hd)
+    for got, ref, what in ((states[32][0], rx, "video"), (states[32][1], rt, "text")):
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        ratio = float(np.max(np.abs(got - ref) / (3e-2 + 2e-2 * np.abs(ref))))
+        log(f"  {name} 32 layers {what} from the input: rel-L2 {rel:.3e} (bar 2e-2), element ratio {ratio:.3f}")
+        assert np.isfinite(got).all() and rel <= 2e-2, f"{name} 32 layers {what}: relative L2 error {rel}"
+
+
 def test_stack_1080p_one_layer_sampled(gpu):
     """One layer of the 1080p, 20 x 128, 256-text-token configuration: the
     video rows of the largest window (all heads, all 2560 features) against
@@ -159,3 +242,48 @@ def test_stack_1080p_one_layer_sampled(gpu):
     got = from_dev(xo[torch.from_numpy(ids.astype(np.int64)).cuda()])
     check_bf16(got, ref, f"1080p stack layer, window {win}")
     check_update(got, ref, x[ids], f"1080p stack layer update, window {win}")
+
+
+def test_stack_1080p_two_layers_sampled(gpu):
+    """Two layers of the 1080p, 20 x 128, 256-text-token configuration with
+    canonical-order I/O (the benchmark's stack): the second, shifted layer on
+    the rows of the largest shifted window, computed by the oracle from the
+    GPU's state after the first layer (video rows of that window and the text
+    rows), and the first layer on the largest regular window's rows."""
+    import torch
+    w = I.WORKLOADS["1080p_bf16"]
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    E, Lt, N = w.heads * w.head_dim, w.text_len, w.n_tokens
+    rng = np.random.default_rng(78)
+    log("  generating 1080p stack inputs")
+    x = O.bf16_round(rng.standard_normal((N, E), dtype=np.float32))
+    t = O.bf16_round(rng.standard_normal((Lt, E), dtype=np.float32))
+    wts = [[O.bf16_round(rng.standard_normal((E, E), dtype=np.float32) * 0.02) for _ in range(4)] for _ in range(2)]
+    dw = [tuple(bf16_dev(a) for a in wl) for wl in wts]
+    dx, dt = bf16_dev(x), bf16_dev(t)
+    x1, t1 = Stack(*geo, 1, w.heads, w.head_dim, Lt, canonical_io=True).forward(dx, dt, dw[:1])
+    x2, _ = Stack(*geo, 2, w.heads, w.head_dim, Lt, canonical_io=True).forward(dx, dt, dw)
+    torch.cuda.synchronize()
+    host_t1 = from_dev(t1)
+
+    def oracle_window(xin, tin, ws, method):
+        op = O.plan(*geo, method)
+        win = int(op.lpt[0])
+        ids = op.ids[op.offsets[win]:op.offsets[win + 1]]
+        X = np.concatenate([xin(ids), tin], axis=0)
+        q, k, v = (O.linear(X, wm).reshape(-1, w.heads, w.head_dim) for wm in ws[:3])
+        L = len(ids)
+        out = np.empty((L, w.heads, w.head_dim))
+        for h in range(w.heads):
+            out[:, h], _ = O.joint_attention(q[:L, h], k[:L, h], v[:L, h], q[L:, h], k[L:, h], v[L:, h])
+        return win, ids, O.linear(O.bf16_round(out).reshape(L, E), ws[3], r=xin(ids))
+
+    rows = lambda dev: (lambda ids: from_dev(dev[torch.from_numpy(ids.astype(np.int64)).cuda()]))
+    win, ids, ref = oracle_window(lambda i: x[i], t, wts[0], O.REGULAR)
+    got = rows(x1)(ids)
+    check_bf16(got, ref, f"1080p stack layer 0, regular window {win}")
+    check_update(got, ref, x[ids], f"1080p stack layer 0 update, regular window {win}")
+    win, ids, ref = oracle_window(rows(x1), host_t1, wts[1], O.SHIFTED)
+    got = rows(x2)(ids)
+    check_bf16(got, ref, f"1080p stack layer 1, shifted window {win}")
+    check_update(got, ref, rows(x1)(ids), f"1080p stack layer 1 update, shifted window {win}")

@@ -29,7 +29,8 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(W.LIB_PATH)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
-    assert W.version() == 100
+    header = open(os.path.join(ROOT, "include", "wsp.h")).read()
+    assert W.version() == int(re.search(r"#define WSP_VERSION (\d+)", header).group(1))
 
 
 def compare(geo, method):
@@ -151,7 +152,9 @@ def test_window_attn_argument_errors():
                                     ctypes.c_float(0), flags, o, None, None, 0, None) == -2
         assert b"2 GiB" in L.wsp_last_error()
     need = W.window_attn_workspace(p, 4, 64, 16, W.F32)
-    assert need == p.n_windows * 16 * 4 * 64 * 4
+    assert need == min(p.n_windows, 16) * 16 * 4 * 64 * 4      # one float32 partial per chunk
+    big = W.Plan(21, 68, 120, 4, 3, 3, W.REGULAR)                 # 100 windows: 16 chunks
+    assert W.window_attn_workspace(big, 20, 128, 256, W.BF16) == 16 * 256 * 20 * 128 * 4
     assert W.window_attn_workspace(p, 4, 64, 0, W.BF16) == 0
 
 
@@ -184,7 +187,8 @@ def test_attn_schedule_option():
     L = raw()
     assert L.wsp_set_attn_schedule(4) == -1
     assert L.wsp_set_attn_schedule(-1) == -1
-    for sc in (W.SCHED_PER_ITEM, W.SCHED_PER_ITEM_128, W.SCHED_PERSISTENT, W.SCHED_AUTO):
+    assert L.wsp_set_attn_schedule(1) == -1      # the removed persistent schedule
+    for sc in (W.SCHED_PER_ITEM, W.SCHED_PER_ITEM_128, W.SCHED_AUTO):
         W.set_attn_schedule(sc)
 
 

@@ -19,7 +19,7 @@ REGULAR, SHIFTED, CANONICAL = 0, 1, 2
 IO_LAYOUT, IO_CANONICAL = 0, 1
 F32, BF16 = 0, 1
 ORDER_LPT_XCD, ORDER_LPT, ORDER_ID = 0, 1, 2
-SCHED_AUTO, SCHED_PERSISTENT, SCHED_PER_ITEM, SCHED_PER_ITEM_128 = 0, 1, 2, 3
+SCHED_AUTO, SCHED_PER_ITEM, SCHED_PER_ITEM_128 = 0, 2, 3
 METHODS = {"regular": REGULAR, "shifted": SHIFTED, "canonical": CANONICAL}
 
 _c_int, _c_i64, _c_sz, _c_vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -143,6 +143,20 @@ def _stream(stream):
     return _c_vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _on(stream):
+    """Context in which torch allocates for work enqueued on `stream`: the
+    caching allocator then hands a freed block to another allocation only
+    after the work queued on that stream (a workspace dropped on return may
+    still be in use by the kernels just enqueued there)."""
+    import contextlib
+    torch = _torch()
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
+
+
 def _dev_ptr(t, name):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor (the library has no CPU path)")
@@ -164,7 +178,8 @@ def relayout(x, src: Plan, dst: Plan, out=None, stream=None):
     """y[j] = x[rows of src holding dst's token j] (whole rows, bytes unchanged)."""
     torch = _torch()
     if out is None:
-        out = torch.empty_like(x)
+        with _on(stream):
+            out = torch.empty_like(x)
     row_bytes = x[0].numel() * x.element_size() if x.shape[0] else 0
     if x.shape[0] != src.n_tokens or out.shape != x.shape or out.dtype != x.dtype:
         raise ValueError("x/out shape does not match the plans")
@@ -182,7 +197,8 @@ def linear(x, w, residual=None, out=None, stream=None):
     M, K = x.shape
     N = w.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+        with _on(stream):
+            out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     if tuple(out.shape) != (M, N) or out.dtype != x.dtype or w.dtype != x.dtype:
         raise ValueError("out must be [M, N] with the dtype of x and w")
     if residual is not None and (tuple(residual.shape) != (M, N) or residual.dtype != x.dtype):
@@ -219,13 +235,14 @@ def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None, out=None, txt
             raise ValueError(f"{name} must match txt_q in shape and q in dtype")
     if txt_q.shape[1:] != (Hh, D) or N != p.n_tokens:
         raise ValueError("shapes do not match the plan / each other")
-    if out is None:
-        out = torch.empty_like(q)
-    if txt_out is None:
-        txt_out = torch.empty_like(txt_q)
     need = window_attn_workspace(p, Hh, D, Lt, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if txt_out is None:
+            txt_out = torch.empty_like(txt_q)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     tp = [(_dev_ptr(t, n) if Lt else _c_vp(0)) for n, t in
           (("txt_q", txt_q), ("txt_k", txt_k), ("txt_v", txt_v), ("txt_out", txt_out))]
@@ -243,7 +260,8 @@ def rope_relayout(x, src: Plan, dst: Plan, pos: Plan, text_len, theta=None, out=
     layout pos (wsp_rope_relayout)."""
     torch = _torch()
     if out is None:
-        out = torch.empty_like(x)
+        with _on(stream):
+            out = torch.empty_like(x)
     if x.shape[0] != src.n_tokens or out.shape != x.shape or out.dtype != x.dtype or x.dim() != 3:
         raise ValueError("x/out shape does not match the plans")
     _check("wsp_rope_relayout", lib().wsp_rope_relayout(
@@ -257,7 +275,8 @@ def rope_text(x, theta=None, out=None, stream=None):
     """Text rows x [Lt, H, 128] rotated by the axial indices (i, i, i) (wsp_rope_text)."""
     torch = _torch()
     if out is None:
-        out = torch.empty_like(x)
+        with _on(stream):
+            out = torch.empty_like(x)
     if out.shape != x.shape or out.dtype != x.dtype or x.dim() != 3:
         raise ValueError("x/out shapes differ")
     if x.shape[0] == 0:
@@ -273,7 +292,8 @@ def fp8_amax(*tensors, amax=None, stream=None):
     torch = _torch()
     H = tensors[0].shape[1]
     if amax is None:
-        amax = torch.zeros(H, dtype=torch.float32, device=tensors[0].device)
+        with _on(stream):  # the zero fill runs on the stream the kernels use
+            amax = torch.zeros(H, dtype=torch.float32, device=tensors[0].device)
     for t in tensors:
         if t.dim() != 3 or t.shape[1] != H:
             raise ValueError("tensors must be [rows, heads, dim] with one head count")
@@ -288,7 +308,8 @@ def fp8_quantize(x, amax, out=None, stream=None):
     """E4M3 codes (torch.uint8, same shape) of x * 448/amax[head] (wsp_fp8_quantize)."""
     torch = _torch()
     if out is None:
-        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        with _on(stream):
+            out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if x.shape[0]:
         _check("wsp_fp8_quantize", lib().wsp_fp8_quantize(
             _dev_ptr(x, "x"), _dev_ptr(out, "out"), x.shape[0], x.shape[1], x.shape[2], _dtype_code(x.dtype),
@@ -306,13 +327,14 @@ def window_attn_qk8(p: Plan, q8, k8, v, txt_q8, txt_k8, txt_v, amax_q, amax_k, s
         raise ValueError("q8 / k8 must be uint8 codes shaped like v")
     if v.dtype != torch.bfloat16 or txt_v.dtype != torch.bfloat16:
         raise ValueError("v and txt_v must be bfloat16")
-    if out is None:
-        out = torch.empty_like(v)
-    if txt_out is None:
-        txt_out = torch.empty_like(txt_v)
     need = window_attn_workspace(p, Hh, D, Lt, BF16)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=v.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(v)
+        if txt_out is None:
+            txt_out = torch.empty_like(txt_v)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=v.device)
     tp = [(_dev_ptr(t, n) if Lt else _c_vp(0)) for n, t in
           (("txt_q8", txt_q8), ("txt_k8", txt_k8), ("txt_v", txt_v), ("txt_out", txt_out))]
     _check("wsp_window_attn_qk8", lib().wsp_window_attn_qk8(

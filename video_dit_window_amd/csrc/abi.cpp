@@ -1,6 +1,7 @@
 // C entry points of libwsp: argument validation, per-device table caches and
 // kernel dispatch.  See include/wsp.h for the contract of each call.
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -142,9 +143,27 @@ int device_rel_ids(wsp_plan_t &p, int dev, int32_t **out) {
     return WSP_OK;
 }
 
-int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
-                 int n_groups, Item **out, int *count) {
-    const auto key = std::make_tuple(n_heads, text_len, bm, order, n_groups);
+int device_windows(wsp_plan_t &p, int dev, bool gather, WinDesc **out) {
+    std::lock_guard<std::mutex> lk(p.mu);
+    DeviceTables &t = p.dev[dev];
+    WinDesc *&d = t.wins[gather ? 1 : 0];
+    if (!d) {
+        std::vector<WinDesc> wins;
+        try {
+            window_descs(p, gather, wins);
+        } catch (const std::bad_alloc &) {
+            return fail(WSP_ENOMEM, "host allocation of the window table failed");
+        }
+        int rc = upload(wins.data(), wins.size(), &d);
+        if (rc) return rc;
+    }
+    *out = d;
+    return WSP_OK;
+}
+
+int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order, bool gather,
+                 ItemDesc **out, int *count) {
+    const auto key = std::make_tuple(n_heads, text_len, bm, order, int(gather));
     {
         std::lock_guard<std::mutex> lk(p.mu);
         auto &m = p.dev[dev].items;
@@ -155,67 +174,20 @@ int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int 
             return WSP_OK;
         }
     }
-    std::vector<Item> items;
+    std::vector<ItemDesc> items;
     int rc;
     try {
-        rc = build_items(p, n_heads, text_len, bm, order, n_groups, items);
+        rc = build_items(p, n_heads, text_len, bm, order, gather, items);
     } catch (const std::bad_alloc &) {
         return fail(WSP_ENOMEM, "host allocation of the attention work list failed");
     }
     if (rc < 0) return rc;
-    Item *d = nullptr;
+    ItemDesc *d = nullptr;
     rc = upload(items.data(), items.size(), &d);
     if (rc) return rc;
     std::lock_guard<std::mutex> lk(p.mu);
     auto &m = p.dev[dev].items;
     auto ins = m.emplace(key, std::make_pair(d, int(items.size())));
-    if (!ins.second) (void)hipFree(d);
-    *out = ins.first->second.first;
-    *count = ins.first->second.second;
-    return WSP_OK;
-}
-
-int device_item_descs(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order,
-                      bool gather, ItemDesc **out, int *count) {
-    const auto key = std::make_tuple(n_heads, text_len, bm, order, int(gather));
-    {
-        std::lock_guard<std::mutex> lk(p.mu);
-        auto &m = p.dev[dev].descs;
-        auto it = m.find(key);
-        if (it != m.end()) {
-            *out = it->second.first;
-            *count = it->second.second;
-            return WSP_OK;
-        }
-    }
-    std::vector<ItemDesc> descs;
-    try {
-        std::vector<Item> items;
-        const int rc = build_items(p, n_heads, text_len, bm, order, 0, items);
-        if (rc < 0) return rc;
-        descs.resize(items.size());
-        for (size_t i = 0; i < items.size(); ++i) {
-            ItemDesc &d = descs[i];
-            d = ItemDesc{};
-            d.w = items[i].x;
-            d.hq = items[i].y;
-            if (d.w < 0) continue;
-            d.off = p.offsets[d.w];
-            d.lw = p.offsets[d.w + 1] - d.off;
-            // a window's rows in canonical order ascend (t, h, w row-major), so
-            // its first id is the smallest and its last the largest
-            d.vrow0 = gather ? p.ids[d.off] : d.off;
-            d.vrows = gather ? p.ids[d.off + d.lw - 1] - p.ids[d.off] + 1 : d.lw;
-        }
-    } catch (const std::bad_alloc &) {
-        return fail(WSP_ENOMEM, "host allocation of the attention work list failed");
-    }
-    ItemDesc *d = nullptr;
-    const int rc = upload(descs.data(), descs.size(), &d);
-    if (rc) return rc;
-    std::lock_guard<std::mutex> lk(p.mu);
-    auto &m = p.dev[dev].descs;
-    auto ins = m.emplace(key, std::make_pair(d, int(descs.size())));
     if (!ins.second) (void)hipFree(d);
     *out = ins.first->second.first;
     *count = ins.first->second.second;
@@ -283,9 +255,10 @@ void wsp_plan_free(wsp_plan_t *p) {
         if (t.ids) (void)hipFree(t.ids);
         if (t.rel) (void)hipFree(t.rel);
         if (t.pos) (void)hipFree(t.pos);
+        for (WinDesc *w : t.wins)
+            if (w) (void)hipFree(w);
         for (auto &pm : t.perm) (void)hipFree(pm.second);
         for (auto &it : t.items) (void)hipFree(it.second.first);
-        for (auto &it : t.descs) (void)hipFree(it.second.first);
     }
     if (have_cur) (void)hipSetDevice(cur);
     delete p;
@@ -323,9 +296,10 @@ int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, in
     if (head_dim != 64 && head_dim != 128) return fail(WSP_EINVAL, "head_dim must be 64 or 128");
     if (text_len < 0) return fail(WSP_EINVAL, "text_len must be >= 0");
     if (dtype != WSP_F32 && dtype != WSP_BF16) return fail(WSP_EINVAL, "unknown dtype");
-    const double b = double(p->nwin) * text_len * n_heads * head_dim * 4.0;
+    const int G = text_chunks(p->nwin);
+    const double b = double(G) * text_len * n_heads * head_dim * 4.0;
     if (b > 9e18) return fail(WSP_ERANGE, "workspace size overflows");
-    *bytes = size_t(p->nwin) * size_t(text_len) * size_t(n_heads) * size_t(head_dim) * 4u;
+    *bytes = size_t(G) * size_t(text_len) * size_t(n_heads) * size_t(head_dim) * 4u;
     return WSP_OK;
 }
 
@@ -338,12 +312,14 @@ int wsp_window_attn(const wsp_plan_t *pc, const void *q, const void *k, const vo
                               stream);
 }
 
-int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const void *v,
-                       const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
-                       int head_dim, int text_len, int dtype, float scale, unsigned flags,
-                       void *out, void *txt_out, void *workspace, size_t workspace_bytes,
-                       void *stream) {
-    g_last_error.clear();
+namespace {
+
+// Shared body of wsp_window_attn_ex (q8 = false) and wsp_window_attn_qk8.
+int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const void *v,
+                     const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                     int head_dim, int text_len, int dtype, bool q8, const float *amax_q,
+                     const float *amax_k, float scale, unsigned flags, void *out, void *txt_out,
+                     void *workspace, size_t workspace_bytes, void *stream) {
     if (flags & ~unsigned(WSP_ATTN_IO_CANONICAL)) return fail(WSP_EINVAL, "unknown attention flags");
     const bool gather = (flags & WSP_ATTN_IO_CANONICAL) != 0;
     size_t need = 0;
@@ -365,9 +341,9 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
                                             " bytes required, got " + std::to_string(workspace_bytes));
         if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
     }
-    // The bf16 kernel addresses a window's video rows (canonical order: the
-    // rows between its smallest and largest canonical id) and the text rows
-    // with 31-bit byte offsets from per-window buffer bases.
+    // The matrix-core kernel addresses a window's video rows (canonical
+    // order: the rows between its smallest and largest canonical id) and the
+    // text rows with 31-bit byte offsets from per-window buffer bases.
     if (dtype == WSP_BF16) {
         const int64_t row_bytes = int64_t(n_heads) * head_dim * 2;
         const int64_t rows = std::max<int64_t>(gather ? p->max_span : p->max_rows, text_len);
@@ -385,55 +361,51 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
     // query tiles: a window's partly empty last tile then wastes less.
     const int sched = g_attn_sched.load();
     const bool short_items = (double(p->n) / double(p->nwin) + text_len) < 1024.0;
-    const bool persist = dtype == WSP_BF16 && sched == WSP_SCHED_PERSISTENT;
     const bool small =
         sched == WSP_SCHED_PER_ITEM_128 || (sched == WSP_SCHED_AUTO && short_items);
-    const int bm = dtype != WSP_BF16 ? attn_f32_tile_m(head_dim)
-                   : persist        ? attn_bf16_persist_tile_m()
-                                    : attn_bf16_tile_m(small);
+    const int bm = dtype != WSP_BF16 ? attn_f32_tile_m(head_dim) : attn_bf16_tile_m(small);
 
     int dev = 0;
     WSP_HIP(hipGetDevice(&dev));
-    int n_groups = 0;
-    if (persist) {
-        WSP_HIP(hipDeviceGetAttribute(&n_groups, hipDeviceAttributeMultiprocessorCount, dev));
-        if (n_groups < 1) return fail(WSP_EDEVICE, "device reports no compute units");
-    }
-    int32_t *d_off = nullptr;
-    if ((rc = device_offsets(*p, dev, &d_off))) return rc;
-    int32_t *d_ids = nullptr;
-    if (gather && (rc = device_ids(*p, dev, &d_ids))) return rc;
-    Item *items = nullptr;
-    ItemDesc *descs = nullptr;
+    ItemDesc *items = nullptr;
+    WinDesc *wins = nullptr;
     int n_items = 0;
-    int32_t *d_rel = nullptr;
-    if (dtype == WSP_BF16 && !persist)
-        rc = device_item_descs(*p, dev, n_heads, text_len, bm, order, gather, &descs, &n_items);
-    else
-        rc = device_items(*p, dev, n_heads, text_len, bm, order, n_groups, &items, &n_items);
-    if (!rc && dtype == WSP_BF16 && gather) rc = device_rel_ids(*p, dev, &d_rel);
-    if (rc) return rc;
+    int32_t *d_ids = nullptr, *d_rel = nullptr;
+    if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, gather, &items, &n_items))) return rc;
+    if ((rc = device_windows(*p, dev, gather, &wins))) return rc;
+    if (gather && dtype == WSP_BF16 && (rc = device_rel_ids(*p, dev, &d_rel))) return rc;
+    if (gather && dtype != WSP_BF16 && (rc = device_ids(*p, dev, &d_ids))) return rc;
     hipStream_t s = hipStream_t(stream);
     float *ws = static_cast<float *>(workspace);
     hipError_t e;
-    if (persist)
-        e = launch_attn_bf16_persist(head_dim, q, k, v, txt_q, txt_k, txt_v, out, ws, d_off, d_ids, d_rel,
-                                     items, n_groups, n_items / n_groups, n_heads, text_len, scale, s);
-    else if (dtype == WSP_BF16)
-        e = launch_attn_bf16(head_dim, small, q, k, v, txt_q, txt_k, txt_v, out, ws, d_rel, descs,
-                             n_items, n_heads, text_len, scale, s);
+    if (dtype == WSP_BF16)
+        e = launch_attn_bf16(head_dim, small, q8, q, k, v, txt_q, txt_k, txt_v, out, ws, d_rel, items, wins,
+                             n_items, amax_q, amax_k, n_heads, text_len, scale, s);
     else
         e = launch_attn_f32(head_dim, static_cast<const float *>(q), static_cast<const float *>(k),
                             static_cast<const float *>(v), static_cast<const float *>(txt_q),
                             static_cast<const float *>(txt_k), static_cast<const float *>(txt_v),
-                            static_cast<float *>(out), ws, d_off, d_ids, items, n_items,
-                            n_heads, text_len, scale, s);
+                            static_cast<float *>(out), ws, d_ids, items, wins, n_items, n_heads,
+                            text_len, scale, s);
     if (e != hipSuccess) return hip_fail(e, "window attention kernel launch");
     if (text_len > 0) {
-        e = launch_text_mean(ws, txt_out, int64_t(text_len) * n_heads * head_dim, p->nwin, dtype, s);
+        e = launch_text_mean(ws, txt_out, int64_t(text_len) * n_heads * head_dim, text_chunks(p->nwin),
+                             p->nwin, dtype, s);
         if (e != hipSuccess) return hip_fail(e, "text mean kernel launch");
     }
     return WSP_OK;
+}
+
+}  // namespace
+
+int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const void *v,
+                       const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                       int head_dim, int text_len, int dtype, float scale, unsigned flags,
+                       void *out, void *txt_out, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    g_last_error.clear();
+    return window_attn_impl(pc, q, k, v, txt_q, txt_k, txt_v, n_heads, head_dim, text_len, dtype, false,
+                            nullptr, nullptr, scale, flags, out, txt_out, workspace, workspace_bytes, stream);
 }
 
 namespace {
@@ -578,57 +550,14 @@ int wsp_window_attn_qk8(const wsp_plan_t *pc, const void *q8, const void *k8, co
                         int text_len, float scale, unsigned flags, void *out, void *txt_out,
                         void *workspace, size_t workspace_bytes, void *stream) {
     g_last_error.clear();
-    if (flags & ~unsigned(WSP_ATTN_IO_CANONICAL)) return fail(WSP_EINVAL, "unknown attention flags");
-    const bool gather = (flags & WSP_ATTN_IO_CANONICAL) != 0;
     if (head_dim != 128) return fail(WSP_EINVAL, "the fp8 q/k attention needs head_dim 128");
     if (!amax_q || !amax_k) return fail(WSP_EINVAL, "amax_q and amax_k must be non-NULL");
-    size_t need = 0;
-    int rc = wsp_window_attn_workspace(pc, n_heads, head_dim, text_len, WSP_BF16, &need);
-    if (rc) return rc;
-    wsp_plan_t *p = const_cast<wsp_plan_t *>(pc);
-    for (const void *ptr : {q8, k8, v, static_cast<const void *>(out)}) {
-        if (!ptr) return fail(WSP_EINVAL, "q, k, v and out must be non-NULL");
-        if (!aligned16(ptr)) return fail(WSP_EINVAL, "q, k, v and out must be 16-byte aligned");
-    }
-    if (out == q8 || out == k8 || out == v) return fail(WSP_EINVAL, "out must not alias q, k or v");
-    if (text_len > 0) {
-        for (const void *ptr : {txt_q8, txt_k8, txt_v, static_cast<const void *>(txt_out)}) {
-            if (!ptr) return fail(WSP_EINVAL, "text tensors and txt_out must be non-NULL when text_len > 0");
-            if (!aligned16(ptr)) return fail(WSP_EINVAL, "text tensors must be 16-byte aligned");
-        }
-        if (!workspace || workspace_bytes < need)
-            return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) +
-                                            " bytes required, got " + std::to_string(workspace_bytes));
-        if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
-    }
-    {
-        const int64_t row_bytes = int64_t(n_heads) * head_dim * 2;
-        const int64_t rows = std::max<int64_t>(gather ? p->max_span : p->max_rows, text_len);
-        if (rows * row_bytes >= (int64_t(1) << 31))
-            return fail(WSP_ERANGE, gather ? "a window's canonical rows span 2 GiB or more"
-                                           : "a window's rows (or the text rows) take 2 GiB or more");
-    }
-    if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
-    const int order = g_attn_order.load();
-    int dev = 0;
-    WSP_HIP(hipGetDevice(&dev));
-    int32_t *d_off = nullptr, *d_ids = nullptr;
-    if ((rc = device_offsets(*p, dev, &d_off))) return rc;
-    if (gather && (rc = device_ids(*p, dev, &d_ids))) return rc;
-    Item *items = nullptr;
-    int n_items = 0;
-    if ((rc = device_items(*p, dev, n_heads, text_len, attn_qk8_tile_m(), order, 0, &items, &n_items)))
-        return rc;
-    hipStream_t s = hipStream_t(stream);
-    float *ws = static_cast<float *>(workspace);
-    hipError_t e = launch_attn_qk8(q8, k8, v, txt_q8, txt_k8, txt_v, out, ws, d_off, d_ids, items,
-                                   n_items, amax_q, amax_k, n_heads, text_len, scale, s);
-    if (e != hipSuccess) return hip_fail(e, "fp8 attention kernel launch");
-    if (text_len > 0) {
-        e = launch_text_mean(ws, txt_out, int64_t(text_len) * n_heads * head_dim, p->nwin, WSP_BF16, s);
-        if (e != hipSuccess) return hip_fail(e, "text mean kernel launch");
-    }
-    return WSP_OK;
+    if (!aligned16(amax_q) && (reinterpret_cast<uintptr_t>(amax_q) & 3u))
+        return fail(WSP_EINVAL, "amax_q must be 4-byte aligned");
+    if (!aligned16(amax_k) && (reinterpret_cast<uintptr_t>(amax_k) & 3u))
+        return fail(WSP_EINVAL, "amax_k must be 4-byte aligned");
+    return window_attn_impl(pc, q8, k8, v, txt_q8, txt_k8, txt_v, n_heads, head_dim, text_len, WSP_BF16, true,
+                            amax_q, amax_k, scale, flags, out, txt_out, workspace, workspace_bytes, stream);
 }
 
 int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, int N, int K,
@@ -662,8 +591,7 @@ int wsp_set_attn_order(int order) {
 
 int wsp_set_attn_schedule(int schedule) {
     g_last_error.clear();
-    if (schedule != WSP_SCHED_AUTO && schedule != WSP_SCHED_PERSISTENT && schedule != WSP_SCHED_PER_ITEM &&
-        schedule != WSP_SCHED_PER_ITEM_128)
+    if (schedule != WSP_SCHED_AUTO && schedule != WSP_SCHED_PER_ITEM && schedule != WSP_SCHED_PER_ITEM_128)
         return fail(WSP_EINVAL, "unknown attention schedule");
     g_attn_sched.store(schedule);
     return WSP_OK;

@@ -146,76 +146,126 @@ void relayout_perm(const wsp_plan_t &src, const wsp_plan_t &dst, std::vector<int
     for (int64_t j = 0; j < dst.n; ++j) perm[size_t(j)] = src.inv[size_t(dst.ids[size_t(j)])];
 }
 
-int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order, int n_groups,
-                std::vector<Item> &items) {
+void window_descs(const wsp_plan_t &p, bool gather, std::vector<WinDesc> &wins) {
+    wins.resize(size_t(p.nwin));
+    for (int32_t w = 0; w < p.nwin; ++w) {
+        WinDesc &d = wins[size_t(w)];
+        d.off = p.offsets[w];
+        d.lw = p.offsets[w + 1] - d.off;
+        // a window's rows in canonical order ascend (row-major in t, h, w):
+        // its first id is the smallest and its last the largest
+        d.vrow0 = gather ? p.ids[d.off] : d.off;
+        d.vrows = gather ? p.ids[d.off + d.lw - 1] - p.ids[d.off] + 1 : d.lw;
+    }
+}
+
+int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order, bool gather,
+                std::vector<ItemDesc> &items) {
     constexpr int kXcds = 8;
+    constexpr int kKeyTile = 64;
+    std::vector<WinDesc> wins;
+    window_descs(p, gather, wins);
     std::vector<int32_t> worder(size_t(p.nwin));
     if (order == WSP_ORDER_ID)
         std::iota(worder.begin(), worder.end(), 0);
     else
         worder = p.lpt;
-    items.clear();
-    auto tiles_of = [&](int32_t w) {
-        return ceil_div(int64_t(p.offsets[w + 1] - p.offsets[w]) + text_len, bm);
-    };
-    for (int32_t w : worder)
-        if (tiles_of(w) > 0xFFFF)
+    // Cost of a query tile over one window: its 64-key tiles.
+    auto key_tiles = [&](int32_t w) { return ceil_div(int64_t(wins[size_t(w)].lw) + text_len, kKeyTile); };
+    const int64_t text_tiles = ceil_div(text_len, bm);
+    if (text_tiles > 0xFFFF) return fail(WSP_ERANGE, "text_len needs more than 65535 query tiles");
+    for (int32_t w = 0; w < p.nwin; ++w)
+        if (ceil_div(wins[size_t(w)].lw, bm) > 0xFFFF)
             return fail(WSP_ERANGE, "window " + std::to_string(w) + " needs more than 65535 query tiles");
-    if (n_groups > 0) {
-        // Persistent lists: work group g (on XCD g % 8) runs items[r * n_groups
-        // + g] for r = 0, 1, ...  Each (window, head) group goes whole to the
-        // least-loaded XCD (ORDER_LPT_XCD; any work group otherwise), and each
-        // of its query tiles to the least-loaded work group there; an item
-        // costs its number of 64-key tiles.  Groups are taken in `worder`.
-        const int xcds = (order == WSP_ORDER_LPT_XCD && n_groups >= kXcds) ? kXcds : 1;
-        std::vector<std::vector<Item>> lists(static_cast<size_t>(n_groups));
-        std::vector<int64_t> wg_load(static_cast<size_t>(n_groups), 0), xcd_load(static_cast<size_t>(xcds), 0);
-        for (int32_t w : worder) {
-            const int64_t len = int64_t(p.offsets[w + 1] - p.offsets[w]) + text_len;
-            const int64_t tiles = tiles_of(w), cost = ceil_div(len, 64);
+
+    // Groups of items that read the same K/V: all query tiles of a (window,
+    // head), and all text query tiles of a (chunk, head); with their cost.
+    struct Group {
+        int64_t cost;
+        std::vector<ItemDesc> items;
+    };
+    std::vector<Group> tgroups, vgroups;
+    if (text_len > 0) {
+        const int G = text_chunks(p.nwin);
+        for (int c = 0; c < G; ++c) {
+            const int w0 = chunk_begin(c, p.nwin, G), w1 = chunk_begin(c + 1, p.nwin, G);
+            int64_t cost = 0;
+            for (int w = w0; w < w1; ++w) cost += key_tiles(w);
             for (int h = 0; h < n_heads; ++h) {
-                const int x = int(std::min_element(xcd_load.begin(), xcd_load.end()) - xcd_load.begin());
-                for (int64_t t = 0; t < tiles; ++t) {
-                    int best = -1;
-                    for (int g = x; g < n_groups; g += xcds)
-                        if (best < 0 || wg_load[size_t(g)] < wg_load[size_t(best)]) best = g;
-                    lists[size_t(best)].push_back({w, (h << 16) | int(t)});
-                    wg_load[size_t(best)] += cost;
+                Group g{cost * text_tiles, {}};
+                for (int64_t t = 0; t < text_tiles; ++t) {
+                    ItemDesc d{};
+                    d.w = w0;
+                    d.hq = (h << 16) | int(t);
+                    d.nwin = w1 - w0;
+                    d.chunk = c;
+                    g.items.push_back(d);
                 }
-                xcd_load[size_t(x)] += tiles * cost;
+                tgroups.push_back(std::move(g));
             }
         }
-        size_t rounds = 0;
-        for (auto &l : lists) rounds = std::max(rounds, l.size());
-        items.assign(rounds * size_t(n_groups), Item{-1, 0});
-        for (int g = 0; g < n_groups; ++g)
-            for (size_t r = 0; r < lists[size_t(g)].size(); ++r) items[r * size_t(n_groups) + size_t(g)] = lists[size_t(g)][r];
-        return int(items.size());
+        std::stable_sort(tgroups.begin(), tgroups.end(),
+                         [](const Group &a, const Group &b) { return a.cost > b.cost; });
     }
+    for (int32_t w : worder) {
+        const int64_t tiles = ceil_div(wins[size_t(w)].lw, bm);
+        for (int h = 0; h < n_heads; ++h) {
+            Group g{tiles * key_tiles(w), {}};
+            for (int64_t t = 0; t < tiles; ++t) {
+                ItemDesc d{};
+                d.w = w;
+                d.hq = (h << 16) | int(t);
+                d.win = wins[size_t(w)];
+                g.items.push_back(d);
+            }
+            vgroups.push_back(std::move(g));
+        }
+    }
+    // A text item covers a whole chunk of windows (several times a video
+    // item) and reads K/V that no other item on its XCD shares, so text
+    // groups are spread evenly over the first half of the video groups of
+    // their list instead of all starting together: early enough to finish
+    // well before the end, without every CU streaming unshared K/V at once.
+    auto merge = [](const std::vector<const Group *> &tg, const std::vector<const Group *> &vg,
+                    std::vector<ItemDesc> &outl) {
+        const size_t nt = tg.size(), nv = vg.size();
+        size_t ti = 0;
+        for (size_t vi = 0; vi <= nv; ++vi) {
+            while (ti < nt && (nv == 0 || ti * (nv / 2 + 1) <= vi * nt)) {
+                outl.insert(outl.end(), tg[ti]->items.begin(), tg[ti]->items.end());
+                ++ti;
+            }
+            if (vi < nv) outl.insert(outl.end(), vg[vi]->items.begin(), vg[vi]->items.end());
+        }
+    };
+    items.clear();
     if (order != WSP_ORDER_LPT_XCD) {
-        for (int32_t w : worder)
-            for (int h = 0; h < n_heads; ++h)
-                for (int64_t t = 0; t < tiles_of(w); ++t) items.push_back({w, (h << 16) | int(t)});
+        std::vector<const Group *> tg, vg;
+        for (const Group &g : tgroups) tg.push_back(&g);
+        for (const Group &g : vgroups) vg.push_back(&g);
+        merge(tg, vg, items);
         return int(items.size());
     }
     // Work groups are handed to the XCDs round-robin by block index, so block
-    // b runs on XCD b % 8.  Each (window, head) group -- whose query tiles all
-    // read the same K/V -- goes whole to the least-loaded XCD (largest group
-    // first), and each XCD's list keeps the largest-first order.
-    std::vector<std::vector<Item>> lists(kXcds);
+    // b runs on XCD b % 8.  Each group -- whose items all read the same K/V --
+    // goes whole to the least-loaded XCD (text groups first, then video
+    // groups largest first), and each XCD's list is merged as above.
+    std::vector<std::vector<const Group *>> tl(kXcds), vl(kXcds);
     std::vector<int64_t> load(kXcds, 0);
-    for (int32_t w : worder) {
-        const int64_t tiles = tiles_of(w);
-        const int64_t cost = tiles * (int64_t(p.offsets[w + 1] - p.offsets[w]) + text_len);
-        for (int h = 0; h < n_heads; ++h) {
-            const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
-            for (int64_t t = 0; t < tiles; ++t) lists[x].push_back({w, (h << 16) | int(t)});
-            load[x] += cost;
-        }
-    }
+    auto place = [&](const Group &g, std::vector<std::vector<const Group *>> &l) {
+        const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
+        l[size_t(x)].push_back(&g);
+        load[size_t(x)] += g.cost;
+    };
+    for (const Group &g : tgroups) place(g, tl);
+    for (const Group &g : vgroups) place(g, vl);
+    std::vector<std::vector<ItemDesc>> lists(kXcds);
+    for (int x = 0; x < kXcds; ++x) merge(tl[size_t(x)], vl[size_t(x)], lists[size_t(x)]);
     size_t longest = 0;
     for (auto &l : lists) longest = std::max(longest, l.size());
-    items.assign(longest * kXcds, Item{-1, 0});
+    ItemDesc idle{};
+    idle.w = -1;
+    items.assign(longest * kXcds, idle);
     for (int x = 0; x < kXcds; ++x)
         for (size_t s = 0; s < lists[x].size(); ++s) items[s * kXcds + x] = lists[x][s];
     return int(items.size());

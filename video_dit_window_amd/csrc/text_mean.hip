@@ -3,9 +3,11 @@
 // "Window-Aligned Sequence Parallelism (SeedVR2)", section "Text stream":
 // every window yields one text output T_w and the next text state is the sum
 // over windows divided by the window count (not a token-weighted mean).  The
-// per-window outputs arrive as float32 rows [n_windows][Lt*H*D]; each thread
-// sums four consecutive elements over the windows in id order (fixed order:
-// bit-identical results run to run), divides once and rounds once.
+// attention kernels leave one float32 partial per chunk of consecutive
+// windows, [n_parts][Lt*H*D] (each the sum of its windows' T_w in id order);
+// each thread adds four consecutive elements of the partials in chunk order
+// (a fixed order: bit-identical results run to run, whatever order the work
+// groups ran in), divides once by the window count and rounds once.
 
 #include "wsp_internal.h"
 
@@ -21,14 +23,14 @@ __device__ inline uint16_t to_bf16_bits(float f) {
 
 __global__ __launch_bounds__(256) void text_mean_kernel(const float *__restrict__ ws,
                                                         void *__restrict__ out,
-                                                        int64_t per_window, int n_windows,
+                                                        int64_t per_part, int n_parts, int n_windows,
                                                         int out_bf16) {
     const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-    if (i >= per_window) return;
+    if (i >= per_part) return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const float *p = ws + i;
-#pragma unroll 8
-    for (int w = 0; w < n_windows; ++w) acc += *reinterpret_cast<const f32x4 *>(p + int64_t(w) * per_window);
+#pragma unroll 4
+    for (int c = 0; c < n_parts; ++c) acc += *reinterpret_cast<const f32x4 *>(p + int64_t(c) * per_part);
     const float n = float(n_windows);
     acc = acc / n;
     if (out_bf16) {
@@ -43,11 +45,11 @@ __global__ __launch_bounds__(256) void text_mean_kernel(const float *__restrict_
 
 }  // namespace
 
-hipError_t launch_text_mean(const float *ws, void *txt_out, int64_t per_window, int n_windows,
-                            int dtype, hipStream_t s) {
-    if (per_window <= 0) return hipSuccess;
-    const int64_t blocks = (per_window / 4 + 255) / 256;
-    text_mean_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(ws, txt_out, per_window,
+hipError_t launch_text_mean(const float *ws, void *txt_out, int64_t per_part, int n_parts,
+                            int n_windows, int dtype, hipStream_t s) {
+    if (per_part <= 0) return hipSuccess;
+    const int64_t blocks = (per_part / 4 + 255) / 256;
+    text_mean_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(ws, txt_out, per_part, n_parts,
                                                                    n_windows, dtype == WSP_BF16);
     return hipGetLastError();
 }
