@@ -67,34 +67,48 @@ def attn_flops(lengths, heads, head_dim, text_len):
 
 
 def cpu_baseline(w, budget_s):
-    """The oracle, as it stands, on a bounded sample of the workload: (window,
-    head) pairs of the regular layout in largest-first order until the time
-    budget is spent.  Returns the cpu_baseline object."""
+    """The oracle, as it stands, on the host cores: its joint_attention in
+    float32 (numpy BLAS), one (window, head) pair per host thread (one BLAS
+    thread each), over the regular layer of the workload, largest windows
+    first.  The whole layer runs unless the time budget ends first; the
+    result is FLOPs done / wall time either way, and the sample says which."""
     import oracle as O
-    from threadpoolctl import threadpool_info
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
     op = O.plan(*geo, O.REGULAR)
-    rng = np.random.default_rng(12345)
-    tq, tk, tv = (rng.standard_normal((w.text_len, w.head_dim)) / np.sqrt(w.head_dim)
-                  for _ in range(3))
-    flops, pairs, el = 0, 0, 0.0
-    for win in op.lpt:
-        L = int(op.offsets[win + 1] - op.offsets[win])
-        for h in range(w.heads):
-            qv, kv, vv = (rng.standard_normal((L, w.head_dim)) / np.sqrt(w.head_dim) for _ in range(3))
-            t1 = time.perf_counter()
-            O.joint_attention(qv, kv, vv, tq, tk, tv)
-            el += time.perf_counter() - t1
-            flops += 4 * w.head_dim * (L + w.text_len) ** 2
-            pairs += 1
-            if el > budget_s:
-                break
-        if el > budget_s:
-            break
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{pairs} (window, head) pairs of the {w.name} regular layout, largest "
-                      f"windows first, float64 numpy; {el:.1f} s inside the oracle",
+    inp = I.qkv(w, bits_only=True)
+    f32 = {n: I.bf16_bits_to_f32(b) for n, (_, b) in inp.items()}      # canonical order
+    del inp
+    threads = min(os.cpu_count() or 1, 64)
+    pairs = [(int(win), h) for win in op.lpt for h in range(w.heads)]
+    deadline = [None]
+
+    def one(pair):
+        win, h = pair
+        if time.perf_counter() > deadline[0]:
+            return 0
+        ids = op.ids[op.offsets[win]:op.offsets[win + 1]]
+        O.joint_attention(f32["q"][ids, h], f32["k"][ids, h], f32["v"][ids, h], f32["txt_q"][:, h],
+                          f32["txt_k"][:, h], f32["txt_v"][:, h], dtype=np.float32)
+        return 4 * w.head_dim * (len(ids) + w.text_len) ** 2
+
+    with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        deadline[0] = t0 + budget_s
+        done = list(ex.map(one, pairs))
+        el = time.perf_counter() - t0
+    flops, n_done = sum(done), sum(1 for d in done if d)
+    total = attn_flops(np.diff(op.offsets), w.heads, w.head_dim, w.text_len)
+    full = n_done == len(pairs)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"the whole {w.name} regular layer ({len(pairs)} (window, head) pairs, "
+                       f"{total:.4e} FLOP) in {el:.1f} s" if full else
+                       f"{n_done} of {len(pairs)} (window, head) pairs of the {w.name} regular layer, "
+                       f"largest windows first, in {el:.1f} s (whole layer extrapolated: "
+                       f"{total / (flops / el):.1f} s)")
+                      + f"; float32 numpy oracle, one pair per host thread",
+            "layer_seconds": round(el if full else total / (flops / el), 2),
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
@@ -161,19 +175,75 @@ def stack_measure(w, n_layers, attn_flops_per_layer, reps=2):
             "flop_per_layer": {"projections": 4 * lin_flops, "attention": attn_flops_per_layer}}
 
 
+def config_launches(names, warmup=3, reps=10):
+    """The other workload grids on the same kernel and launch (canonical-order
+    I/O): the 720p-shaped regular layer and the 4K-shaped shifted layer
+    (inputs N(0,1)/sqrt(128) from torch's seeded device generator, rounded
+    to bf16).  Per grid: average launch time by HIP events on the launch
+    stream (attention kernel + text-mean combine of one call), TFLOP/s,
+    fraction of the bf16 MFMA peak and video tokens/s/layer."""
+    import torch
+    import video_dit_window_amd as W
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, method in names:
+        w = I.WORKLOADS[name]
+        geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+        p = W.Plan(*geo, W.REGULAR if method == "regular" else W.SHIFTED)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.index)
+
+        def rnd(rows):
+            t = torch.empty((rows, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+            for lo in range(0, rows, 1 << 16):   # bounded float32 temporaries
+                hi = min(rows, lo + (1 << 16))
+                t[lo:hi] = (torch.randn((hi - lo, w.heads, w.head_dim), device="cuda", generator=g)
+                            * w.std).to(torch.bfloat16)
+            return t
+        q, k, v = (rnd(w.n_tokens) for _ in range(3))
+        tq, tk, tv = (rnd(w.text_len) for _ in range(3))
+        out, txt = torch.empty_like(q), torch.empty_like(tq)
+        ws = torch.empty(max(W.window_attn_workspace(p, w.heads, w.head_dim, w.text_len, W.BF16, per_window=True), 16),
+                         dtype=torch.uint8, device="cuda")
+        call = lambda: W.window_attn(p, q, k, v, tq, tk, tv, out=out, txt_out=txt, workspace=ws, canonical=True)
+        r = max(2, reps if w.n_tokens < 500000 else reps // 2)
+        for _ in range(warmup):
+            call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(r):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / r
+        flops = attn_flops(np.diff(p.tables()["offsets"]), w.heads, w.head_dim, w.text_len)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[f"{name}_{method}"] = {
+            "grid_thw": [w.T, w.H, w.W], "windows": p.n_windows, "text_len": w.text_len,
+            "avg_launch_ms": round(ms, 4), "flop_per_launch": flops, "attn_kernel_tflops": round(tf, 2),
+            "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "video_tokens_per_s_per_layer": round(w.n_tokens / (ms * 1e-3), 1), "launches": r}
+        del q, k, v, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="1080p_bf16", choices=["720p_bf16", "1080p_bf16", "4k_bf16"])
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
+    ap.add_argument("--cpu-budget", type=float, default=40.0,
+                    help="seconds of oracle timing at most (the whole regular layer if it fits)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true",
                     help="headline = the pass with explicit relayout kernels (skip the fused pass)")
     ap.add_argument("--stack-layers", type=int, default=32,
                     help="layers of the multi-layer stack side measurement")
     ap.add_argument("--no-stack", action="store_true", help="skip the multi-layer stack side measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 720p regular / 4K shifted attention launches")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (a known-size "
                          "reference for HBM byte counters)")
@@ -199,13 +269,17 @@ def main():
     outs = [torch.empty_like(dev["q"]) for _ in plans]
     out_c = torch.empty_like(dev["q"])
     txts = [torch.empty_like(dev["txt_q"]) for _ in plans]
-    ws_bytes = max(W.window_attn_workspace(p, Hh, D, Lt, W.BF16) for p in plans)
+    # one text partial per window (the faster text reduction); the minimum
+    # workspace (16 chunks of windows) is timed beside it as `text_chunked`
+    ws_bytes = max(W.window_attn_workspace(p, Hh, D, Lt, W.BF16, per_window=True) for p in plans)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws_min_bytes = max(W.window_attn_workspace(p, Hh, D, Lt, W.BF16) for p in plans)
+    ws_min = torch.empty(max(ws_min_bytes, 16), dtype=torch.uint8, device="cuda")
     flops = [attn_flops(np.diff(p.tables()["offsets"]), Hh, D, Lt) for p in plans]
     row_bytes = Hh * D * 2
     stream = torch.cuda.current_stream()
 
-    ev = {"attn": [], "relayout": [], "fused_attn": [], "rope": [], "qk8_attn": []}
+    ev = {"attn": [], "relayout": [], "fused_attn": [], "rope": [], "qk8_attn": [], "chunked_attn": []}
 
     def timed(kind, fn, record):
         if record:
@@ -352,6 +426,21 @@ def main():
             orders[name] = round(run(step_fused)[0], 4)
         W.set_attn_order(W.ORDER_LPT_XCD)
         res["dispatch_order_ms_per_step"] = orders
+        # The same pass with the minimum workspace: the text mean from 16
+        # chunks of windows (text items over whole chunks) instead of one
+        # partial per window.
+        def step_chunked(record):
+            for li, p in enumerate(plans):
+                timed("chunked_attn", lambda li=li, p=p: W.window_attn(
+                    p, dev["q"], dev["k"], dev["v"], dev["txt_q"], dev["txt_k"], dev["txt_v"],
+                    out=outs[li], txt_out=txts[li], workspace=ws_min, canonical=True), record)
+        ms_ch = run(step_chunked)[0]
+        ch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["chunked_attn"]]))
+        res["text_chunked"] = {
+            "note": "headline pass with the minimum workspace (text mean from min(windows, 16) chunk sums)",
+            "workspace_bytes": ws_min_bytes, "headline_workspace_bytes": ws_bytes,
+            "ms_per_step": round(ms_ch, 4), "avg_launch_ms": round(ch_ms, 4),
+            "attn_kernel_tflops": round(per_call_flops / (ch_ms * 1e-3) / 1e12, 2)}
     rope_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["rope"]]))
     rope_bytes = 2 * N * row_bytes + 12 * N   # rows in + out, perm + id + position per row
     res["rope_relayout"] = {"note": "q or k moved canonical -> layout with window-local 3D RoPE",
@@ -363,6 +452,8 @@ def main():
         "note": "q, k as OCP E4M3 codes (per-head scales) on the FP8 matrix cores; v, P, outputs bf16",
         "avg_launch_ms": round(q8_ms, 4),
         "attn_kernel_tflops": round(per_call_flops / (q8_ms * 1e-3) / 1e12, 2)}
+    if not args.no_configs:
+        res["configs"] = config_launches([("720p_bf16", "regular"), ("4k_bf16", "shifted")])
     if not args.no_stack:
         res["stack"] = stack_measure(w, args.stack_layers, per_call_flops)
     if not args.no_cpu_baseline:

@@ -144,12 +144,16 @@ int wsp_relayout(const void *x, void *y, int64_t row_bytes, const wsp_plan_t *sr
                  const wsp_plan_t *dst, void *stream);
 
 /*
- * wsp_window_attn_workspace -- device workspace (bytes) wsp_window_attn needs:
- * G * text_len * n_heads * head_dim * 4 with G = min(n_windows, 16): one
- * float32 partial text sum per chunk of consecutive windows (the windows
- * split into G runs of ids, run c starting at floor(c * n_windows / G)).
- * 0 when text_len == 0.  1080p-shaped layer (20 x 128, 256 text tokens):
- * 42 MB; 4K-shaped (512 text tokens): 84 MB.
+ * wsp_window_attn_workspace -- the smallest device workspace (bytes)
+ * wsp_window_attn accepts: G * text_len * n_heads * head_dim * 4 with
+ * G = min(n_windows, 16), one float32 partial text sum per chunk of
+ * consecutive windows (the windows split into G runs of ids, run c starting
+ * at floor(c * n_windows / G)).  0 when text_len == 0.  1080p-shaped layer
+ * (20 x 128, 256 text tokens): 42 MB; 4K-shaped (512 text tokens): 84 MB.
+ * A workspace of n_windows * text_len * n_heads * head_dim * 4 bytes or more
+ * (262 MB at 1080p, 2.6 GB at 4K) selects one partial per window: each text
+ * work item then covers one window and shares that window's K/V in L2 with
+ * its video items (a few percent faster at 1080p).
  * Errors: WSP_EINVAL (bad plan/shape/dtype), WSP_ERANGE.
  */
 int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, int text_len,
@@ -172,9 +176,12 @@ int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, in
  *   V = [v[a:b, h]; txt_v[:, h]],  O = softmax(Q K^T * scale) V;
  *   out[a:b, h] = the first b-a rows of O; T_w = the last text_len rows.
  *   txt_out[:, h] = (sum_w T_w) / n_windows, summed in float32 in a fixed
- *   order -- window order inside each of G = min(n_windows, 16) chunks of
- *   consecutive windows, then the chunk sums in chunk order -- and rounded
- *   once to dtype (bit-identical from run to run and across dispatch orders).
+ *   order -- window order inside each of G chunks of consecutive windows,
+ *   then the chunk sums in chunk order -- and rounded once to dtype.  G is
+ *   n_windows when workspace_bytes >= n_windows * text_len * n_heads *
+ *   head_dim * 4, else min(n_windows, 16) (wsp_window_attn_workspace); for a
+ *   given G the result is bit-identical from run to run and across dispatch
+ *   orders.
  *
  * p                 plan; q/k/v/out rows are in its layout
  * q, k, v           device, [n_tokens, n_heads, head_dim] of dtype

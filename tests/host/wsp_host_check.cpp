@@ -144,8 +144,9 @@ static void check_plan(int T, int H, int W, int nt, int nh, int nw, int method) 
             for (int bm : {64, 128, 256})
                 for (int Lt : {0, 1, 40, 300})
                     for (int heads : {1, 3}) {
+                      for (int G : {text_chunks(nwin), int(nwin)}) {
                         std::vector<ItemDesc> items;
-                        const int cnt = build_items(*p, heads, Lt, bm, order, gather != 0, items);
+                        const int cnt = build_items(*p, heads, Lt, bm, order, gather != 0, G, items);
                         CHECK(cnt == int(items.size()));
                         std::set<std::tuple<int, int, int>> vid, txt;
                         int64_t real = 0;
@@ -164,7 +165,6 @@ static void check_plan(int T, int H, int W, int nt, int nh, int nw, int method) 
                                 CHECK(vid.insert({it.w, h, t}).second);
                             } else {
                                 CHECK(Lt > 0);
-                                const int G = text_chunks(nwin);
                                 CHECK(it.chunk >= 0 && it.chunk < G);
                                 CHECK(it.w == chunk_begin(it.chunk, nwin, G));
                                 CHECK(it.w + it.nwin == chunk_begin(it.chunk + 1, nwin, G));
@@ -175,10 +175,11 @@ static void check_plan(int T, int H, int W, int nt, int nh, int nw, int method) 
                         int64_t want_vid = 0;
                         for (int32_t w = 0; w < nwin; ++w)
                             want_vid += heads * ((int64_t(off[size_t(w) + 1] - off[size_t(w)]) + bm - 1) / bm);
-                        const int64_t want_txt = Lt > 0 ? int64_t(text_chunks(nwin)) * heads * ((Lt + bm - 1) / bm) : 0;
+                        const int64_t want_txt = Lt > 0 ? int64_t(G) * heads * ((Lt + bm - 1) / bm) : 0;
                         CHECK(int64_t(vid.size()) == want_vid);
                         CHECK(int64_t(txt.size()) == want_txt);
                         CHECK(real == want_vid + want_txt);
+                      }
                     }
     }
     // chunks cover the windows once, in id order

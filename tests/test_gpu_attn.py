@@ -30,10 +30,11 @@ def host_f64(inp, name):
     return (v if v is not None else I.bf16_bits_to_f32(b)).astype(np.float64)
 
 
-def run_full(w, method, dtype_check, order=None, scale=None):
+def run_full(w, method, dtype_check, order=None, scale=None, per_window=True):
     """Whole-grid comparison for a small workload: canonical inputs are
     relayouted to the method's layout on the GPU, attended, and compared with
-    the oracle over every output element."""
+    the oracle over every output element.  per_window=False runs the text
+    mean from min(windows, 16) chunk sums (the minimum workspace)."""
     import torch
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
     om, wm = METH[method]
@@ -45,7 +46,8 @@ def run_full(w, method, dtype_check, order=None, scale=None):
     if order is not None:
         W.set_attn_order(order)
     try:
-        out, txt = W.window_attn(wp, q, k, v, d["txt_q"], d["txt_k"], d["txt_v"], scale=scale)
+        out, txt = W.window_attn(wp, q, k, v, d["txt_q"], d["txt_k"], d["txt_v"], scale=scale,
+                                 per_window=per_window)
     finally:
         W.set_attn_order(W.ORDER_LPT_XCD)
     out_c = W.relayout(out, wp, wc)
@@ -121,6 +123,21 @@ def test_mid_bf16(gpu, case, method):
     run_full(w, method, check_bf16)
 
 
+@pytest.mark.parametrize("case", MID, ids=[c[0] for c in MID])
+@pytest.mark.parametrize("method", ["regular", "shifted"])
+def test_mid_bf16_chunked_text(gpu, case, method):
+    """The minimum workspace: text items over chunks of consecutive windows
+    (16 chunks, or one per window when there are fewer)."""
+    w = I.custom(*case, "bf16", index=300 + MID.index(case))
+    run_full(w, method, check_bf16, per_window=False)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_mid_f32_chunked_text(gpu, D):
+    w = I.custom("mid_f32", 6, 30, 52, 2, 3, 3, 2, D, 37, "f32", index=201)
+    run_full(w, "regular", check_f32, per_window=False)
+
+
 def test_bf16_unscaled_inputs(gpu):
     """N(0,1) inputs give logits of standard deviation ~1 (the default
     N(0,1)/sqrt(D) inputs give ~0.008, a nearly uniform softmax), which
@@ -161,8 +178,11 @@ def test_bf16_explicit_scale(gpu):
     run_full(w, "shifted", check_bf16, scale=0.05)
 
 
-def test_bf16_order_independent_and_deterministic(gpu):
-    """Results do not depend on the dispatch order, and repeat bit for bit."""
+@pytest.mark.parametrize("per_window", [True, False], ids=["per_window_text", "chunked_text"])
+def test_bf16_order_independent_and_deterministic(gpu, per_window):
+    """Results do not depend on the dispatch order, and repeat bit for bit
+    (for either text reduction; the grid has 27 shifted windows, so the
+    minimum workspace gives 16 chunks of one or two windows)."""
     import torch
     w = I.custom("mid_order", 6, 30, 52, 2, 3, 3, 3, 128, 40, "bf16", index=330)
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
@@ -171,7 +191,7 @@ def test_bf16_order_independent_and_deterministic(gpu):
     outs = []
     for order in (W.ORDER_LPT_XCD, W.ORDER_LPT, W.ORDER_ID, W.ORDER_LPT_XCD):
         W.set_attn_order(order)
-        o, t = W.window_attn(p, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"])
+        o, t = W.window_attn(p, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"], per_window=per_window)
         outs.append((o.clone(), t.clone()))
     W.set_attn_order(W.ORDER_LPT_XCD)
     torch.cuda.synchronize()
@@ -182,7 +202,8 @@ def test_bf16_order_independent_and_deterministic(gpu):
 
 @pytest.mark.parametrize("case", MID, ids=[c[0] for c in MID])
 @pytest.mark.parametrize("canonical", [False, True], ids=["layout_io", "canonical_io"])
-def test_bf16_schedules_bit_identical(gpu, case, canonical):
+@pytest.mark.parametrize("per_window", [True, False], ids=["per_window_text", "chunked_text"])
+def test_bf16_schedules_bit_identical(gpu, case, canonical, per_window):
     """One work group per 256-row item and one per 128-row item run the same
     per-wavefront arithmetic in the same order: identical bits, for both I/O
     orders."""
@@ -197,7 +218,7 @@ def test_bf16_schedules_bit_identical(gpu, case, canonical):
             W.set_attn_schedule(sched)
             try:
                 o, t = W.window_attn(p, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"],
-                                     canonical=canonical)
+                                     canonical=canonical, per_window=per_window)
             finally:
                 W.set_attn_schedule(W.SCHED_AUTO)
             res[(method, sched)] = (o, t)
@@ -309,7 +330,7 @@ def test_1080p_sampled(gpu, method):
 
 
 # ------------------------------------------------------------------ full-size, every element
-def full_layer_check(w, method, workers=16):
+def full_layer_check(w, method, workers=16, per_window=True):
     """The whole layer of workload w on the GPU with canonical-order I/O (the
     launch the benchmark times), compared with the oracle over EVERY window
     and head, element by element at the bf16 bar, and the complete text mean
@@ -326,7 +347,8 @@ def full_layer_check(w, method, workers=16):
     log(f"  generating {w.name} inputs")
     inp = I.qkv(w, bits_only=True)
     d = upload(inp, "bf16")
-    out, txt = W.window_attn(wp, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"], canonical=True)
+    out, txt = W.window_attn(wp, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"], canonical=True,
+                             per_window=per_window)
     torch.cuda.synchronize()
     got = dev_bits(out).reshape(w.n_tokens, w.heads, w.head_dim)
     got_txt = from_dev(txt)
@@ -359,7 +381,8 @@ def full_layer_check(w, method, workers=16):
     tsum = np.zeros((w.text_len, w.heads, w.head_dim))
     for r in res:       # window order
         tsum += r[2]
-    log(f"  {w.name} {method}: {op.n_windows} windows x {w.heads} heads, worst element ratio {worst:.3f} "
+    log(f"  {w.name} {method} ({'per-window' if per_window else 'chunked'} text): "
+        f"{op.n_windows} windows x {w.heads} heads, worst element ratio {worst:.3f} "
         f"(bar 1), worst rel-L2 {worst_rel:.3e} (bar {BF16_REL_L2}); oracle {time.time() - t0:.1f} s")
     assert worst <= 1.0, f"element error exceeds 3e-2 + 2e-2*|ref| (ratio {worst})"
     assert worst_rel <= BF16_REL_L2, f"relative L2 error {worst_rel}"
@@ -368,14 +391,17 @@ def full_layer_check(w, method, workers=16):
 
 @pytest.mark.timeout(900)
 def test_720p_regular_full(gpu):
-    full_layer_check(I.WORKLOADS["720p_bf16"], "regular")
+    """Minimum workspace: 36 windows in 16 chunks of two or three."""
+    full_layer_check(I.WORKLOADS["720p_bf16"], "regular", per_window=False)
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("method", ["regular", "shifted"])
-def test_1080p_full(gpu, method):
-    """Both layers of the benchmark's step, every output element."""
-    full_layer_check(I.WORKLOADS["1080p_bf16"], method)
+@pytest.mark.parametrize("method,per_window", [("regular", True), ("shifted", True), ("regular", False)],
+                         ids=["regular", "shifted", "regular_chunked_text"])
+def test_1080p_full(gpu, method, per_window):
+    """Both layers of the benchmark's step, every output element (and the
+    regular layer again with the minimum workspace)."""
+    full_layer_check(I.WORKLOADS["1080p_bf16"], method, per_window=per_window)
 
 
 @pytest.mark.timeout(900)

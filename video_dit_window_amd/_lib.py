@@ -209,20 +209,29 @@ def linear(x, w, residual=None, out=None, stream=None):
     return out
 
 
-def window_attn_workspace(p: Plan, n_heads, head_dim, text_len, dtype) -> int:
+def window_attn_workspace(p: Plan, n_heads, head_dim, text_len, dtype, per_window=False) -> int:
+    """Workspace bytes of window_attn: the minimum the call accepts (float32
+    text sums of min(n_windows, 16) chunks), or with per_window=True the size
+    that selects one text partial per window (n_windows chunks: each text
+    item then shares its window's K/V in L2 with the video items; faster)."""
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     b = ctypes.c_size_t()
     _check("wsp_window_attn_workspace",
            lib().wsp_window_attn_workspace(p.handle, n_heads, head_dim, text_len, code, ctypes.byref(b)))
+    if per_window:
+        return p.n_windows * text_len * n_heads * head_dim * 4
     return b.value
 
 
 def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None, out=None, txt_out=None,
-                workspace=None, stream=None, canonical=False):
+                workspace=None, stream=None, canonical=False, per_window=True):
     """Joint window attention; returns (out [N,H,D], txt_out [Lt,H,D]).
 
     canonical=True: q, k, v and out rows are in canonical token order (the
-    layout permutation happens inside the kernel, wsp_window_attn_ex)."""
+    layout permutation happens inside the kernel, wsp_window_attn_ex).
+    Without a workspace, one is allocated: per_window=True sizes it for one
+    text partial per window (the faster text reduction), False for the
+    minimum (16 chunks of windows)."""
     torch = _torch()
     N, Hh, D = q.shape
     Lt = txt_q.shape[0]
@@ -235,7 +244,7 @@ def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None, out=None, txt
             raise ValueError(f"{name} must match txt_q in shape and q in dtype")
     if txt_q.shape[1:] != (Hh, D) or N != p.n_tokens:
         raise ValueError("shapes do not match the plan / each other")
-    need = window_attn_workspace(p, Hh, D, Lt, code)
+    need = window_attn_workspace(p, Hh, D, Lt, code, per_window=per_window)
     with _on(stream):
         if out is None:
             out = torch.empty_like(q)
@@ -318,7 +327,7 @@ def fp8_quantize(x, amax, out=None, stream=None):
 
 
 def window_attn_qk8(p: Plan, q8, k8, v, txt_q8, txt_k8, txt_v, amax_q, amax_k, scale=None, out=None,
-                    txt_out=None, workspace=None, stream=None, canonical=False):
+                    txt_out=None, workspace=None, stream=None, canonical=False, per_window=True):
     """Window attention with E4M3 q / k codes and bf16 v (wsp_window_attn_qk8)."""
     torch = _torch()
     N, Hh, D = v.shape
@@ -327,7 +336,7 @@ def window_attn_qk8(p: Plan, q8, k8, v, txt_q8, txt_k8, txt_v, amax_q, amax_k, s
         raise ValueError("q8 / k8 must be uint8 codes shaped like v")
     if v.dtype != torch.bfloat16 or txt_v.dtype != torch.bfloat16:
         raise ValueError("v and txt_v must be bfloat16")
-    need = window_attn_workspace(p, Hh, D, Lt, BF16)
+    need = window_attn_workspace(p, Hh, D, Lt, BF16, per_window=per_window)
     with _on(stream):
         if out is None:
             out = torch.empty_like(v)

@@ -162,8 +162,8 @@ int device_windows(wsp_plan_t &p, int dev, bool gather, WinDesc **out) {
 }
 
 int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order, bool gather,
-                 ItemDesc **out, int *count) {
-    const auto key = std::make_tuple(n_heads, text_len, bm, order, int(gather));
+                 int n_chunks, ItemDesc **out, int *count) {
+    const auto key = std::make_tuple(n_heads, text_len, bm, order, int(gather), n_chunks);
     {
         std::lock_guard<std::mutex> lk(p.mu);
         auto &m = p.dev[dev].items;
@@ -177,7 +177,7 @@ int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int 
     std::vector<ItemDesc> items;
     int rc;
     try {
-        rc = build_items(p, n_heads, text_len, bm, order, gather, items);
+        rc = build_items(p, n_heads, text_len, bm, order, gather, n_chunks, items);
     } catch (const std::bad_alloc &) {
         return fail(WSP_ENOMEM, "host allocation of the attention work list failed");
     }
@@ -356,6 +356,11 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
         // 2^31 / row_bytes <= 2^24 because row_bytes >= 128.
     }
     if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
+    // One text partial per window when the workspace holds them (each text
+    // item then shares its window's K/V with the video items in L2), else
+    // min(n_windows, 16) chunks.
+    const size_t per_part = size_t(text_len) * size_t(n_heads) * size_t(head_dim) * 4u;
+    const int n_chunks = workspace_bytes >= per_part * size_t(p->nwin) ? p->nwin : text_chunks(p->nwin);
     const int order = g_attn_order.load();
     // Short windows (joint sequences averaging < 1024 rows) take 128-row
     // query tiles: a window's partly empty last tile then wastes less.
@@ -371,7 +376,7 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
     WinDesc *wins = nullptr;
     int n_items = 0;
     int32_t *d_ids = nullptr, *d_rel = nullptr;
-    if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, gather, &items, &n_items))) return rc;
+    if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, gather, n_chunks, &items, &n_items))) return rc;
     if ((rc = device_windows(*p, dev, gather, &wins))) return rc;
     if (gather && dtype == WSP_BF16 && (rc = device_rel_ids(*p, dev, &d_rel))) return rc;
     if (gather && dtype != WSP_BF16 && (rc = device_ids(*p, dev, &d_ids))) return rc;
@@ -389,8 +394,7 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
                             text_len, scale, s);
     if (e != hipSuccess) return hip_fail(e, "window attention kernel launch");
     if (text_len > 0) {
-        e = launch_text_mean(ws, txt_out, int64_t(text_len) * n_heads * head_dim, text_chunks(p->nwin),
-                             p->nwin, dtype, s);
+        e = launch_text_mean(ws, txt_out, int64_t(text_len) * n_heads * head_dim, n_chunks, p->nwin, dtype, s);
         if (e != hipSuccess) return hip_fail(e, "text mean kernel launch");
     }
     return WSP_OK;

@@ -267,11 +267,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             }
         };
         auto kid = [&](const Ids &d, int i) { return Q8 ? d.k[i] : d.v[i]; };
-        // The window's video rows travel with cache policy CP: 0 for a video
-        // item, whose K/V the other query tiles of its group read from the
-        // same L2; non-temporal (2) for a text item, the only reader of that
-        // K/V on its XCD, so that streaming it does not evict the video
-        // groups' K/V.  Text rows (shared by every item) keep the default.
+        // The window's video rows travel with cache policy CP: 0 where other
+        // items of the same XCD read the same K/V from L2 (video items, and a
+        // text item of a single window, which runs beside that window's video
+        // items); non-temporal (2) for a text item over a chunk of several
+        // windows, the only reader of that K/V on its XCD, so that streaming
+        // it does not evict the video groups' K/V.  Text rows (shared by
+        // every item) keep the default.
         auto dma_cp = [&](auto cp_c, uint8_t LDS_AS *dst, int j, Ids &idp, Ids &idn) {
             constexpr int CP = decltype(cp_c)::value;
             if constexpr (GATHER) load_ids(idn, j + 1);
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             }
         };
         auto dma = [&](uint8_t LDS_AS *dst, int j, Ids &idp, Ids &idn) {
-            if (text) dma_cp(std::integral_constant<int, 2>{}, dst, j, idp, idn);
+            if (it.nwin > 1) dma_cp(std::integral_constant<int, 2>{}, dst, j, idp, idn);
             else dma_cp(std::integral_constant<int, 0>{}, dst, j, idp, idn);
         };
 

@@ -160,7 +160,7 @@ void window_descs(const wsp_plan_t &p, bool gather, std::vector<WinDesc> &wins) 
 }
 
 int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order, bool gather,
-                std::vector<ItemDesc> &items) {
+                int n_chunks, std::vector<ItemDesc> &items) {
     constexpr int kXcds = 8;
     constexpr int kKeyTile = 64;
     std::vector<WinDesc> wins;
@@ -178,39 +178,47 @@ int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int orde
         if (ceil_div(wins[size_t(w)].lw, bm) > 0xFFFF)
             return fail(WSP_ERANGE, "window " + std::to_string(w) + " needs more than 65535 query tiles");
 
-    // Groups of items that read the same K/V: all query tiles of a (window,
-    // head), and all text query tiles of a (chunk, head); with their cost.
+    // Groups of items that read the same K/V: all video query tiles of a
+    // (window, head), with that window's text items when every chunk is a
+    // single window; otherwise all text query tiles of a (chunk, head) form
+    // a group of their own.  Each group has a cost in key tiles.
     struct Group {
         int64_t cost;
         std::vector<ItemDesc> items;
     };
-    std::vector<Group> tgroups, vgroups;
-    if (text_len > 0) {
-        const int G = text_chunks(p.nwin);
+    const int G = text_len > 0 ? n_chunks : 0;
+    const bool per_window = G == p.nwin;
+    auto text_items = [&](int c, int h, std::vector<ItemDesc> &out) {
+        const int w0 = chunk_begin(c, p.nwin, G), w1 = chunk_begin(c + 1, p.nwin, G);
+        for (int64_t t = 0; t < text_tiles; ++t) {
+            ItemDesc d{};
+            d.w = w0;
+            d.hq = (h << 16) | int(t);
+            d.nwin = w1 - w0;
+            d.chunk = c;
+            out.push_back(d);
+        }
+    };
+    std::vector<Group> groups;
+    if (G > 0 && !per_window) {
         for (int c = 0; c < G; ++c) {
-            const int w0 = chunk_begin(c, p.nwin, G), w1 = chunk_begin(c + 1, p.nwin, G);
             int64_t cost = 0;
-            for (int w = w0; w < w1; ++w) cost += key_tiles(w);
+            for (int w = chunk_begin(c, p.nwin, G); w < chunk_begin(c + 1, p.nwin, G); ++w) cost += key_tiles(w);
             for (int h = 0; h < n_heads; ++h) {
                 Group g{cost * text_tiles, {}};
-                for (int64_t t = 0; t < text_tiles; ++t) {
-                    ItemDesc d{};
-                    d.w = w0;
-                    d.hq = (h << 16) | int(t);
-                    d.nwin = w1 - w0;
-                    d.chunk = c;
-                    g.items.push_back(d);
-                }
-                tgroups.push_back(std::move(g));
+                text_items(c, h, g.items);
+                groups.push_back(std::move(g));
             }
         }
-        std::stable_sort(tgroups.begin(), tgroups.end(),
+        // a text item covers a whole chunk of windows (several times a video
+        // item): those groups go first, largest first
+        std::stable_sort(groups.begin(), groups.end(),
                          [](const Group &a, const Group &b) { return a.cost > b.cost; });
     }
     for (int32_t w : worder) {
         const int64_t tiles = ceil_div(wins[size_t(w)].lw, bm);
         for (int h = 0; h < n_heads; ++h) {
-            Group g{tiles * key_tiles(w), {}};
+            Group g{(tiles + (per_window ? text_tiles : 0)) * key_tiles(w), {}};
             for (int64_t t = 0; t < tiles; ++t) {
                 ItemDesc d{};
                 d.w = w;
@@ -218,49 +226,26 @@ int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int orde
                 d.win = wins[size_t(w)];
                 g.items.push_back(d);
             }
-            vgroups.push_back(std::move(g));
+            if (per_window) text_items(w, h, g.items);
+            groups.push_back(std::move(g));
         }
     }
-    // A text item covers a whole chunk of windows (several times a video
-    // item) and reads K/V that no other item on its XCD shares, so text
-    // groups are spread evenly over the first half of the video groups of
-    // their list instead of all starting together: early enough to finish
-    // well before the end, without every CU streaming unshared K/V at once.
-    auto merge = [](const std::vector<const Group *> &tg, const std::vector<const Group *> &vg,
-                    std::vector<ItemDesc> &outl) {
-        const size_t nt = tg.size(), nv = vg.size();
-        size_t ti = 0;
-        for (size_t vi = 0; vi <= nv; ++vi) {
-            while (ti < nt && (nv == 0 || ti * (nv / 2 + 1) <= vi * nt)) {
-                outl.insert(outl.end(), tg[ti]->items.begin(), tg[ti]->items.end());
-                ++ti;
-            }
-            if (vi < nv) outl.insert(outl.end(), vg[vi]->items.begin(), vg[vi]->items.end());
-        }
-    };
     items.clear();
     if (order != WSP_ORDER_LPT_XCD) {
-        std::vector<const Group *> tg, vg;
-        for (const Group &g : tgroups) tg.push_back(&g);
-        for (const Group &g : vgroups) vg.push_back(&g);
-        merge(tg, vg, items);
+        for (const Group &g : groups) items.insert(items.end(), g.items.begin(), g.items.end());
         return int(items.size());
     }
     // Work groups are handed to the XCDs round-robin by block index, so block
     // b runs on XCD b % 8.  Each group -- whose items all read the same K/V --
-    // goes whole to the least-loaded XCD (text groups first, then video
-    // groups largest first), and each XCD's list is merged as above.
-    std::vector<std::vector<const Group *>> tl(kXcds), vl(kXcds);
-    std::vector<int64_t> load(kXcds, 0);
-    auto place = [&](const Group &g, std::vector<std::vector<const Group *>> &l) {
-        const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
-        l[size_t(x)].push_back(&g);
-        load[size_t(x)] += g.cost;
-    };
-    for (const Group &g : tgroups) place(g, tl);
-    for (const Group &g : vgroups) place(g, vl);
+    // goes whole to the least-loaded XCD, in list order, and each XCD's list
+    // keeps that order.
     std::vector<std::vector<ItemDesc>> lists(kXcds);
-    for (int x = 0; x < kXcds; ++x) merge(tl[size_t(x)], vl[size_t(x)], lists[size_t(x)]);
+    std::vector<int64_t> load(kXcds, 0);
+    for (const Group &g : groups) {
+        const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
+        lists[size_t(x)].insert(lists[size_t(x)].end(), g.items.begin(), g.items.end());
+        load[size_t(x)] += g.cost;
+    }
     size_t longest = 0;
     for (auto &l : lists) longest = std::max(longest, l.size());
     ItemDesc idle{};

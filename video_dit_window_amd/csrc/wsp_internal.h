@@ -16,10 +16,13 @@
 namespace wsp {
 
 // Text outputs are reduced over windows in fixed chunks: the windows of a
-// plan split into min(n_windows, kTextChunks) runs of consecutive ids, each
-// summed (float32, id order) into one partial of the workspace by the text
-// work items, and the partials are added in chunk order by the text-mean
-// kernel.
+// plan split into G runs of consecutive ids, each summed (float32, id order)
+// into one partial of the workspace by the text work items, and the partials
+// are added in chunk order by the text-mean kernel.  G is
+// min(n_windows, kTextChunks) (the workspace every call accepts), or
+// n_windows -- one partial per window -- when the caller's workspace holds
+// that many: each text item then covers a single window and runs beside that
+// window's video items, sharing their K/V in L2.
 constexpr int kTextChunks = 16;
 inline int text_chunks(int n_windows) { return n_windows < kTextChunks ? n_windows : kTextChunks; }
 // First window of chunk c (chunk c covers windows chunk_begin(c) ..
@@ -62,8 +65,8 @@ struct DeviceTables {
     int32_t *pos = nullptr;                                     // [n_tokens] window positions
     WinDesc *wins[2] = {nullptr, nullptr};                      // [n_windows] layout / canonical order
     std::map<std::tuple<int, int, int, int>, int32_t *> perm;   // src layout -> perm
-    // (H, Lt, BM, order, canonical-order I/O) -> work list
-    std::map<std::tuple<int, int, int, int, int>, std::pair<ItemDesc *, int>> items;
+    // (H, Lt, BM, order, canonical-order I/O, text chunks) -> work list
+    std::map<std::tuple<int, int, int, int, int, int>, std::pair<ItemDesc *, int>> items;
 };
 
 }  // namespace wsp
@@ -105,7 +108,7 @@ void window_descs(const wsp_plan_t &p, bool gather, std::vector<WinDesc> &wins);
 // every (chunk, head, text tile)), ordered for dispatch; returns its length
 // or a negative status.
 int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order, bool gather,
-                std::vector<ItemDesc> &items);
+                int n_chunks, std::vector<ItemDesc> &items);
 
 // ---- device tables (abi.cpp) ----------------------------------------------
 int device_offsets(wsp_plan_t &p, int dev, int32_t **out);
@@ -115,7 +118,7 @@ int device_positions(wsp_plan_t &p, int dev, int32_t **out);
 int device_rel_ids(wsp_plan_t &p, int dev, int32_t **out);
 int device_windows(wsp_plan_t &p, int dev, bool gather, WinDesc **out);
 int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order, bool gather,
-                 ItemDesc **out, int *count);
+                 int n_chunks, ItemDesc **out, int *count);
 
 // ---- kernel launchers -------------------------------------------------------
 // relayout.hip

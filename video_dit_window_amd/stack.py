@@ -43,7 +43,8 @@ class Stack:
         self.X = [torch.empty((rows, self.E), dtype=bf16, device=device) for _ in range(1 if canonical_io else 2)]
         self.q, self.k, self.v, self.A = (torch.empty((rows, self.E), dtype=bf16, device=device)
                                           for _ in range(4))
-        need = max(L.window_attn_workspace(p, heads, head_dim, text_len, L.BF16) for p in self.layouts)
+        need = max(L.window_attn_workspace(p, heads, head_dim, text_len, L.BF16, per_window=True)
+                   for p in self.layouts)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
 
     def layout(self, l):
