@@ -241,6 +241,36 @@ int wsp_window_attn_ex(const wsp_plan_t *p, const void *q, const void *k, const 
                        void *stream);
 
 /*
+ * wsp_window_attn_noalloc -- wsp_window_attn_ex for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same kernels and results, bit for bit;
+ * it calls no hipMalloc, hipFree or allocating routine:
+ *   - the text mean's float32 partials go to a fixed scratch array of 96 MiB
+ *     that the library holds on each GPU it runs on until the process ends.
+ *     One partial per window when those fit (n_windows * text_len * n_heads
+ *     * head_dim * 4 bytes <= 96 MiB, e.g. the 720p-shaped layer), else
+ *     min(n_windows, 16) chunk partials (42 MB for the 1080p-shaped layer,
+ *     84 MB for the 4K-shaped one); a larger need returns WSP_ERANGE;
+ *   - the plan's device tables must already be on the device: a call of
+ *     wsp_window_attn_ex with the same plan, n_heads, head_dim, text_len,
+ *     dtype and flags, the same wsp_set_attn_order / _schedule setting and a
+ *     workspace selecting the same text reduction uploads them; without one
+ *     this call returns WSP_EINVAL and launches nothing.  The first call on
+ *     a device also looks up the scratch array's device address once
+ *     (hipGetSymbolAddress).
+ * Every call on one GPU shares that GPU's scratch array: calls that overlap
+ * in time on one GPU (different streams, or host threads) race and must be
+ * ordered by the caller.  The kernels write every scratch element they read
+ * within the call, so nothing needs clearing between calls.
+ * Arguments as wsp_window_attn_ex without the workspace; errors as
+ * wsp_window_attn_ex plus the two above.
+ */
+int wsp_window_attn_noalloc(const wsp_plan_t *p, const void *q, const void *k, const void *v,
+                            const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                            int head_dim, int text_len, int dtype, float scale, unsigned flags,
+                            void *out, void *txt_out, void *stream);
+
+/*
  * wsp_rope_relayout -- window-local 3D rotary position embedding, fused with
  * the row move between two layouts (for q and k; v takes wsp_relayout).
  *

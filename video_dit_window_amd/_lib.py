@@ -37,6 +37,8 @@ _SIGNATURES = {
                                                 _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "wsp_window_attn_ex": (_c_int, [_c_vp] * 7 + [_c_int, _c_int, _c_int, _c_int, ctypes.c_float,
                                                    ctypes.c_uint, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "wsp_window_attn_noalloc": (_c_int, [_c_vp] * 7 + [_c_int, _c_int, _c_int, _c_int, ctypes.c_float,
+                                                        ctypes.c_uint, _c_vp, _c_vp, _c_vp]),
     "wsp_rope_relayout": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_int,
                                    ctypes.c_float, _c_vp]),
     "wsp_rope_text": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _c_vp]),
@@ -261,6 +263,35 @@ def window_attn(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None, out=None, txt
         IO_CANONICAL if canonical else IO_LAYOUT,
         _dev_ptr(out, "out"), tp[3], _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)))
     return out, txt_out
+
+
+def window_attn_noalloc(p: Plan, q, k, v, txt_q, txt_k, txt_v, out, txt_out, scale=None, stream=None,
+                        canonical=False):
+    """wsp_window_attn_noalloc: window_attn without a workspace (the library's
+    fixed scratch array) and without uploading anything; the plan's tables
+    must be resident from an earlier window_attn call with the same
+    arguments and the same text reduction (one partial per window when
+    those fit in the scratch array, else 16 chunks: window_attn with
+    per_window=noalloc_per_window(...)).  out and txt_out are the caller's."""
+    N, Hh, D = q.shape
+    Lt = txt_q.shape[0]
+    if out.shape != q.shape or out.dtype != q.dtype or txt_out.shape != txt_q.shape or txt_out.dtype != q.dtype:
+        raise ValueError("out / txt_out must match q / txt_q")
+    if N != p.n_tokens or txt_q.shape[1:] != (Hh, D):
+        raise ValueError("shapes do not match the plan / each other")
+    tp = [(_dev_ptr(t, n) if Lt else _c_vp(0)) for n, t in
+          (("txt_q", txt_q), ("txt_k", txt_k), ("txt_v", txt_v), ("txt_out", txt_out))]
+    _check("wsp_window_attn_noalloc", lib().wsp_window_attn_noalloc(
+        p.handle, _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), tp[0], tp[1], tp[2],
+        Hh, D, Lt, _dtype_code(q.dtype), ctypes.c_float(0.0 if scale is None else float(scale)),
+        IO_CANONICAL if canonical else IO_LAYOUT, _dev_ptr(out, "out"), tp[3], _stream(stream)))
+    return out, txt_out
+
+
+def noalloc_per_window(p: Plan, n_heads, head_dim, text_len) -> bool:
+    """Whether wsp_window_attn_noalloc reduces the text with one partial per
+    window (they fit in its 96 MiB scratch) rather than in 16 chunks."""
+    return p.n_windows * text_len * n_heads * head_dim * 4 <= (96 << 20)
 
 
 def rope_relayout(x, src: Plan, dst: Plan, pos: Plan, text_len, theta=None, out=None, stream=None):

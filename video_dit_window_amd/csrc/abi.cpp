@@ -314,12 +314,69 @@ int wsp_window_attn(const wsp_plan_t *pc, const void *q, const void *k, const vo
 
 namespace {
 
-// Shared body of wsp_window_attn_ex (q8 = false) and wsp_window_attn_qk8.
+// ---- the no-allocation entry point's scratch --------------------------------
+// Float32 text partials for wsp_window_attn_noalloc: a file-scope device array
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never passes the array's name to a kernel: its device address
+// comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(96) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void *> g_scratch_ptr;  // device ordinal -> device address of `scratch`
+
+int scratch_address(int dev, void **out) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress of the scratch array");
+        }
+        it = g_scratch_ptr.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return WSP_OK;
+}
+
+// Device tables of one attention call, looked up only (nothing is uploaded
+// or allocated): the no-allocation entry point runs on tables that a call of
+// wsp_window_attn_ex with the same plan and shape left on the device.
+int resident_tables(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order, bool gather,
+                    int n_chunks, bool bf16, ItemDesc **items, int *n_items, WinDesc **wins, int32_t **ids,
+                    int32_t **rel) {
+    std::lock_guard<std::mutex> lk(p.mu);
+    auto d = p.dev.find(dev);
+    if (d != p.dev.end()) {
+        DeviceTables &t = d->second;
+        auto it = t.items.find(std::make_tuple(n_heads, text_len, bm, order, int(gather), n_chunks));
+        WinDesc *w = t.wins[gather ? 1 : 0];
+        const bool have_ids = !gather || (bf16 ? t.rel != nullptr : t.ids != nullptr);
+        if (it != t.items.end() && w && have_ids) {
+            *items = it->second.first;
+            *n_items = it->second.second;
+            *wins = w;
+            *ids = gather && !bf16 ? t.ids : nullptr;
+            *rel = gather && bf16 ? t.rel : nullptr;
+            return WSP_OK;
+        }
+    }
+    return fail(WSP_EINVAL,
+                "the plan's device tables for this head count, text length, dtype, I/O order, schedule and "
+                "text reduction are not on this device: call wsp_window_attn_ex once with the same arguments "
+                "first (it uploads them; wsp_window_attn_noalloc allocates nothing)");
+}
+
+// Shared body of wsp_window_attn_ex (q8 = false), wsp_window_attn_qk8 and
+// wsp_window_attn_noalloc (no_alloc: resident tables, the scratch array as
+// workspace).
 int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const void *v,
                      const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
                      int head_dim, int text_len, int dtype, bool q8, const float *amax_q,
                      const float *amax_k, float scale, unsigned flags, void *out, void *txt_out,
-                     void *workspace, size_t workspace_bytes, void *stream) {
+                     void *workspace, size_t workspace_bytes, void *stream, bool no_alloc = false) {
     if (flags & ~unsigned(WSP_ATTN_IO_CANONICAL)) return fail(WSP_EINVAL, "unknown attention flags");
     const bool gather = (flags & WSP_ATTN_IO_CANONICAL) != 0;
     size_t need = 0;
@@ -336,10 +393,18 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
             if (!ptr) return fail(WSP_EINVAL, "text tensors and txt_out must be non-NULL when text_len > 0");
             if (!aligned16(ptr)) return fail(WSP_EINVAL, "text tensors must be 16-byte aligned");
         }
-        if (!workspace || workspace_bytes < need)
-            return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) +
-                                            " bytes required, got " + std::to_string(workspace_bytes));
-        if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
+        if (no_alloc) {
+            if (need > kScratchBytes)
+                return fail(WSP_ERANGE, "wsp_window_attn_noalloc: the text mean needs " + std::to_string(need) +
+                                            " bytes of scratch, more than its fixed " +
+                                            std::to_string(kScratchBytes) + " (use wsp_window_attn_ex)");
+            workspace_bytes = kScratchBytes;
+        } else {
+            if (!workspace || workspace_bytes < need)
+                return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) +
+                                                " bytes required, got " + std::to_string(workspace_bytes));
+            if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
+        }
     }
     // The matrix-core kernel addresses a window's video rows (canonical
     // order: the rows between its smallest and largest canonical id) and the
@@ -376,10 +441,18 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
     WinDesc *wins = nullptr;
     int n_items = 0;
     int32_t *d_ids = nullptr, *d_rel = nullptr;
-    if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, gather, n_chunks, &items, &n_items))) return rc;
-    if ((rc = device_windows(*p, dev, gather, &wins))) return rc;
-    if (gather && dtype == WSP_BF16 && (rc = device_rel_ids(*p, dev, &d_rel))) return rc;
-    if (gather && dtype != WSP_BF16 && (rc = device_ids(*p, dev, &d_ids))) return rc;
+    if (no_alloc) {
+        if ((rc = resident_tables(*p, dev, n_heads, text_len, bm, order, gather, n_chunks, dtype == WSP_BF16,
+                                  &items, &n_items, &wins, &d_ids, &d_rel)))
+            return rc;
+        if (text_len > 0 && (rc = scratch_address(dev, &workspace))) return rc;
+    } else {
+        if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, gather, n_chunks, &items, &n_items)))
+            return rc;
+        if ((rc = device_windows(*p, dev, gather, &wins))) return rc;
+        if (gather && dtype == WSP_BF16 && (rc = device_rel_ids(*p, dev, &d_rel))) return rc;
+        if (gather && dtype != WSP_BF16 && (rc = device_ids(*p, dev, &d_ids))) return rc;
+    }
     hipStream_t s = hipStream_t(stream);
     float *ws = static_cast<float *>(workspace);
     hipError_t e;
@@ -546,6 +619,15 @@ int wsp_fp8_quantize(const void *x, void *y, int64_t n_rows, int n_heads, int he
     hipError_t e = launch_fp8_quantize(x, y, amax, n_rows, n_heads, head_dim, dtype, hipStream_t(stream));
     if (e != hipSuccess) return hip_fail(e, "fp8 quantize kernel launch");
     return WSP_OK;
+}
+
+int wsp_window_attn_noalloc(const wsp_plan_t *pc, const void *q, const void *k, const void *v,
+                            const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                            int head_dim, int text_len, int dtype, float scale, unsigned flags,
+                            void *out, void *txt_out, void *stream) {
+    g_last_error.clear();
+    return window_attn_impl(pc, q, k, v, txt_q, txt_k, txt_v, n_heads, head_dim, text_len, dtype, false,
+                            nullptr, nullptr, scale, flags, out, txt_out, nullptr, 0, stream, true);
 }
 
 int wsp_window_attn_qk8(const wsp_plan_t *pc, const void *q8, const void *k8, const void *v,
