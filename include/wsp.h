@@ -319,6 +319,48 @@ int wsp_rope_text(const void *x, void *y, int text_len, int n_heads, int head_di
                   float theta, void *stream);
 
 /*
+ * wsp_window_attn_rope -- window attention of rotated queries and keys:
+ * wsp_window_attn_ex's result for q, k rotated as wsp_rope_relayout (src =
+ * dst = pos = p, or canonical order with pos = p) and txt_q, txt_k rotated
+ * as wsp_rope_text would rotate them -- bit for bit.  The video queries turn
+ * inside the attention kernel as each work item loads them; k is rotated
+ * once by the stand-alone rotation kernel into the workspace (every query
+ * tile of a window reads each key row, so rotating keys on the kernel's
+ * loads would repeat the work per query tile), the text rows likewise.
+ * q, k, txt_q and txt_k are left untouched.
+ *
+ * "Window-Aligned Sequence Parallelism (SeedVR2)", section "Reference quirks
+ * reproduced on purpose" (window-local axial indices, temporal index raised
+ * by text_len); section "SeedVR2 integration" (attention over [video window;
+ * text]); the readings of wsp_rope_relayout (axis blocks, pair layout, theta).
+ *
+ * Arguments as wsp_window_attn_ex, plus theta (rotary base; <= 0 or
+ * non-finite: 10000).  dtype must be WSP_BF16 and head_dim 128.
+ * workspace  device, >= wsp_window_attn_rope_workspace() bytes, 16-byte
+ *            aligned, never NULL: the rotated k (n_tokens * n_heads * 128 *
+ *            2 bytes), text q and text k (text_len * n_heads * 128 * 2 bytes
+ *            each), each part rounded up to 256, then the float32 text
+ *            partials as in wsp_window_attn_ex (one per window when the rest
+ *            holds text_len * n_heads * 128 * 4 bytes per window, else
+ *            min(n_windows, 16) chunks).
+ * Errors: as wsp_window_attn_ex; WSP_EINVAL for another dtype or head_dim;
+ * WSP_ERANGE for window extents beyond 1024 (t) / 2048 (h, w).
+ */
+int wsp_window_attn_rope(const wsp_plan_t *p, const void *q, const void *k, const void *v,
+                         const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                         int head_dim, int text_len, int dtype, float scale, float theta, unsigned flags,
+                         void *out, void *txt_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * wsp_window_attn_rope_workspace -- the smallest workspace (bytes) of
+ * wsp_window_attn_rope: wsp_window_attn_workspace's plus the rotated k,
+ * text q and text k.  Errors: as wsp_window_attn_workspace; WSP_EINVAL
+ * unless dtype is WSP_BF16 and head_dim 128.
+ */
+int wsp_window_attn_rope_workspace(const wsp_plan_t *p, int n_heads, int head_dim, int text_len, int dtype,
+                                   size_t *bytes);
+
+/*
  * wsp_fp8_amax -- per-head largest |x| of a [n_rows, n_heads, head_dim]
  * tensor, max-accumulated into amax[n_heads] (float32, device memory; the
  * caller zeroes it before the first call, then may accumulate several
@@ -411,7 +453,7 @@ const char *wsp_last_error(void);
 /* wsp_version -- ABI version of this header (major*10000 + minor*100 + patch). */
 int wsp_version(void);
 
-#define WSP_VERSION 20000
+#define WSP_VERSION 20100
 
 #ifdef __cplusplus
 }

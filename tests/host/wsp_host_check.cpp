@@ -43,7 +43,7 @@ int fp8_max_row_chunks() { return 2048; }
 hipError_t launch_relayout(const void *, void *, const int32_t *, int64_t, int64_t, hipStream_t) { reached("relayout"); }
 hipError_t launch_attn_bf16(int, bool, bool, const void *, const void *, const void *, const void *, const void *,
                             const void *, void *, float *, const int32_t *, const ItemDesc *, const WinDesc *, int,
-                            const float *, const float *, int, int, float, hipStream_t) {
+                            const float *, const float *, const RopeTables *, int, int, float, hipStream_t) {
     reached("attn_bf16");
 }
 hipError_t launch_attn_f32(int, const float *, const float *, const float *, const float *, const float *,
@@ -240,6 +240,24 @@ static void check_arguments() {
           WSP_EINVAL);
     CHECK(wsp_window_attn_qk8(p, a, b, c, a, b, c, nullptr, am, 4, 128, 16, 0.f, 0, o, o, nullptr, 0,
                               nullptr) == WSP_EINVAL);
+    // attention with in-kernel rotary embedding
+    size_t wr = 0;
+    CHECK(wsp_window_attn_rope_workspace(p, 4, 128, 16, WSP_BF16, &wr) == WSP_OK);
+    CHECK(wsp_window_attn_workspace(p, 4, 128, 16, WSP_BF16, &ws) == WSP_OK);
+    CHECK(wr == ws + 3600 * 4 * 128 * 2 + 2 * 16 * 4 * 128 * 2);  // rotated k, text q, text k (bf16)
+    CHECK(wsp_window_attn_rope_workspace(p, 4, 64, 16, WSP_BF16, &wr) == WSP_EINVAL);
+    CHECK(wsp_window_attn_rope_workspace(p, 4, 128, 16, WSP_F32, &wr) == WSP_EINVAL);
+    auto rattn = [&](wsp_plan_t *pl, void *w, size_t wb, int D, int dt) {
+        return wsp_window_attn_rope(pl, a, b, c, a, b, c, 4, D, 16, dt, 0.f, 0.f, 1, o, o, w, wb, nullptr);
+    };
+    CHECK(rattn(p, buf[3], 0, 64, WSP_BF16) == WSP_EINVAL);
+    CHECK(rattn(p, buf[3], 0, 128, WSP_F32) == WSP_EINVAL);
+    CHECK(rattn(p, buf[3], 16, 128, WSP_BF16) == WSP_EWORKSPACE);
+    CHECK(rattn(p, buf[3], ws, 128, WSP_BF16) == WSP_EWORKSPACE);  // partials only, no room for the rotated rows
+    wsp_plan_t *tall = nullptr;                                     // windows 3286 rows high: beyond 2048
+    CHECK(wsp_plan(2, 6000, 2, 1, 1, 1, WSP_REGULAR, &tall) == WSP_OK);
+    CHECK(rattn(tall, buf[3], 0, 128, WSP_BF16) == WSP_ERANGE);
+    wsp_plan_free(tall);
     // rope, fp8, linear, options
     CHECK(wsp_rope_relayout(a, b, 4, 64, WSP_BF16, p, p, p, 0, 0.f, nullptr) == WSP_EINVAL);
     CHECK(wsp_rope_relayout(a, b, 4, 128, WSP_BF16, p, p, other, 0, 0.f, nullptr) == WSP_EINVAL);

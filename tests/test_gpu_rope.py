@@ -139,3 +139,110 @@ def test_rope_relayout_1080p_sampled(gpu):
     cids = osh.ids[rows]
     ref = O.rope(I.bf16_bits_to_f32(bits[cids]).astype(np.float64), pos[cids])
     check_rot(from_dev(y[torch.from_numpy(rows).cuda()]), ref, "bf16", "1080p sampled rows")
+
+
+# ---- rotation inside the attention kernel (wsp_window_attn_rope) -----------
+
+def rope_chain(g, lay, d, Lt, canonical, theta=None, per_window=True):
+    """The unfused reference path on the device: stand-alone rotation of
+    q, k (into the layout, or in canonical order for layout `lay`) and of the
+    text q, k, then window attention with the same I/O order."""
+    src = g["canonical"] if canonical else g[lay]
+    q = W.rope_relayout(d["q"], src, src, g[lay], Lt, theta=theta)
+    k = W.rope_relayout(d["k"], src, src, g[lay], Lt, theta=theta)
+    tq, tk = W.rope_text(d["txt_q"], theta=theta), W.rope_text(d["txt_k"], theta=theta)
+    return W.window_attn(g[lay], q, k, d["v"], tq, tk, d["txt_v"], canonical=canonical, per_window=per_window)
+
+
+FUSED = [("rope_fused_mid", 6, 30, 52, 2, 3, 3, 3, 40), ("rope_fused_notext", 5, 20, 36, 2, 3, 3, 2, 0),
+         ("rope_fused_ragged", 7, 33, 41, 3, 2, 3, 2, 77), ("rope_fused_onewin", 3, 12, 20, 1, 1, 1, 2, 19)]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
+@pytest.mark.parametrize("method", ["regular", "shifted"])
+@pytest.mark.parametrize("canonical", [True, False], ids=["canonical_io", "layout_io"])
+def test_fused_rope_attention_bit_identical(gpu, case, method, canonical):
+    """wsp_window_attn_rope equals rope_relayout / rope_text followed by
+    window attention bit for bit: the kernel rotates with the same table,
+    the same float32 steps and one bf16 rounding, and runs the same
+    per-wavefront attention arithmetic."""
+    import torch
+    name, T, H, Wd, nt, nh, nw, heads, Lt = case
+    w = I.custom(name, T, H, Wd, nt, nh, nw, heads, 128, Lt, "bf16", std=1.0, index=540 + FUSED.index(case))
+    o, g = plans(w)
+    inp = I.qkv(w)
+    d = {n: to_dev(v, b, "bf16") for n, (v, b) in inp.items()}
+    if not canonical:  # layout-order inputs
+        d = {n: (W.relayout(t, g["canonical"], g[method]) if n in ("q", "k", "v") else t) for n, t in d.items()}
+    out, txt = W.window_attn_rope(g[method], d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"],
+                                  canonical=canonical)
+    ref, rtxt = rope_chain(g, method, d, Lt, canonical)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"{name} {method}: video"
+    if Lt:
+        assert torch.equal(txt.view(torch.int16), rtxt.view(torch.int16)), f"{name} {method}: text mean"
+
+
+@pytest.mark.parametrize("method", ["regular", "shifted"])
+def test_fused_rope_attention_oracle(gpu, method):
+    """Canonical-order layer with RoPE in the kernel against the oracle's
+    rotation (float64, window-local positions, rounded to bf16 as the device
+    rounds rotated q / k) and float64 attention, element by element."""
+    import torch
+    w = I.custom("rope_fused_oracle", 6, 30, 52, 2, 3, 3, 3, 128, 40, "bf16", std=1.0, index=550)
+    o, g = plans(w)
+    inp = I.qkv(w)
+    d = {n: to_dev(v, b, "bf16") for n, (v, b) in inp.items()}
+    out, txt = W.window_attn_rope(g[method], d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"])
+    torch.cuda.synchronize()
+    h = {n: I.bf16_bits_to_f32(inp[n][1]).astype(np.float64) for n in I.QKV_NAMES}
+    c, p = o["canonical"], o[method]
+    r16 = lambda x: I.bf16_bits_to_f32(I.f32_to_bf16_bits(x)).astype(np.float64)
+    rq = r16(O.rope_relayout(h["q"], c, p, p, w.text_len))
+    rk = r16(O.rope_relayout(h["k"], c, p, p, w.text_len))
+    tp = O.text_positions(w.text_len)
+    ref_out, ref_txt = O.window_attn(p, rq, rk, O.relayout(h["v"], c, p), r16(O.rope(h["txt_q"], tp)),
+                                     r16(O.rope(h["txt_k"], tp)), h["txt_v"])
+    check_bf16(from_dev(out), O.relayout(ref_out, p, c), f"fused rope attention {method} video")
+    check_bf16(from_dev(txt), ref_txt, f"fused rope attention {method} text mean")
+
+
+def test_fused_rope_theta_and_workspace(gpu):
+    """A non-default rotary base reaches the kernel's table (fused == chain
+    with theta 500, != the default), and with the minimum workspace (text
+    sums in 16 chunks) the fused call still equals the chain run with the
+    same text reduction."""
+    import torch
+    w = I.custom("rope_fused_theta", 6, 30, 52, 2, 3, 3, 2, 128, 40, "bf16", std=1.0, index=560)
+    o, g = plans(w)
+    d = {n: to_dev(v, b, "bf16") for n, (v, b) in I.qkv(w).items()}
+    args = (g["shifted"], d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"])
+    a, ta = W.window_attn_rope(*args, theta=500.0)
+    b, tb = rope_chain(g, "shifted", d, w.text_len, True, theta=500.0)
+    c, tc = W.window_attn_rope(*args)
+    e, te = W.window_attn_rope(*args, theta=500.0, per_window=False)
+    f, tf = rope_chain(g, "shifted", d, w.text_len, True, theta=500.0, per_window=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(ta.view(torch.int16), tb.view(torch.int16))
+    assert not torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), e.view(torch.int16))
+    assert torch.equal(e.view(torch.int16), f.view(torch.int16))
+    assert torch.equal(te.view(torch.int16), tf.view(torch.int16))
+
+
+@pytest.mark.parametrize("method", ["regular", "shifted"])
+def test_fused_rope_attention_1080p(gpu, method):
+    """Full 1080p canonical-order layer in the benchmark's configuration:
+    fused rotation bit-identical to the stand-alone rotation + attention."""
+    import torch
+    w = I.WORKLOADS["1080p_bf16"]
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    g = {"canonical": W.canonical(*geo[:3]), method: W.Plan(*geo, METH[method][1])}
+    log(f"  generating 1080p q, k, v ({method})")
+    d = {n: to_dev(None, b, "bf16") for n, (_, b) in I.qkv(w, bits_only=True).items()}
+    out, txt = W.window_attn_rope(g[method], d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"])
+    ref, rtxt = rope_chain(g, method, d, w.text_len, True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"1080p {method}: video"
+    assert torch.equal(txt.view(torch.int16), rtxt.view(torch.int16)), f"1080p {method}: text mean"

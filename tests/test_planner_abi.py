@@ -197,3 +197,27 @@ def test_attn_order_option():
     assert L.wsp_set_attn_order(7) == -1
     for o in (W.ORDER_ID, W.ORDER_LPT, W.ORDER_LPT_XCD):
         W.set_attn_order(o)
+
+
+def test_rope_attention_argument_errors():
+    """wsp_window_attn_rope / _workspace validate before any device work."""
+    p = W.Plan(5, 20, 36, 2, 3, 3, W.REGULAR)
+    tall = W.Plan(2, 6000, 2, 1, 1, 1, W.REGULAR)   # windows 3286 rows high > 2048
+    L = raw()
+    a, b, o = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    f0 = ctypes.c_float(0)
+    need = ctypes.c_size_t()
+    assert L.wsp_window_attn_rope_workspace(p.handle, 4, 128, 16, W.BF16, ctypes.byref(need)) == 0
+    rot = 5 * 20 * 36 * 4 * 128 * 2 + 2 * 16 * 4 * 128 * 2            # rotated k, text q, text k
+    assert need.value == W.window_attn_workspace(p, 4, 128, 16, W.BF16) + rot
+    assert L.wsp_window_attn_rope_workspace(p.handle, 4, 64, 16, W.BF16, ctypes.byref(need)) == -1
+    assert L.wsp_window_attn_rope_workspace(p.handle, 4, 128, 16, W.F32, ctypes.byref(need)) == -1
+    assert W.window_attn_rope_workspace(p, 4, 16, per_window=True) == rot + p.n_windows * 16 * 4 * 128 * 4
+
+    def call(pl=p, D=128, dt=W.BF16, ws=None, wb=0):
+        return L.wsp_window_attn_rope(pl.handle, a, b, a, a, b, a, 4, D, 16, dt, f0, f0, 1, o, o, ws, wb, None)
+
+    assert call(D=64) == -1 and b"head_dim 128" in L.wsp_last_error()
+    assert call(dt=W.F32) == -1
+    assert call(ws=o, wb=16) == -4                          # workspace too small
+    assert call(pl=tall) == -2 and b"extents" in L.wsp_last_error()

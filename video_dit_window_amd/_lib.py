@@ -42,6 +42,10 @@ _SIGNATURES = {
     "wsp_rope_relayout": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_int,
                                    ctypes.c_float, _c_vp]),
     "wsp_rope_text": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _c_vp]),
+    "wsp_window_attn_rope": (_c_int, [_c_vp] * 7 + [_c_int, _c_int, _c_int, _c_int, ctypes.c_float,
+                                                     ctypes.c_float, ctypes.c_uint, _c_vp, _c_vp, _c_vp, _c_sz,
+                                                     _c_vp]),
+    "wsp_window_attn_rope_workspace": (_c_int, [_c_vp, _c_int, _c_int, _c_int, _c_int, _szp]),
     "wsp_fp8_amax": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp]),
     "wsp_fp8_quantize": (_c_int, [_c_vp, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp]),
     "wsp_window_attn_qk8": (_c_int, [_c_vp] * 9 + [_c_int, _c_int, _c_int, ctypes.c_float, ctypes.c_uint,
@@ -325,6 +329,55 @@ def rope_text(x, theta=None, out=None, stream=None):
         _dev_ptr(x, "x"), _dev_ptr(out, "out"), x.shape[0], x.shape[1], x.shape[2], _dtype_code(x.dtype),
         ctypes.c_float(0.0 if theta is None else theta), _stream(stream)))
     return out
+
+
+def window_attn_rope_workspace(p: Plan, n_heads, text_len, per_window=True) -> int:
+    """Workspace bytes of window_attn_rope (bf16, head dim 128): the rotated
+    text q and k, then the text partials -- the minimum the call accepts, or
+    with per_window=True one partial per window (the faster text reduction)."""
+    b = ctypes.c_size_t()
+    _check("wsp_window_attn_rope_workspace",
+           lib().wsp_window_attn_rope_workspace(p.handle, n_heads, 128, text_len, BF16, ctypes.byref(b)))
+    if per_window:
+        return b.value - window_attn_workspace(p, n_heads, 128, text_len, BF16) + \
+            window_attn_workspace(p, n_heads, 128, text_len, BF16, per_window=True)
+    return b.value
+
+
+def window_attn_rope(p: Plan, q, k, v, txt_q, txt_k, txt_v, scale=None, theta=None, out=None, txt_out=None,
+                     workspace=None, stream=None, canonical=True, per_window=True):
+    """Window attention of rotated q, k (wsp_window_attn_rope): the same bits
+    as rope_relayout / rope_text followed by window_attn, with the video
+    rotation inside the attention kernel; q and k are not modified.
+    bf16, head dim 128.  Returns (out, txt_out)."""
+    torch = _torch()
+    N, Hh, D = q.shape
+    Lt = txt_q.shape[0]
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    for name, t in (("txt_k", txt_k), ("txt_v", txt_v)):
+        if t.shape != txt_q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match txt_q in shape and q in dtype")
+    if txt_q.shape[1:] != (Hh, D) or N != p.n_tokens:
+        raise ValueError("shapes do not match the plan / each other")
+    need = window_attn_rope_workspace(p, Hh, Lt, per_window=per_window)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if txt_out is None:
+            txt_out = torch.empty_like(txt_q)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    tp = [(_dev_ptr(t, n) if Lt else _c_vp(0)) for n, t in
+          (("txt_q", txt_q), ("txt_k", txt_k), ("txt_v", txt_v), ("txt_out", txt_out))]
+    _check("wsp_window_attn_rope", lib().wsp_window_attn_rope(
+        p.handle, _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), tp[0], tp[1], tp[2],
+        Hh, D, Lt, _dtype_code(q.dtype), ctypes.c_float(0.0 if scale is None else float(scale)),
+        ctypes.c_float(0.0 if theta is None else float(theta)), IO_CANONICAL if canonical else IO_LAYOUT,
+        _dev_ptr(out, "out"), tp[3], _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)))
+    return out, txt_out
 
 
 def fp8_amax(*tensors, amax=None, stream=None):

@@ -143,6 +143,25 @@ int device_rel_ids(wsp_plan_t &p, int dev, int32_t **out) {
     return WSP_OK;
 }
 
+int device_layout_positions(wsp_plan_t &p, int dev, int32_t **out) {
+    std::lock_guard<std::mutex> lk(p.mu);
+    DeviceTables &t = p.dev[dev];
+    if (!t.lpos) {
+        std::vector<int32_t> pos, lpos;
+        try {
+            window_positions(p, pos);
+            lpos.resize(p.ids.size());
+        } catch (const std::bad_alloc &) {
+            return fail(WSP_ENOMEM, "host allocation of a position table failed");
+        }
+        for (size_t j = 0; j < lpos.size(); ++j) lpos[j] = pos[size_t(p.ids[j])];
+        int rc = upload(lpos.data(), lpos.size(), &t.lpos);
+        if (rc) return rc;
+    }
+    *out = t.lpos;
+    return WSP_OK;
+}
+
 int device_windows(wsp_plan_t &p, int dev, bool gather, WinDesc **out) {
     std::lock_guard<std::mutex> lk(p.mu);
     DeviceTables &t = p.dev[dev];
@@ -314,6 +333,63 @@ int wsp_window_attn(const wsp_plan_t *pc, const void *q, const void *k, const vo
 
 namespace {
 
+constexpr int kRopeHeadDim = 128;
+constexpr int kRopeAxisPairs = 21;
+
+// (cos, sin) of position p times theta^(-2i/42), i < 21, for p < P; one table
+// per (device, theta, P), built in double and kept until the process ends.
+std::mutex g_rope_mu;
+std::map<std::tuple<int, uint32_t, int>, float2 *> g_rope_tables;
+
+int rope_table(int dev, float theta, int P, const float2 **out) {
+    uint32_t tb;
+    std::memcpy(&tb, &theta, sizeof tb);
+    const auto key = std::make_tuple(dev, tb, P);
+    std::lock_guard<std::mutex> lk(g_rope_mu);
+    auto it = g_rope_tables.find(key);
+    if (it != g_rope_tables.end()) {
+        *out = it->second;
+        return WSP_OK;
+    }
+    std::vector<float2> host;
+    try {
+        host.resize(size_t(P) * kRopeAxisPairs);
+    } catch (const std::bad_alloc &) {
+        return fail(WSP_ENOMEM, "host allocation of a rotary table failed");
+    }
+    const int axis = 2 * kRopeAxisPairs;
+    for (int p = 0; p < P; ++p)
+        for (int i = 0; i < kRopeAxisPairs; ++i) {
+            const double a = double(p) * std::pow(double(theta), -2.0 * i / axis);
+            host[size_t(p) * kRopeAxisPairs + i] = float2{float(std::cos(a)), float(std::sin(a))};
+        }
+    float2 *d = nullptr;
+    int rc = upload(host.data(), host.size(), &d);
+    if (rc) return rc;
+    g_rope_tables.emplace(key, d);
+    *out = d;
+    return WSP_OK;
+}
+
+int rope_args(const void *x, const void *y, int n_heads, int head_dim, int dtype, int text_len,
+              float &theta) {
+    if (!x || !y) return fail(WSP_EINVAL, "x or y is NULL");
+    if (!aligned16(x) || !aligned16(y)) return fail(WSP_EINVAL, "x and y must be 16-byte aligned");
+    if (x == y) return fail(WSP_EINVAL, "x and y must not alias");
+    if (head_dim != kRopeHeadDim)
+        return fail(WSP_EINVAL, "rotary embedding needs head_dim 128 (three 42-channel axis blocks), got " +
+                                    std::to_string(head_dim));
+    if (n_heads < 1 || n_heads > 32767) return fail(WSP_EINVAL, "n_heads must be in 1..32767");
+    if (dtype != WSP_F32 && dtype != WSP_BF16) return fail(WSP_EINVAL, "unknown dtype");
+    if (text_len < 0 || text_len > (1 << 20)) return fail(WSP_EINVAL, "text_len must be in 0..2^20");
+    if (!(theta > 0.0f) || !std::isfinite(theta)) theta = 10000.0f;
+    return WSP_OK;
+}
+
+}  // namespace
+
+namespace {
+
 // ---- the no-allocation entry point's scratch --------------------------------
 // Float32 text partials for wsp_window_attn_noalloc: a file-scope device array
 // (each GPU the library runs on holds its own copy until the process ends).
@@ -369,25 +445,55 @@ int resident_tables(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, i
                 "first (it uploads them; wsp_window_attn_noalloc allocates nothing)");
 }
 
-// Shared body of wsp_window_attn_ex (q8 = false), wsp_window_attn_qk8 and
+// Bytes of the rotated k (n_tokens rows) and the rotated text q and k that
+// lead wsp_window_attn_rope's workspace (bf16, head dim 128), each part
+// rounded up to 256.
+size_t rope_part_bytes(int64_t rows, int n_heads) {
+    return (size_t(rows) * size_t(n_heads) * kRopeHeadDim * 2u + 255u) & ~size_t(255);
+}
+size_t rope_bytes(const wsp_plan_t &p, int text_len, int n_heads) {
+    return rope_part_bytes(p.n, n_heads) + 2 * rope_part_bytes(text_len, n_heads);
+}
+
+// Shared body of wsp_window_attn_ex (q8 = false), wsp_window_attn_qk8,
 // wsp_window_attn_noalloc (no_alloc: resident tables, the scratch array as
-// workspace).
+// workspace) and wsp_window_attn_rope (rope_theta != NULL: the workspace
+// starts with the rotated k, text q and text k; the video queries turn
+// inside the attention kernel).
 int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const void *v,
                      const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
                      int head_dim, int text_len, int dtype, bool q8, const float *amax_q,
                      const float *amax_k, float scale, unsigned flags, void *out, void *txt_out,
-                     void *workspace, size_t workspace_bytes, void *stream, bool no_alloc = false) {
+                     void *workspace, size_t workspace_bytes, void *stream, bool no_alloc = false,
+                     const float *rope_theta = nullptr) {
     if (flags & ~unsigned(WSP_ATTN_IO_CANONICAL)) return fail(WSP_EINVAL, "unknown attention flags");
     const bool gather = (flags & WSP_ATTN_IO_CANONICAL) != 0;
     size_t need = 0;
     int rc = wsp_window_attn_workspace(pc, n_heads, head_dim, text_len, dtype, &need);
     if (rc) return rc;
     wsp_plan_t *p = const_cast<wsp_plan_t *>(pc);
+    const bool rope = rope_theta != nullptr;
+    float theta = rope ? *rope_theta : 0.f;
+    size_t rot_bytes = 0;
+    if (rope) {
+        if (dtype != WSP_BF16 || head_dim != kRopeHeadDim)
+            return fail(WSP_EINVAL, "rotary attention needs bf16 and head_dim 128");
+        if (text_len > (1 << 20)) return fail(WSP_EINVAL, "text_len must be in 0..2^20");
+        if (!(theta > 0.0f) || !std::isfinite(theta)) theta = 10000.0f;
+        if (p->max_ext[0] > 1024 || p->max_ext[1] > 2048 || p->max_ext[2] > 2048)
+            return fail(WSP_ERANGE, "window extents beyond 1024 (t) / 2048 (h, w)");
+        rot_bytes = rope_bytes(*p, text_len, n_heads);
+        need += rot_bytes;
+    }
     for (const void *ptr : {q, k, v, static_cast<const void *>(out)}) {
         if (!ptr) return fail(WSP_EINVAL, "q, k, v and out must be non-NULL");
         if (!aligned16(ptr)) return fail(WSP_EINVAL, "q, k, v and out must be 16-byte aligned");
     }
     if (out == q || out == k || out == v) return fail(WSP_EINVAL, "out must not alias q, k or v");
+    if (rope && (!workspace || workspace_bytes < need))
+        return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) + " bytes required, got " +
+                                        std::to_string(workspace_bytes));
+    if (rope && !aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
     if (text_len > 0) {
         for (const void *ptr : {txt_q, txt_k, txt_v, static_cast<const void *>(txt_out)}) {
             if (!ptr) return fail(WSP_EINVAL, "text tensors and txt_out must be non-NULL when text_len > 0");
@@ -405,6 +511,17 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
                                                 " bytes required, got " + std::to_string(workspace_bytes));
             if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
         }
+    }
+    // Rotated k, text q and text k at the start of the workspace, the
+    // partials after.
+    void *rot_k = nullptr, *rot_tq = nullptr, *rot_tk = nullptr;
+    if (rope) {
+        uint8_t *w = static_cast<uint8_t *>(workspace);
+        rot_k = w;
+        rot_tq = w + rope_part_bytes(p->n, n_heads);
+        rot_tk = static_cast<uint8_t *>(rot_tq) + rope_part_bytes(text_len, n_heads);
+        workspace = w + rot_bytes;
+        workspace_bytes -= rot_bytes;
     }
     // The matrix-core kernel addresses a window's video rows (canonical
     // order: the rows between its smallest and largest canonical id) and the
@@ -456,9 +573,35 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
     hipStream_t s = hipStream_t(stream);
     float *ws = static_cast<float *>(workspace);
     hipError_t e;
+    RopeTables rt;
+    if (rope) {
+        // k rotated once for every query tile that reads it (the stand-alone
+        // rotation kernel, in the I/O order: canonical rows take positions by
+        // canonical id, layout rows through the plan's ids), the text rows
+        // at (i, i, i); the queries turn as the attention kernel loads them.
+        const float2 *cs = nullptr;
+        int32_t *pos = nullptr, *lpos = nullptr, *cid = nullptr;
+        const int P = std::max({text_len + p->max_ext[0], p->max_ext[1], p->max_ext[2], text_len, 1});
+        if ((rc = rope_table(dev, theta, P, &cs))) return rc;
+        if ((rc = device_positions(*p, dev, &pos))) return rc;
+        if ((rc = device_layout_positions(*p, dev, &lpos))) return rc;
+        if (!gather && (rc = device_ids(*p, dev, &cid))) return rc;
+        rt = RopeTables{cs, lpos};
+        e = launch_rope(k, rot_k, nullptr, cid, pos, cs, p->n, n_heads, dtype, text_len, s);
+        if (e == hipSuccess && text_len > 0)
+            e = launch_rope(txt_q, rot_tq, nullptr, nullptr, nullptr, cs, text_len, n_heads, dtype, 0, s);
+        if (e == hipSuccess && text_len > 0)
+            e = launch_rope(txt_k, rot_tk, nullptr, nullptr, nullptr, cs, text_len, n_heads, dtype, 0, s);
+        if (e != hipSuccess) return hip_fail(e, "rope kernel launch");
+        k = rot_k;
+        if (text_len > 0) {
+            txt_q = rot_tq;
+            txt_k = rot_tk;
+        }
+    }
     if (dtype == WSP_BF16)
         e = launch_attn_bf16(head_dim, small, q8, q, k, v, txt_q, txt_k, txt_v, out, ws, d_rel, items, wins,
-                             n_items, amax_q, amax_k, n_heads, text_len, scale, s);
+                             n_items, amax_q, amax_k, rope ? &rt : nullptr, n_heads, text_len, scale, s);
     else
         e = launch_attn_f32(head_dim, static_cast<const float *>(q), static_cast<const float *>(k),
                             static_cast<const float *>(v), static_cast<const float *>(txt_q),
@@ -485,62 +628,6 @@ int wsp_window_attn_ex(const wsp_plan_t *pc, const void *q, const void *k, const
                             nullptr, nullptr, scale, flags, out, txt_out, workspace, workspace_bytes, stream);
 }
 
-namespace {
-
-constexpr int kRopeHeadDim = 128;
-constexpr int kRopeAxisPairs = 21;
-
-// (cos, sin) of position p times theta^(-2i/42), i < 21, for p < P; one table
-// per (device, theta, P), built in double and kept until the process ends.
-std::mutex g_rope_mu;
-std::map<std::tuple<int, uint32_t, int>, float2 *> g_rope_tables;
-
-int rope_table(int dev, float theta, int P, const float2 **out) {
-    uint32_t tb;
-    std::memcpy(&tb, &theta, sizeof tb);
-    const auto key = std::make_tuple(dev, tb, P);
-    std::lock_guard<std::mutex> lk(g_rope_mu);
-    auto it = g_rope_tables.find(key);
-    if (it != g_rope_tables.end()) {
-        *out = it->second;
-        return WSP_OK;
-    }
-    std::vector<float2> host;
-    try {
-        host.resize(size_t(P) * kRopeAxisPairs);
-    } catch (const std::bad_alloc &) {
-        return fail(WSP_ENOMEM, "host allocation of a rotary table failed");
-    }
-    const int axis = 2 * kRopeAxisPairs;
-    for (int p = 0; p < P; ++p)
-        for (int i = 0; i < kRopeAxisPairs; ++i) {
-            const double a = double(p) * std::pow(double(theta), -2.0 * i / axis);
-            host[size_t(p) * kRopeAxisPairs + i] = float2{float(std::cos(a)), float(std::sin(a))};
-        }
-    float2 *d = nullptr;
-    int rc = upload(host.data(), host.size(), &d);
-    if (rc) return rc;
-    g_rope_tables.emplace(key, d);
-    *out = d;
-    return WSP_OK;
-}
-
-int rope_args(const void *x, const void *y, int n_heads, int head_dim, int dtype, int text_len,
-              float &theta) {
-    if (!x || !y) return fail(WSP_EINVAL, "x or y is NULL");
-    if (!aligned16(x) || !aligned16(y)) return fail(WSP_EINVAL, "x and y must be 16-byte aligned");
-    if (x == y) return fail(WSP_EINVAL, "x and y must not alias");
-    if (head_dim != kRopeHeadDim)
-        return fail(WSP_EINVAL, "rotary embedding needs head_dim 128 (three 42-channel axis blocks), got " +
-                                    std::to_string(head_dim));
-    if (n_heads < 1 || n_heads > 32767) return fail(WSP_EINVAL, "n_heads must be in 1..32767");
-    if (dtype != WSP_F32 && dtype != WSP_BF16) return fail(WSP_EINVAL, "unknown dtype");
-    if (text_len < 0 || text_len > (1 << 20)) return fail(WSP_EINVAL, "text_len must be in 0..2^20");
-    if (!(theta > 0.0f) || !std::isfinite(theta)) theta = 10000.0f;
-    return WSP_OK;
-}
-
-}  // namespace
 
 int wsp_rope_relayout(const void *x, void *y, int n_heads, int head_dim, int dtype,
                       const wsp_plan_t *src, const wsp_plan_t *dst, const wsp_plan_t *pos,
@@ -619,6 +706,27 @@ int wsp_fp8_quantize(const void *x, void *y, int64_t n_rows, int n_heads, int he
     hipError_t e = launch_fp8_quantize(x, y, amax, n_rows, n_heads, head_dim, dtype, hipStream_t(stream));
     if (e != hipSuccess) return hip_fail(e, "fp8 quantize kernel launch");
     return WSP_OK;
+}
+
+int wsp_window_attn_rope_workspace(const wsp_plan_t *p, int n_heads, int head_dim, int text_len, int dtype,
+                                   size_t *bytes) {
+    g_last_error.clear();
+    int rc = wsp_window_attn_workspace(p, n_heads, head_dim, text_len, dtype, bytes);
+    if (rc) return rc;
+    if (dtype != WSP_BF16 || head_dim != kRopeHeadDim)
+        return fail(WSP_EINVAL, "rotary attention needs bf16 and head_dim 128");
+    *bytes += rope_bytes(*p, text_len, n_heads);
+    return WSP_OK;
+}
+
+int wsp_window_attn_rope(const wsp_plan_t *pc, const void *q, const void *k, const void *v,
+                         const void *txt_q, const void *txt_k, const void *txt_v, int n_heads,
+                         int head_dim, int text_len, int dtype, float scale, float theta, unsigned flags,
+                         void *out, void *txt_out, void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error.clear();
+    return window_attn_impl(pc, q, k, v, txt_q, txt_k, txt_v, n_heads, head_dim, text_len, dtype, false,
+                            nullptr, nullptr, scale, flags, out, txt_out, workspace, workspace_bytes, stream,
+                            false, &theta);
 }
 
 int wsp_window_attn_noalloc(const wsp_plan_t *pc, const void *q, const void *k, const void *v,

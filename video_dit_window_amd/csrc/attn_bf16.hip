@@ -81,21 +81,52 @@ __device__ __host__ constexpr int kswz(int r) {
     return Q8 ? swz8(r) : swz<D>(r);
 }
 
+// Window-local rotary embedding of the queries inside the kernel (ROPE).
+constexpr int kRopePairs = 21;  // pairs per axis block (42 of 128 channels)
+
+// Rotation of one 16-byte chunk: bf16 channels 8c .. 8c+7, i.e. pairs 4c ..
+// 4c+3 of the row (pair k of axis block k / 21), of a row at window offset
+// pk = dt | dh << 10 | dw << 21, i.e. axial positions (Lt + dt, dh, dw);
+// cs = (cos, sin) of 21 pairs per position.  Pairs 0..62 turn, pair 63
+// (channels 126, 127) passes through.  Same float32 steps and one rounding
+// to bf16 as the stand-alone rotation kernel.
+__device__ inline u32x4 rope_chunk(u32x4 w, int c, uint32_t pk, int Lt, const float2 *__restrict__ cs) {
+    const int pos[3] = {Lt + int(pk & 1023u), int((pk >> 10) & 2047u), int(pk >> 21)};
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int k = 4 * c + e;
+        const int ax = (k * 3121) >> 16;  // k / 21 for 0 <= k < 64
+        if (ax < 3) {
+            const float2 t = cs[pos[ax] * kRopePairs + (k - kRopePairs * ax)];
+            const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
+            o[e] = pack_bf16(fmaf(x0, t.x, -x1 * t.y), fmaf(x0, t.y, x1 * t.x));
+        } else {
+            o[e] = w[e];
+        }
+    }
+    return o;
+}
+
 // GATHER: q, k, v and out hold rows in canonical token order; video row r
 // of window w is canonical row vrow0 + rel[off + r] (the plan's ids relative
 // to the window's smallest id), so the layout permutation happens inside the
 // loads and the output stores.  Q8: q, k, tq, tk are E4M3 codes (D = 128).
-template <int D, int kWaves, bool GATHER, bool Q8>
+// ROPE (bf16, D = 128): the video query rows are rotated by their
+// window-local positions as an item loads them; k, tq and tk arrive rotated.
+template <int D, int kWaves, bool GATHER, bool Q8, bool ROPE>
 __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint8_t *__restrict__ tq, const uint8_t *__restrict__ tk, const uint16_t *__restrict__ tv,
     uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ rel,
     const ItemDesc *__restrict__ items, const WinDesc *__restrict__ wins,
-    const float *__restrict__ amax_q, const float *__restrict__ amax_k, int H, int Lt, float c2_unit) {
+    const float *__restrict__ amax_q, const float *__restrict__ amax_k, const float2 *__restrict__ rope_cs,
+    const int32_t *__restrict__ rope_pos, int H, int Lt, float c2_unit) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     using VS = Shape<D, kWaves>;       // V tiles (bf16 rows)
     using KS = KShape<D, kWaves, Q8>;  // K tiles
     static_assert(!Q8 || D == 128, "E4M3 scores need head_dim 128");
+    static_assert(!ROPE || (D == 128 && !Q8), "in-kernel RoPE: bf16 rows of head_dim 128");
     constexpr int kBM = 32 * kWaves;   // query rows per work group
     constexpr int QE = Q8 ? 1 : 2;     // bytes per q / k element
     // Two stages, each a K tile followed by a V tile.
@@ -145,6 +176,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 #pragma unroll
             for (int s = 0; s < VS::KSTEPS; ++s)
                 Qr[s] = *reinterpret_cast<const bf16x8 *>(p + 2 * (16 * s + 8 * hh));
+            if constexpr (ROPE) {
+                // video queries: rotated in registers (chunk 2s + hh of the row)
+                if (!text) {
+                    const uint32_t pk = uint32_t(rope_pos[it.win.off + min(qrow, nq - 1)]);
+#pragma unroll
+                    for (int s = 0; s < VS::KSTEPS; ++s)
+                        Qr[s] = __builtin_bit_cast(
+                            bf16x8, rope_chunk(__builtin_bit_cast(u32x4, Qr[s]), 2 * s + hh, pk, Lt, rope_cs));
+                }
+            }
         }
     }
 
@@ -528,27 +569,36 @@ int attn_bf16_tile_m(bool small) { return 32 * (small ? kSmallItemWaves : kItemW
 hipError_t launch_attn_bf16(int head_dim, bool small, bool q8, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out, float *ws,
                             const int32_t *rel, const ItemDesc *items, const WinDesc *wins, int n_items,
-                            const float *amax_q, const float *amax_k, int n_heads, int text_len, float scale,
-                            hipStream_t s) {
+                            const float *amax_q, const float *amax_k, const RopeTables *rope, int n_heads,
+                            int text_len, float scale, hipStream_t s) {
     if (n_items <= 0) return hipSuccess;
     if (q8 && head_dim != 128) return hipErrorInvalidValue;
+    if (rope && (q8 || head_dim != 128)) return hipErrorInvalidValue;
     const float c2 = scale * kLog2e;
+    const RopeTables none{};
+    const RopeTables &rt = rope ? *rope : none;
     auto B = [](const void *p) { return static_cast<const uint8_t *>(p); };
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
     auto launch = [&](auto kern, int waves) {
         kern<<<dim3(n_items), dim3(64 * waves), 0, s>>>(B(q), B(k), U(v), B(tq), B(tk), U(tv),
                                                          static_cast<uint16_t *>(out), ws, rel, items, wins,
-                                                         amax_q, amax_k, n_heads, text_len, c2);
+                                                         amax_q, amax_k, rt.cs, rt.pos, n_heads, text_len, c2);
     };
     auto dispatch = [&](auto waves_c) {
         constexpr int NW = decltype(waves_c)::value;
         const bool g = rel != nullptr;
-        if (q8) {
-            g ? launch(attn_bf16_kernel<128, NW, true, true>, NW) : launch(attn_bf16_kernel<128, NW, false, true>, NW);
+        if (rope) {
+            g ? launch(attn_bf16_kernel<128, NW, true, false, true>, NW)
+              : launch(attn_bf16_kernel<128, NW, false, false, true>, NW);
+        } else if (q8) {
+            g ? launch(attn_bf16_kernel<128, NW, true, true, false>, NW)
+              : launch(attn_bf16_kernel<128, NW, false, true, false>, NW);
         } else if (head_dim == 128) {
-            g ? launch(attn_bf16_kernel<128, NW, true, false>, NW) : launch(attn_bf16_kernel<128, NW, false, false>, NW);
+            g ? launch(attn_bf16_kernel<128, NW, true, false, false>, NW)
+              : launch(attn_bf16_kernel<128, NW, false, false, false>, NW);
         } else if (head_dim == 64) {
-            g ? launch(attn_bf16_kernel<64, NW, true, false>, NW) : launch(attn_bf16_kernel<64, NW, false, false>, NW);
+            g ? launch(attn_bf16_kernel<64, NW, true, false, false>, NW)
+              : launch(attn_bf16_kernel<64, NW, false, false, false>, NW);
         } else {
             return hipErrorInvalidValue;
         }

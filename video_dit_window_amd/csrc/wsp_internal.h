@@ -63,6 +63,7 @@ struct DeviceTables {
     int32_t *ids = nullptr;                                     // [n_tokens]
     int32_t *rel = nullptr;                                     // [n_tokens] ids - first id of the window
     int32_t *pos = nullptr;                                     // [n_tokens] window positions
+    int32_t *lpos = nullptr;                                    // [n_tokens] window positions, layout order
     WinDesc *wins[2] = {nullptr, nullptr};                      // [n_windows] layout / canonical order
     std::map<std::tuple<int, int, int, int>, int32_t *> perm;   // src layout -> perm
     // (H, Lt, BM, order, canonical-order I/O, text chunks) -> work list
@@ -116,6 +117,8 @@ int device_ids(wsp_plan_t &p, int dev, int32_t **out);
 int device_perm(const wsp_plan_t &src, wsp_plan_t &dst, int dev, int32_t **out);
 int device_positions(wsp_plan_t &p, int dev, int32_t **out);
 int device_rel_ids(wsp_plan_t &p, int dev, int32_t **out);
+// Window positions in layout order (pos[ids[j]]), for the in-kernel RoPE.
+int device_layout_positions(wsp_plan_t &p, int dev, int32_t **out);
 int device_windows(wsp_plan_t &p, int dev, bool gather, WinDesc **out);
 int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int order, bool gather,
                  int n_chunks, ItemDesc **out, int *count);
@@ -132,11 +135,19 @@ hipError_t launch_relayout(const void *x, void *y, const int32_t *perm, int64_t 
 // ones) are E4M3 codes with per-head scales amax/448 (head dim 128 only).
 // ws receives the float32 text partials of the items' chunks.
 int attn_bf16_tile_m(bool small);
+// In-kernel rotary embedding of the video queries (bf16, head dim 128):
+// cs = (cos, sin) of 21 pairs per position (positions 0 .. text_len +
+// largest temporal extent - 1 at least); pos[layout row] = the row's window
+// offset dt | dh << 10 | dw << 21 (axial positions text_len + dt, dh, dw).
+struct RopeTables {
+    const float2 *cs = nullptr;
+    const int32_t *pos = nullptr;
+};
 hipError_t launch_attn_bf16(int head_dim, bool small, bool q8, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out, float *ws,
                             const int32_t *rel, const ItemDesc *items, const WinDesc *wins, int n_items,
-                            const float *amax_q, const float *amax_k, int n_heads, int text_len, float scale,
-                            hipStream_t s);
+                            const float *amax_q, const float *amax_k, const RopeTables *rope, int n_heads,
+                            int text_len, float scale, hipStream_t s);
 // attn_f32.hip: the float32 kernel (same items; ids != NULL: canonical-order
 // tensors, video row r of window w is tensor row ids[offsets[w] + r]).
 int attn_f32_tile_m(int head_dim);
