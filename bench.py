@@ -45,6 +45,8 @@ METRIC = "window-attn TFLOP/s + video tokens/s/layer at 1080p grid; % MFMA peak"
 # (FETCH_SIZE x2.0, WRITE_SIZE x1.0); the committed summary under profiles/ holds the
 # figures and commands.  Keyed by the sha256 prefix of the attention kernel source the
 # counters were taken on: any later change to the kernel reports null.
+# QK^T at the fp8 rate and PV at the bf16 rate, equal FLOPs each.
+MIXED_FP8_PEAK_TFLOPS = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
 MEASURED_TRAFFIC = {"b86c05816fb7e5c7": {"1080p_bf16": {"layout": 4.3906e9, "canonical": 4.4107e9}}}
 ATTN_SRCS = [os.path.join(ROOT, "video_dit_window_amd", "csrc", f)
              for f in ("attn_bf16.hip", "attn_bf16_common.h")]
@@ -279,7 +281,8 @@ def main():
     row_bytes = Hh * D * 2
     stream = torch.cuda.current_stream()
 
-    ev = {"attn": [], "relayout": [], "fused_attn": [], "rope": [], "qk8_attn": [], "chunked_attn": []}
+    ev = {"attn": [], "relayout": [], "fused_attn": [], "rope": [], "qk8_attn": [], "chunked_attn": [],
+          "rope_attn": [], "rope_chain": []}
 
     def timed(kind, fn, record):
         if record:
@@ -441,6 +444,44 @@ def main():
             "workspace_bytes": ws_min_bytes, "headline_workspace_bytes": ws_bytes,
             "ms_per_step": round(ms_ch, 4), "avg_launch_ms": round(ch_ms, 4),
             "attn_kernel_tflops": round(per_call_flops / (ch_ms * 1e-3) / 1e12, 2)}
+        # The headline pass with window-local RoPE of q and k: queries rotated
+        # inside the attention kernel, keys and text rows by the stand-alone
+        # rotation kernel (wsp_window_attn_rope); beside it the unfused chain
+        # (rotation of q, k and text rows, then the plain launch).
+        ws_rope = torch.empty(max(W.window_attn_rope_workspace(p, Hh, Lt) for p in plans), dtype=torch.uint8,
+                              device="cuda")
+        rtq, rtk = torch.empty_like(dev["txt_q"]), torch.empty_like(dev["txt_k"])
+
+        def step_rope_attn(record):
+            for li, p in enumerate(plans):
+                timed("rope_attn", lambda li=li, p=p: W.window_attn_rope(
+                    p, dev["q"], dev["k"], dev["v"], dev["txt_q"], dev["txt_k"], dev["txt_v"],
+                    out=outs[li], txt_out=txts[li], workspace=ws_rope, canonical=True), record)
+
+        def step_rope_chain(record):
+            for li, p in enumerate(plans):
+                def chain(li=li, p=p):
+                    W.rope_relayout(dev["q"], canon, canon, p, Lt, out=bufs["q"])
+                    W.rope_relayout(dev["k"], canon, canon, p, Lt, out=bufs["k"])
+                    W.rope_text(dev["txt_q"], out=rtq)
+                    W.rope_text(dev["txt_k"], out=rtk)
+                    W.window_attn(p, bufs["q"], bufs["k"], dev["v"], rtq, rtk, dev["txt_v"], out=outs[li],
+                                  txt_out=txts[li], workspace=ws, canonical=True)
+                timed("rope_chain", chain, record)
+        ms_ra = run(step_rope_attn)[0]
+        ms_rc = run(step_rope_chain)[0]
+        del ws_rope
+        head_launch = float(np.mean([a.elapsed_time(b) for a, b in ev["fused_attn"]]))
+        ra_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["rope_attn"]]))
+        rc_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["rope_chain"]]))
+        res["rope_attention"] = {
+            "note": "headline pass with window-local RoPE of q and k: queries rotated inside the attention "
+                    "kernel, keys and text rows by the rotation kernel (wsp_window_attn_rope); 'chain' = "
+                    "rotation of q, k and text rows by the rotation kernel, then the plain launch",
+            "ms_per_step": round(ms_ra, 4), "avg_layer_ms": round(ra_ms, 4),
+            "ratio_vs_plain_layer": round(ra_ms / head_launch, 4),
+            "chain_ms_per_step": round(ms_rc, 4), "chain_avg_layer_ms": round(rc_ms, 4),
+            "chain_ratio_vs_plain_layer": round(rc_ms / head_launch, 4)}
     rope_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["rope"]]))
     rope_bytes = 2 * N * row_bytes + 12 * N   # rows in + out, perm + id + position per row
     res["rope_relayout"] = {"note": "q or k moved canonical -> layout with window-local 3D RoPE",
@@ -448,10 +489,14 @@ def main():
                             "gbps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
                             "hbm_frac": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     q8_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["qk8_attn"]]))
+    q8_tflops = per_call_flops / (q8_ms * 1e-3) / 1e12
     res["fp8_qk_attention"] = {
-        "note": "q, k as OCP E4M3 codes (per-head scales) on the FP8 matrix cores; v, P, outputs bf16",
+        "note": "q, k as OCP E4M3 codes (per-head scales) on the FP8 matrix cores; v, P, outputs bf16. "
+                "Roofline: half the FLOPs (QK^T) at the fp8 peak, half (PV) at the bf16 peak",
         "avg_launch_ms": round(q8_ms, 4),
-        "attn_kernel_tflops": round(per_call_flops / (q8_ms * 1e-3) / 1e12, 2)}
+        "attn_kernel_tflops": round(q8_tflops, 2),
+        "mixed_peak_tflops": round(MIXED_FP8_PEAK_TFLOPS, 1),
+        "frac": round(q8_tflops / MIXED_FP8_PEAK_TFLOPS, 4)}
     if not args.no_configs:
         res["configs"] = config_launches([("720p_bf16", "regular"), ("4k_bf16", "shifted")])
     if not args.no_stack:
