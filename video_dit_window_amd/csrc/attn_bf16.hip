@@ -152,6 +152,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     // Its tensor row also addresses the output store of a video item.
     const int nq = text ? Lt : it.win.lw;
     const int qrow = qt * kBM + wave * 32 + l32;
+    // ROPE: the query row's window offset, requested first: its (cos, sin)
+    // loads depend on it and then run beside the query row's own load.
+    uint32_t qpk = 0;
+    if constexpr (ROPE) {
+        if (!text) qpk = uint32_t(rope_pos[it.win.off + min(qrow, nq - 1)]);
+    }
     int64_t qtrow;
     {
         const int r = min(qrow, nq - 1);
@@ -177,13 +183,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             for (int s = 0; s < VS::KSTEPS; ++s)
                 Qr[s] = *reinterpret_cast<const bf16x8 *>(p + 2 * (16 * s + 8 * hh));
             if constexpr (ROPE) {
-                // video queries: rotated in registers (chunk 2s + hh of the row)
+                // video queries rotated in registers (chunk 2s + hh of the row)
                 if (!text) {
-                    const uint32_t pk = uint32_t(rope_pos[it.win.off + min(qrow, nq - 1)]);
 #pragma unroll
                     for (int s = 0; s < VS::KSTEPS; ++s)
                         Qr[s] = __builtin_bit_cast(
-                            bf16x8, rope_chunk(__builtin_bit_cast(u32x4, Qr[s]), 2 * s + hh, pk, Lt, rope_cs));
+                            bf16x8, rope_chunk(__builtin_bit_cast(u32x4, Qr[s]), 2 * s + hh, qpk, Lt, rope_cs));
                 }
             }
         }
@@ -275,15 +280,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         const int32_t *const wrel = GATHER ? rel + wd.off : nullptr;
         const __amdgpu_buffer_rsrc_t krs = rsrc(k + (vrow0 * rs + hd) * QE, vrows * krow_bytes);
         const __amdgpu_buffer_rsrc_t vrs = rsrc(v + vrow0 * rs + hd, vrows * vrow_bytes);
-        // Layout order: loop-invariant per-lane offsets of a tile's rows,
-        // the tile step in the scalar offset.
-        int kdoff[KS::LOADS], vdoff[VS::LOADS];
-#pragma unroll
-        for (int i = 0; i < KS::LOADS; ++i)
-            kdoff[i] = (kdrow0 + KS::ROWS_PER_LOAD * i) * int(krow_bytes) + kdchunk[i];
-#pragma unroll
-        for (int i = 0; i < VS::LOADS; ++i)
-            vdoff[i] = (vdrow0 + VS::ROWS_PER_LOAD * i) * int(vrow_bytes) + vdchunk[i];
+        // Layout order: the lane's first row as a per-lane offset (its chunk
+        // added at the load), the tile and row steps in the scalar offset.
+        const int kdbase = kdrow0 * int(krow_bytes), vdbase = vdrow0 * int(vrow_bytes);
         // Gather mode: the ids of the next tile's rows are loaded one tile
         // ahead of their DMA by buffer loads whose per-lane offset holds the
         // row (the range check covers it: rows past the window read 0, and
@@ -295,7 +294,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         // offset below 2^31.
         const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<int32_t *>(GATHER ? wrel : rel), 0, GATHER ? 4 * Lw : 0, kBufferFlags);
-        auto load_ids = [&](Ids &d, int j) {
+        auto load_ids = [&](Ids &d, int j) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < VS::LOADS; ++i)
                 d.v[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (j * kBN + vdrow0 + VS::ROWS_PER_LOAD * i),
@@ -315,17 +314,23 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         // windows, the only reader of that K/V on its XCD, so that streaming
         // it does not evict the video groups' K/V.  Text rows (shared by
         // every item) keep the default.
-        auto dma_cp = [&](auto cp_c, uint8_t LDS_AS *dst, int j, Ids &idp, Ids &idn) {
+        // (The tile-step lambdas are forced inline: left to the inliner, the
+        // 4-wave layout-order kernel called one and kept its closure in
+        // scratch memory.)
+        auto dma_cp = [&](auto cp_c, uint8_t LDS_AS *dst, int j, Ids &idp,
+                          Ids &idn) __attribute__((always_inline)) {
             constexpr int CP = decltype(cp_c)::value;
             if constexpr (GATHER) load_ids(idn, j + 1);
             if (!GATHER && (j + 1) * kBN <= Lw) {
                 const int ks = j * kBN * int(krow_bytes), vs = j * kBN * int(vrow_bytes);
 #pragma unroll
                 for (int i = 0; i < KS::LOADS; ++i)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (void LDS_AS *)(dst + klo(i)), 16, kdoff[i], ks, 0, CP);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (void LDS_AS *)(dst + klo(i)), 16, kdbase + kdchunk[i],
+                                                             ks + KS::ROWS_PER_LOAD * i * int(krow_bytes), 0, CP);
 #pragma unroll
                 for (int i = 0; i < VS::LOADS; ++i)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + vlo(i)), 16, vdoff[i], vs, 0, CP);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (void LDS_AS *)(dst + vlo(i)), 16, vdbase + vdchunk[i],
+                                                             vs + VS::ROWS_PER_LOAD * i * int(vrow_bytes), 0, CP);
             } else if (GATHER && (j + 1) * kBN <= Lw) {
 #pragma unroll
                 for (int i = 0; i < KS::LOADS; ++i) {
@@ -371,7 +376,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                 }
             }
         };
-        auto dma = [&](uint8_t LDS_AS *dst, int j, Ids &idp, Ids &idn) {
+        auto dma = [&](uint8_t LDS_AS *dst, int j, Ids &idp, Ids &idn) __attribute__((always_inline)) {
             if (it.nwin > 1) dma_cp(std::integral_constant<int, 2>{}, dst, j, idp, idn);
             else dma_cp(std::integral_constant<int, 0>{}, dst, j, idp, idn);
         };
@@ -383,7 +388,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         const int ntiles = (M + kBN - 1) / kBN;
 
         // One tile: cur holds tile j; the DMA of tile j+1 goes to nxt.
-        auto tile = [&](const uint8_t LDS_AS *cur, uint8_t LDS_AS *nxt, int j, Ids &idu, Ids &idn) {
+        auto tile = [&](const uint8_t LDS_AS *cur, uint8_t LDS_AS *nxt, int j, Ids &idu,
+                        Ids &idn) __attribute__((always_inline)) {
             if (j + 1 < ntiles) dma(nxt, j + 1, idu, idn);
             if (active) {
 
