@@ -48,7 +48,7 @@ def test_window_positions_are_window_local(method):
         assert len(hits) == 1
         t0, _, h0, _, w0, _ = hits[0]
         assert tuple(pos[cid]) == (Lt + t - t0, h - h0, w - w0)
-    # every window restarts: its corner token sits at (Lt, 0, 0)
+    # positions count from each window's own corner, which sits at (Lt, 0, 0)
     for (t0, t1, h0, h1, w0, w1) in p.boxes:
         assert tuple(pos[(t0 * H + h0) * W + w0]) == (Lt, 0, 0)
 

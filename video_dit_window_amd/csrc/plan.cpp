@@ -128,7 +128,8 @@ int build_plan(int T, int H, int W, int nt, int nh, int nw, int method, wsp_plan
 
 void window_positions(const wsp_plan_t &p, std::vector<int32_t> &pos) {
     // "Window-Aligned Sequence Parallelism (SeedVR2)", section "Reference
-    // quirks reproduced on purpose": RoPE positions restart in every window.
+    // quirks reproduced on purpose": RoPE positions are offsets from each
+    // window's own corner.
     pos.assign(size_t(p.n), 0);
     for (int32_t w = 0; w < p.nwin; ++w) {
         const int32_t *b = &p.boxes[6 * size_t(w)];

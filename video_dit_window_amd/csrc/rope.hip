@@ -2,10 +2,11 @@
 // layouts (one read and one write of each q / k row).
 //
 // "Window-Aligned Sequence Parallelism (SeedVR2)", section "Reference quirks
-// reproduced on purpose": a video token at window-local offset (dt, dh, dw)
-// uses the axial indices (text_len + dt, dh, dw), restarting in every window;
-// 3 * (rope_dim // 3) = 126 of the 128 channels of a head are rotated, the
-// last two pass through.  The rotated span is three contiguous axis blocks
+// reproduced on purpose": a video token turns by its offset (dt, dh, dw) from
+// its own window's corner, the temporal component raised by text_len, so
+// tokens of different windows share positions; the rotated width is three
+// times head_dim / 3 (126 for a 128-wide head) and the remaining two channels
+// are copied.  The rotated span is three contiguous axis blocks
 // [t | h | w] of 42 channels, each rotated in adjacent pairs (2k, 2k+1), pair
 // i of a block by position * theta^(-2i/42); text token i uses (i, i, i).
 // The (cos, sin) of every (position, pair) comes from a host-built table
