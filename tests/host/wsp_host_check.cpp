@@ -9,9 +9,11 @@
 //     permutations, offsets box volumes, boxes inside the grid);
 //   * the relayout permutations and window-position tables of every pair;
 //   * the attention work lists for every order, both I/O orders and both
-//     tile heights: every (window, head, video query tile) and every
-//     (chunk, head, text query tile) exactly once, chunks partitioning the
-//     windows in id order, window rows matching the window table;
+//     tile heights: every (window, head, query tile) exactly once -- tiles of
+//     the joint rows [video; text] where a window has its own partial and
+//     that saves a tile -- and every other (chunk, head, text query tile)
+//     exactly once, chunks partitioning the windows in id order, window rows
+//     matching the window table;
 //   * argument validation of every entry point that takes device pointers
 //     (NULL, misaligned, aliasing, bad sizes) -- these return before any
 //     device call.
@@ -150,6 +152,13 @@ static void check_plan(int T, int H, int W, int nt, int nh, int nw, int method) 
                         CHECK(cnt == int(items.size()));
                         std::set<std::tuple<int, int, int>> vid, txt;
                         int64_t real = 0;
+                        // one partial per window: joint tiles [video; text] for the
+                        // windows where they save a tile, text items for the others
+                        const bool per_window = Lt > 0 && G == int(nwin);
+                        auto joint = [&](int32_t w) {
+                            const int64_t lw = off[size_t(w) + 1] - off[size_t(w)];
+                            return per_window && (lw + Lt + bm - 1) / bm < (lw + bm - 1) / bm + (Lt + bm - 1) / bm;
+                        };
                         for (const ItemDesc &it : items) {
                             if (it.w < 0) continue;
                             ++real;
@@ -161,11 +170,13 @@ static void check_plan(int T, int H, int W, int nt, int nh, int nw, int method) 
                                 const WinDesc &d = wins[size_t(it.w)];
                                 CHECK(it.win.off == d.off && it.win.lw == d.lw && it.win.vrow0 == d.vrow0 &&
                                       it.win.vrows == d.vrows);
-                                CHECK(int64_t(t) * bm < d.lw);
+                                CHECK(it.chunk == (joint(it.w) ? it.w : -1));
+                                CHECK(int64_t(t) * bm < d.lw + (joint(it.w) ? Lt : 0));
                                 CHECK(vid.insert({it.w, h, t}).second);
                             } else {
                                 CHECK(Lt > 0);
                                 CHECK(it.chunk >= 0 && it.chunk < G);
+                                CHECK(!per_window || (it.nwin == 1 && !joint(it.w)));
                                 CHECK(it.w == chunk_begin(it.chunk, nwin, G));
                                 CHECK(it.w + it.nwin == chunk_begin(it.chunk + 1, nwin, G));
                                 CHECK(int64_t(t) * bm < Lt);
@@ -173,9 +184,13 @@ static void check_plan(int T, int H, int W, int nt, int nh, int nw, int method) 
                             }
                         }
                         int64_t want_vid = 0;
-                        for (int32_t w = 0; w < nwin; ++w)
-                            want_vid += heads * ((int64_t(off[size_t(w) + 1] - off[size_t(w)]) + bm - 1) / bm);
-                        const int64_t want_txt = Lt > 0 ? int64_t(G) * heads * ((Lt + bm - 1) / bm) : 0;
+                        int64_t want_txt = 0;
+                        for (int32_t w = 0; w < nwin; ++w) {
+                            want_vid += heads * ((int64_t(off[size_t(w) + 1] - off[size_t(w)]) + (joint(w) ? Lt : 0) +
+                                                  bm - 1) / bm);
+                            if (per_window && !joint(w)) want_txt += heads * ((Lt + bm - 1) / bm);
+                        }
+                        if (Lt > 0 && !per_window) want_txt = int64_t(G) * heads * ((Lt + bm - 1) / bm);
                         CHECK(int64_t(vid.size()) == want_vid);
                         CHECK(int64_t(txt.size()) == want_txt);
                         CHECK(real == want_vid + want_txt);

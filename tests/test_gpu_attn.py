@@ -390,9 +390,12 @@ def full_layer_check(w, method, workers=16, per_window=True):
 
 
 @pytest.mark.timeout(900)
-def test_720p_regular_full(gpu):
-    """Minimum workspace: 36 windows in 16 chunks of two or three."""
-    full_layer_check(I.WORKLOADS["720p_bf16"], "regular", per_window=False)
+@pytest.mark.parametrize("per_window", [False, True], ids=["chunked_text", "per_window_text"])
+def test_720p_regular_full(gpu, per_window):
+    """Minimum workspace: 36 windows in 16 chunks of two or three; one
+    partial per window: each window's 128 text rows follow its video rows in
+    the same query tiles."""
+    full_layer_check(I.WORKLOADS["720p_bf16"], "regular", per_window=per_window)
 
 
 @pytest.mark.timeout(900)

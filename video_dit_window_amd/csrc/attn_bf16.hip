@@ -147,21 +147,24 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     float c2 = c2_unit;
     if constexpr (Q8) c2 = c2_unit * (amax_q[h] * (1.0f / 448.0f)) * (amax_k[h] * (1.0f / 448.0f));
 
-    // Query row of this lane (B operand of S^T = K Q^T): video rows of the
-    // item's window (through the ids table in gather mode), or text rows.
-    // Its tensor row also addresses the output store of a video item.
-    const int nq = text ? Lt : it.win.lw;
+    // Query row of this lane (B operand of S^T = K Q^T): the item's query
+    // rows are nv video rows of its window (through the ids table in gather
+    // mode), then -- joint items, or text items (nv = 0) -- text rows.  Its
+    // tensor row also addresses the output store.
+    const bool joint = !text && it.chunk >= 0;
+    const int nv = text ? 0 : it.win.lw;
+    const int nq = nv + (text || joint ? Lt : 0);
     const int qrow = qt * kBM + wave * 32 + l32;
     // ROPE: the query row's window offset, requested first: its (cos, sin)
     // loads depend on it and then run beside the query row's own load.
     uint32_t qpk = 0;
     if constexpr (ROPE) {
-        if (!text) qpk = uint32_t(rope_pos[it.win.off + min(qrow, nq - 1)]);
+        if (qrow < nv) qpk = uint32_t(rope_pos[it.win.off + qrow]);
     }
     int64_t qtrow;
     {
         const int r = min(qrow, nq - 1);
-        if (text) qtrow = r;
+        if (r >= nv) qtrow = r - nv;
         else if (GATHER) qtrow = int64_t(it.win.vrow0) + rel[it.win.off + r];
         else qtrow = int64_t(it.win.off) + r;
     }
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     bf16x8 Qr[Q8 ? 1 : VS::KSTEPS];
     v8i Qr8[2];
     {
-        const uint8_t *p = (text ? tq : q) + (qtrow * rs + hd) * QE;
+        const uint8_t *p = (min(qrow, nq - 1) >= nv ? tq : q) + (qtrow * rs + hd) * QE;
         if constexpr (Q8) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                 Qr[s] = *reinterpret_cast<const bf16x8 *>(p + 2 * (16 * s + 8 * hh));
             if constexpr (ROPE) {
                 // video queries rotated in registers (chunk 2s + hh of the row)
-                if (!text) {
+                if (qrow < nv) {
 #pragma unroll
                     for (int s = 0; s < VS::KSTEPS; ++s)
                         Qr[s] = __builtin_bit_cast(
@@ -535,24 +538,23 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         // Normalise.  The lane holds query qrow, dims 32t + 8g + 4hh + 0..3.
         const float l = halves_sum(l_run);
         const float inv = 1.0f / l;
-        if (text) {
-            // T_w into the chunk's float32 partial: the first window of the
-            // chunk writes it, the later ones add in window order (the same
-            // lane reads back what it wrote).
-            if (qrow < Lt) {
-                float *dst = ws + ((int64_t(it.chunk) * Lt + qrow) * H + h) * D;
+        if (qrow >= nv && qrow < nq) {
+            // A text row: T_w into the float32 partial `chunk`.  A text item
+            // writes it on its chunk's first window and adds the later ones
+            // in window order (the same lane reads back what it wrote); a
+            // joint item is the only writer of its window's text rows.
+            float *dst = ws + ((int64_t(it.chunk) * Lt + (qrow - nv)) * H + h) * D;
 #pragma unroll
-                for (int t = 0; t < VS::DT; ++t)
+            for (int t = 0; t < VS::DT; ++t)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        f32x4 *p = reinterpret_cast<f32x4 *>(dst + 32 * t + 8 * g + 4 * hh);
-                        f32x4 val = f32x4{O[t][4 * g] * inv, O[t][4 * g + 1] * inv, O[t][4 * g + 2] * inv,
-                                          O[t][4 * g + 3] * inv};
-                        if (wi > 0) val = *p + val;
-                        *p = val;
-                    }
-            }
-        } else if (qrow < Lw) {
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 *p = reinterpret_cast<f32x4 *>(dst + 32 * t + 8 * g + 4 * hh);
+                    f32x4 val = f32x4{O[t][4 * g] * inv, O[t][4 * g + 1] * inv, O[t][4 * g + 2] * inv,
+                                      O[t][4 * g + 3] * inv};
+                    if (wi > 0) val = *p + val;
+                    *p = val;
+                }
+        } else if (qrow < nv) {
             uint16_t *dst = out + qtrow * rs + hd;
 #pragma unroll
             for (int t = 0; t < VS::DT; ++t)

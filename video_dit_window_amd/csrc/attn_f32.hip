@@ -5,11 +5,13 @@
 // [video window; replicated text].  "Parallelize new models with USP (text
 // replica)", section "3. Attention with USP": plain SDPA, no mask, no dropout.
 //
-// Work items as in attn_bf16.hip: a video item is (window, head, 64 video
-// query rows) and writes `out`; a text item is (chunk of consecutive
-// windows, head, 64 text query rows): its queries attend over each window of
-// the chunk in turn and the normalised outputs T_w are summed in window order
-// into the chunk's float32 partial of the workspace.  Four lanes share a
+// Work items as in attn_bf16.hip: a video item is (window, head, 64 query
+// rows) -- of the window's video rows, or of its joint rows [video; text]
+// (the text rows' outputs stored to the window's float32 partial) -- and
+// writes `out`; a text item is (chunk of consecutive windows, head, 64 text
+// query rows): its queries attend over each window of the chunk in turn and
+// the normalised outputs T_w are summed in window order into the chunk's
+// float32 partial of the workspace.  Four lanes share a
 // query, each holding a quarter of the head dimension (element d = 16*e +
 // 4*sub + 0..3 for lane `sub`), so a K/V row read from LDS is one 64-byte
 // broadcast per quarter.  Keys stream through LDS in tiles of 32 rows with an
@@ -46,14 +48,18 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
     const int64_t rs = int64_t(H) * D;  // row stride (elements)
     const int tid = threadIdx.x, sub = tid & 3, qi = tid >> 2;
     const int qrow = qt * kBM + qi;
-    const int nq = text ? Lt : it.win.lw;
+    // nv video rows of the window, then (text and joint items) text rows
+    const bool joint = !text && it.chunk >= 0;
+    const int nv = text ? 0 : it.win.lw;
+    const int nq = nv + (text || joint ? Lt : 0);
 
     // Query row (zeros past the end of the item's query rows).
     f32x4 qv[E];
     const float *qp = nullptr;
     if (qrow < nq) {
-        const int64_t r = text ? int64_t(qrow) : (ids ? int64_t(ids[it.win.off + qrow]) : int64_t(it.win.off) + qrow);
-        qp = (text ? tq : q) + r * rs + int64_t(h) * D;
+        const int64_t r = qrow >= nv ? int64_t(qrow - nv)
+                                     : (ids ? int64_t(ids[it.win.off + qrow]) : int64_t(it.win.off) + qrow);
+        qp = (qrow >= nv ? tq : q) + r * rs + int64_t(h) * D;
     }
 #pragma unroll
     for (int e = 0; e < E; ++e)
@@ -134,10 +140,11 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(
 
         if (qrow >= nq) continue;
         const float inv = 1.0f / l_run;
-        if (text) {
-            // the chunk's partial: written by its first window, added to by
-            // the later ones in window order (same thread, same addresses)
-            float *dst = ws + ((int64_t(it.chunk) * Lt + qrow) * H + h) * D;
+        if (qrow >= nv) {
+            // the partial `chunk`: a text item writes it on its chunk's first
+            // window and adds the later ones in window order (same thread,
+            // same addresses); a joint item is its window's only writer
+            float *dst = ws + ((int64_t(it.chunk) * Lt + (qrow - nv)) * H + h) * D;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 f32x4 *p = reinterpret_cast<f32x4 *>(dst + 16 * e + 4 * sub);

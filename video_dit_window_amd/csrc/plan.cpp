@@ -174,21 +174,29 @@ int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int orde
     // Cost of a query tile over one window: its 64-key tiles.
     auto key_tiles = [&](int32_t w) { return ceil_div(int64_t(wins[size_t(w)].lw) + text_len, kKeyTile); };
     const int64_t text_tiles = ceil_div(text_len, bm);
+    const int G = text_len > 0 ? n_chunks : 0;
+    const bool per_window = G == p.nwin;
+    // With one partial per window, a window whose text rows fit in the empty
+    // part of its last video query tile takes tiles of the joint sequence
+    // [video rows; text rows] (item chunk = w); the others keep a video
+    // sequence and text items of their own (which then run full tiles).
+    auto joint = [&](int32_t w) {
+        const int64_t lw = wins[size_t(w)].lw;
+        return per_window && ceil_div(lw + text_len, bm) < ceil_div(lw, bm) + text_tiles;
+    };
+    auto query_rows = [&](int32_t w) { return int64_t(wins[size_t(w)].lw) + (joint(w) ? text_len : 0); };
     if (text_tiles > 0xFFFF) return fail(WSP_ERANGE, "text_len needs more than 65535 query tiles");
     for (int32_t w = 0; w < p.nwin; ++w)
-        if (ceil_div(wins[size_t(w)].lw, bm) > 0xFFFF)
+        if (ceil_div(query_rows(w), bm) > 0xFFFF)
             return fail(WSP_ERANGE, "window " + std::to_string(w) + " needs more than 65535 query tiles");
 
-    // Groups of items that read the same K/V: all video query tiles of a
-    // (window, head), with that window's text items when every chunk is a
-    // single window; otherwise all text query tiles of a (chunk, head) form
-    // a group of their own.  Each group has a cost in key tiles.
+    // Groups of items that read the same K/V: all query tiles of a (window,
+    // head); in chunk mode all text query tiles of a (chunk, head) form a
+    // group of their own.  Each group has a cost in key tiles.
     struct Group {
         int64_t cost;
         std::vector<ItemDesc> items;
     };
-    const int G = text_len > 0 ? n_chunks : 0;
-    const bool per_window = G == p.nwin;
     auto text_items = [&](int c, int h, std::vector<ItemDesc> &out) {
         const int w0 = chunk_begin(c, p.nwin, G), w1 = chunk_begin(c + 1, p.nwin, G);
         for (int64_t t = 0; t < text_tiles; ++t) {
@@ -217,17 +225,19 @@ int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int orde
                          [](const Group &a, const Group &b) { return a.cost > b.cost; });
     }
     for (int32_t w : worder) {
-        const int64_t tiles = ceil_div(wins[size_t(w)].lw, bm);
+        const int64_t tiles = ceil_div(query_rows(w), bm);
+        const bool own_text = per_window && !joint(w);
         for (int h = 0; h < n_heads; ++h) {
-            Group g{(tiles + (per_window ? text_tiles : 0)) * key_tiles(w), {}};
+            Group g{(tiles + (own_text ? text_tiles : 0)) * key_tiles(w), {}};
             for (int64_t t = 0; t < tiles; ++t) {
                 ItemDesc d{};
                 d.w = w;
                 d.hq = (h << 16) | int(t);
+                d.chunk = joint(w) ? w : -1;
                 d.win = wins[size_t(w)];
                 g.items.push_back(d);
             }
-            if (per_window) text_items(w, h, g.items);
+            if (own_text) text_items(w, h, g.items);
             groups.push_back(std::move(g));
         }
     }

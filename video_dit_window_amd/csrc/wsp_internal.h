@@ -17,12 +17,14 @@ namespace wsp {
 
 // Text outputs are reduced over windows in fixed chunks: the windows of a
 // plan split into G runs of consecutive ids, each summed (float32, id order)
-// into one partial of the workspace by the text work items, and the partials
-// are added in chunk order by the text-mean kernel.  G is
-// min(n_windows, kTextChunks) (the workspace every call accepts), or
-// n_windows -- one partial per window -- when the caller's workspace holds
-// that many: each text item then covers a single window and runs beside that
-// window's video items, sharing their K/V in L2.
+// into one partial of the workspace, and the partials are added in chunk
+// order by the text-mean kernel.  G is min(n_windows, kTextChunks) (the
+// workspace every call accepts): text work items then loop over a chunk's
+// windows.  Or G = n_windows -- one partial per window -- when the caller's
+// workspace holds that many: a window's text rows are then queried beside its
+// video rows, from the same K/V stream on the same XCD -- in the same query
+// tiles (the joint sequence [video; text] cut into tiles) where that saves a
+// tile, else by text items of that one window.
 constexpr int kTextChunks = 16;
 inline int text_chunks(int n_windows) { return n_windows < kTextChunks ? n_windows : kTextChunks; }
 // First window of chunk c (chunk c covers windows chunk_begin(c) ..
@@ -42,8 +44,10 @@ struct alignas(16) WinDesc {
 
 // Work item of the attention kernels, resolved on the host so that a work
 // group starts with one scalar load.
-//  video item (nwin == 0): query tile `hq & 0xFFFF` of the video rows of
-//    window w, head hq >> 16; the window's rows in `win`;
+//  video item (nwin == 0): query tile `hq & 0xFFFF` of window w, head
+//    hq >> 16; the window's rows in `win`.  chunk < 0: tiles of the video
+//    rows; chunk >= 0: tiles of the joint query rows [video rows; text rows],
+//    the normalised outputs of the text rows stored to partial `chunk`;
 //  text item (nwin > 0): query tile `hq & 0xFFFF` of the text rows, head
 //    hq >> 16, attended in turn over windows w .. w + nwin - 1 (rows from the
 //    per-plan WinDesc table); the normalised outputs are summed into the
@@ -105,9 +109,10 @@ void window_positions(const wsp_plan_t &p, std::vector<int32_t> &pos);
 // Window rows as the attention kernels address them (gather: canonical-order
 // tensors, vrow0 = the window's smallest canonical id).
 void window_descs(const wsp_plan_t &p, bool gather, std::vector<WinDesc> &wins);
-// Attention work list (video items of every (window, head), text items of
-// every (chunk, head, text tile)), ordered for dispatch; returns its length
-// or a negative status.
+// Attention work list, ordered for dispatch: the query tiles of every
+// (window, head) -- of its video rows, or (one chunk per window, where that
+// saves a tile) of [video rows; text rows] -- and text items of every other
+// (chunk, head, text tile); returns its length or a negative status.
 int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int order, bool gather,
                 int n_chunks, std::vector<ItemDesc> &items);
 
