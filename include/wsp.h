@@ -151,9 +151,11 @@ int wsp_relayout(const void *x, void *y, int64_t row_bytes, const wsp_plan_t *sr
  * at floor(c * n_windows / G)).  0 when text_len == 0.  1080p-shaped layer
  * (20 x 128, 256 text tokens): 42 MB; 4K-shaped (512 text tokens): 84 MB.
  * A workspace of n_windows * text_len * n_heads * head_dim * 4 bytes or more
- * (262 MB at 1080p, 2.6 GB at 4K) selects one partial per window: each text
- * work item then covers one window and shares that window's K/V in L2 with
- * its video items (a few percent faster at 1080p).
+ * (262 MB at 1080p, 2.6 GB at 4K) selects one partial per window: a
+ * window's text rows are then queried beside its video rows -- in the same
+ * query tiles where that saves a tile -- sharing that window's K/V in L2
+ * (about 2% faster at 1080p).  The video output of the two modes may differ
+ * in the last bits (a wave's 32 query rows share their rescaling steps).
  * Errors: WSP_EINVAL (bad plan/shape/dtype), WSP_ERANGE.
  */
 int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, int text_len,
