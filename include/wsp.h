@@ -407,6 +407,20 @@ int wsp_window_attn_qk8(const wsp_plan_t *p, const void *q8, const void *k8, con
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * wsp_device_info -- how work groups reach the current device's dies: the
+ * number of XCDs (accelerated compute dies) a launch spreads over, and
+ * whether work group b runs on XCD b mod that count.  Probed once per
+ * device by a one-wave kernel reading each work group's XCC_ID register
+ * (synchronous, like the first upload of a plan's tables; the first
+ * attention call on a device runs the same probe).  The XCD-grouped work
+ * list (WSP_ORDER_LPT_XCD) is used only where the count is 8 and the
+ * placement round-robin; otherwise the attention calls fall back to
+ * WSP_ORDER_LPT.
+ * Errors: WSP_EINVAL (NULL pointers), WSP_ENOMEM, WSP_EDEVICE.
+ */
+int wsp_device_info(int *n_xcds, int *xcd_round_robin);
+
+/*
  * wsp_set_attn_order -- process-wide dispatch order of wsp_window_attn
  * (enum wsp_order; default WSP_ORDER_LPT_XCD).  "Window-Aligned Sequence
  * Parallelism (SeedVR2)", section "Planner": ragged windows are balanced by
@@ -455,7 +469,7 @@ const char *wsp_last_error(void);
 /* wsp_version -- ABI version of this header (major*10000 + minor*100 + patch). */
 int wsp_version(void);
 
-#define WSP_VERSION 20100
+#define WSP_VERSION 20200
 
 #ifdef __cplusplus
 }

@@ -65,6 +65,7 @@ hipError_t launch_gemm_bf16(const void *, const void *, void *, const void *, in
     reached("gemm");
 }
 hipError_t launch_text_mean(const float *, void *, int64_t, int, int, int, hipStream_t) { reached("text_mean"); }
+hipError_t launch_xcd_probe(int32_t *, int, hipStream_t) { reached("xcd_probe"); }
 }  // namespace wsp
 
 using namespace wsp;
@@ -286,6 +287,9 @@ static void check_arguments() {
     CHECK(wsp_linear(a, b, nullptr, a, 8, 256, 64, WSP_BF16, nullptr) == WSP_EINVAL);
     CHECK(wsp_linear(a, b, nullptr, o, 0, 256, 64, WSP_BF16, nullptr) == WSP_OK);
     CHECK(wsp_set_attn_order(7) == WSP_EINVAL);
+    int nx = 0, rr = 0;
+    CHECK(wsp_device_info(nullptr, &rr) == WSP_EINVAL);
+    CHECK(wsp_device_info(&nx, nullptr) == WSP_EINVAL);
     CHECK(wsp_set_attn_schedule(1) == WSP_EINVAL);
     CHECK(wsp_last_error()[0] != '\0');
     wsp_plan_free(other);

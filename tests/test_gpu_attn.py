@@ -417,3 +417,14 @@ def test_4k_regular_sampled(gpu):
     """4K grid, regular layout (324 windows of 2520-3240 rows; the last
     temporal window is 7 of the 31 frames deep)."""
     sampled_check(I.WORKLOADS["4k_bf16"], "regular", heads_full_text=[11], text_dtype=np.float32)
+
+
+def test_xcd_placement_probe(gpu):
+    """The XCD-grouped work list assumes work group b runs on XCD b mod 8;
+    the library probes that once per device (XCC_ID of each work group) and
+    uses the grouping only where it holds.  On an MI355X the probe must find
+    the 8 dies of the device in round-robin order."""
+    info = W.device_info()
+    log(f"  device: {info}")
+    assert info == {"n_xcds": 8, "xcd_round_robin": True}, info
+

@@ -199,6 +199,13 @@ def test_attn_order_option():
         W.set_attn_order(o)
 
 
+def test_device_info_argument_errors():
+    L = raw()
+    n = ctypes.c_int32()
+    assert L.wsp_device_info(None, ctypes.byref(n)) == -1
+    assert L.wsp_device_info(ctypes.byref(n), None) == -1
+
+
 def test_rope_attention_argument_errors():
     """wsp_window_attn_rope / _workspace validate before any device work."""
     p = W.Plan(5, 20, 36, 2, 3, 3, W.REGULAR)

@@ -52,6 +52,7 @@ _SIGNATURES = {
                                                     _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "wsp_linear": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp]),
     "wsp_set_attn_order": (_c_int, [_c_int]),
+    "wsp_device_info": (_c_int, [_i32p, _i32p]),
     "wsp_set_attn_schedule": (_c_int, [_c_int]),
     "wsp_last_error": (ctypes.c_char_p, []),
     "wsp_version": (_c_int, []),
@@ -329,6 +330,14 @@ def rope_text(x, theta=None, out=None, stream=None):
         _dev_ptr(x, "x"), _dev_ptr(out, "out"), x.shape[0], x.shape[1], x.shape[2], _dtype_code(x.dtype),
         ctypes.c_float(0.0 if theta is None else theta), _stream(stream)))
     return out
+
+
+def device_info():
+    """wsp_device_info on the current device: {"n_xcds": XCD count,
+    "xcd_round_robin": whether work group b runs on XCD b mod n_xcds}."""
+    n, rr = ctypes.c_int32(), ctypes.c_int32()
+    _check("wsp_device_info", lib().wsp_device_info(ctypes.byref(n), ctypes.byref(rr)))
+    return {"n_xcds": n.value, "xcd_round_robin": bool(rr.value)}
 
 
 def window_attn_rope_workspace(p: Plan, n_heads, text_len, per_window=True) -> int:

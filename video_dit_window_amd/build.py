@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libwsp.so")
 ARCH = "gfx950"
 
 SOURCES = ["plan.cpp", "abi.cpp", "relayout.hip", "rope.hip", "text_mean.hip", "attn_f32.hip",
-           "attn_bf16.hip", "fp8.hip", "gemm_bf16.hip"]
+           "attn_bf16.hip", "fp8.hip", "gemm_bf16.hip", "xcd_probe.hip"]
 
 # Packed-FP32 VALU ops are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

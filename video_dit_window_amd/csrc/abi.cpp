@@ -162,6 +162,50 @@ int device_layout_positions(wsp_plan_t &p, int dev, int32_t **out) {
     return WSP_OK;
 }
 
+namespace {
+struct XcdInfo {
+    int n = 0;
+    bool round_robin = false;
+};
+std::mutex g_xcd_mu;
+std::map<int, XcdInfo> g_xcd;  // device ordinal -> probed work-group placement
+}  // namespace
+
+int device_xcds(int dev, int *n_xcds, bool *round_robin, bool probe) {
+    std::lock_guard<std::mutex> lk(g_xcd_mu);
+    auto it = g_xcd.find(dev);
+    if (it == g_xcd.end() && !probe) {  // not known yet: report the assumed placement
+        *n_xcds = 8;
+        *round_robin = true;
+        return WSP_OK;
+    }
+    if (it == g_xcd.end()) {
+        // One synchronous probe per device (like the first table upload):
+        // 1024 one-wave work groups report the XCD they ran on.
+        constexpr int kBlocks = 1024;
+        int32_t *d = nullptr;
+        hipError_t e = hipMalloc(reinterpret_cast<void **>(&d), kBlocks * sizeof(int32_t));
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(e == hipErrorOutOfMemory ? WSP_ENOMEM : WSP_EDEVICE,
+                        std::string("hipMalloc of the XCD probe failed: ") + hipGetErrorString(e));
+        }
+        std::vector<int32_t> xcc(kBlocks, -1);
+        e = launch_xcd_probe(d, kBlocks, nullptr);
+        if (e == hipSuccess) e = hipMemcpy(xcc.data(), d, kBlocks * sizeof(int32_t), hipMemcpyDeviceToHost);
+        (void)hipFree(d);
+        if (e != hipSuccess) return hip_fail(e, "XCD probe");
+        XcdInfo info;
+        info.n = 1 + *std::max_element(xcc.begin(), xcc.end());
+        info.round_robin = true;
+        for (int b = 0; b < kBlocks; ++b) info.round_robin = info.round_robin && xcc[size_t(b)] == b % info.n;
+        it = g_xcd.emplace(dev, info).first;
+    }
+    *n_xcds = it->second.n;
+    *round_robin = it->second.round_robin;
+    return WSP_OK;
+}
+
 int device_windows(wsp_plan_t &p, int dev, bool gather, WinDesc **out) {
     std::lock_guard<std::mutex> lk(p.mu);
     DeviceTables &t = p.dev[dev];
@@ -543,7 +587,7 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
     // min(n_windows, 16) chunks.
     const size_t per_part = size_t(text_len) * size_t(n_heads) * size_t(head_dim) * 4u;
     const int n_chunks = workspace_bytes >= per_part * size_t(p->nwin) ? p->nwin : text_chunks(p->nwin);
-    const int order = g_attn_order.load();
+    int order = g_attn_order.load();
     // Short windows (joint sequences averaging < 1024 rows) take 128-row
     // query tiles: a window's partly empty last tile then wastes less.
     const int sched = g_attn_sched.load();
@@ -554,6 +598,16 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
 
     int dev = 0;
     WSP_HIP(hipGetDevice(&dev));
+    if (order == WSP_ORDER_LPT_XCD) {
+        // The XCD grouping of the work list holds only where work group b
+        // runs on XCD b mod 8; elsewhere plain largest-first order.
+        // (the no-allocation entry point never probes: its tables, built by
+        // an earlier wsp_window_attn_ex call, already reflect the probe)
+        int n_xcds = 0;
+        bool rr = false;
+        if ((rc = device_xcds(dev, &n_xcds, &rr, !no_alloc))) return rc;
+        if (n_xcds != 8 || !rr) order = WSP_ORDER_LPT;
+    }
     ItemDesc *items = nullptr;
     WinDesc *wins = nullptr;
     int n_items = 0;
@@ -772,6 +826,18 @@ int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, 
     if (y == x || y == w) return fail(WSP_EINVAL, "y must not alias x or w");
     hipError_t e = launch_gemm_bf16(x, w, y, r, M, N, K, hipStream_t(stream));
     if (e != hipSuccess) return hip_fail(e, "linear kernel launch");
+    return WSP_OK;
+}
+
+int wsp_device_info(int *n_xcds, int *xcd_round_robin) {
+    g_last_error.clear();
+    if (!n_xcds || !xcd_round_robin) return fail(WSP_EINVAL, "n_xcds and xcd_round_robin must be non-NULL");
+    int dev = 0;
+    WSP_HIP(hipGetDevice(&dev));
+    bool rr = false;
+    int rc = device_xcds(dev, n_xcds, &rr, true);
+    if (rc) return rc;
+    *xcd_round_robin = rr ? 1 : 0;
     return WSP_OK;
 }
 

@@ -178,6 +178,12 @@ int gemm_bf16_tile_n();
 int gemm_bf16_tile_k();
 hipError_t launch_gemm_bf16(const void *x, const void *w, void *y, const void *r, int64_t M, int N,
                             int K, hipStream_t s);
+// xcd_probe.hip: xcc[b] = the XCD that work group b of an n_blocks launch ran on.
+hipError_t launch_xcd_probe(int32_t *xcc, int n_blocks, hipStream_t s);
+// abi.cpp: the XCD count of device dev and whether work group b of a launch
+// runs on XCD b mod that count (probed once per device; without probe, a
+// device not probed yet reports 8 and round-robin).
+int device_xcds(int dev, int *n_xcds, bool *round_robin, bool probe);
 // text_mean.hip: txt_out = (sum of the n_parts float32 partials, in order) /
 // n_windows, rounded once to dtype.
 hipError_t launch_text_mean(const float *ws, void *txt_out, int64_t per_part, int n_parts,
