@@ -84,28 +84,37 @@ __device__ __host__ constexpr int kswz(int r) {
 // Window-local rotary embedding of the queries inside the kernel (ROPE).
 constexpr int kRopePairs = 21;  // pairs per axis block (42 of 128 channels)
 
-// Rotation of one 16-byte chunk: bf16 channels 8c .. 8c+7, i.e. pairs 4c ..
-// 4c+3 of the row (pair k of axis block k / 21), of a row at window offset
-// pk = dt | dh << 10 | dw << 21, i.e. axial positions (Lt + dt, dh, dw);
+// Rotation of query chunk c = 2S + hh of a row: bf16 channels 8c .. 8c+7,
+// i.e. pairs 8S + 4hh + e (e < 4; pair k of axis block k / 21), with the
+// row's table offsets p21[a] = position_a * 21 (positions Lt + dt, dh, dw);
 // cs = (cos, sin) of 21 pairs per position.  Pairs 0..62 turn, pair 63
-// (channels 126, 127) passes through.  Same float32 steps and one rounding
-// to bf16 as the stand-alone rotation kernel.
-__device__ inline u32x4 rope_chunk(u32x4 w, int c, uint32_t pk, int Lt, const float2 *__restrict__ cs) {
-    const int pos[3] = {Lt + int(pk & 1023u), int((pk >> 10) & 2047u), int(pk >> 21)};
+// (channels 126, 127) passes through.  The axis and in-block index of each
+// pair are compile-time up to the lane's hh.  Same float32 steps and one
+// rounding to bf16 as the stand-alone rotation kernel.
+template <int S>
+__device__ inline u32x4 rope_q_chunk(u32x4 w, int hh, const int (&p21)[3], const float2 *__restrict__ cs) {
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int k = 4 * c + e;
-        const int ax = (k * 3121) >> 16;  // k / 21 for 0 <= k < 64
-        if (ax < 3) {
-            const float2 t = cs[pos[ax] * kRopePairs + (k - kRopePairs * ax)];
-            const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
-            o[e] = pack_bf16(fmaf(x0, t.x, -x1 * t.y), fmaf(x0, t.y, x1 * t.x));
-        } else {
-            o[e] = w[e];
-        }
+        const int k0 = 8 * S + e, k1 = k0 + 4;
+        const int ax0 = k0 / kRopePairs, ax1 = k1 / kRopePairs;
+        const int i0 = k0 - kRopePairs * ax0, i1 = k1 - kRopePairs * ax1;
+        int idx;
+        if (ax0 == ax1) idx = p21[ax0] + i0 + 4 * hh;
+        else idx = hh ? (ax1 < 3 ? p21[ax1] + i1 : 0) : p21[ax0] + i0;
+        const float2 t = cs[idx];
+        const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
+        const uint32_t r = pack_bf16(fmaf(x0, t.x, -x1 * t.y), fmaf(x0, t.y, x1 * t.x));
+        o[e] = (ax1 >= 3 && hh) ? w[e] : r;  // pair 63 (channels 126, 127) passes through
     }
     return o;
+}
+template <int S, int N>
+__device__ inline void rope_q_row(bf16x8 (&Qr)[N], int hh, const int (&p21)[3], const float2 *__restrict__ cs) {
+    if constexpr (S < N) {
+        Qr[S] = __builtin_bit_cast(bf16x8, rope_q_chunk<S>(__builtin_bit_cast(u32x4, Qr[S]), hh, p21, cs));
+        rope_q_row<S + 1, N>(Qr, hh, p21, cs);
+    }
 }
 
 // GATHER: q, k, v and out hold rows in canonical token order; video row r
@@ -188,10 +197,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             if constexpr (ROPE) {
                 // video queries rotated in registers (chunk 2s + hh of the row)
                 if (qrow < nv) {
-#pragma unroll
-                    for (int s = 0; s < VS::KSTEPS; ++s)
-                        Qr[s] = __builtin_bit_cast(
-                            bf16x8, rope_chunk(__builtin_bit_cast(u32x4, Qr[s]), 2 * s + hh, qpk, Lt, rope_cs));
+                    const int p21[3] = {(Lt + int(qpk & 1023u)) * kRopePairs, int((qpk >> 10) & 2047u) * kRopePairs,
+                                        int(qpk >> 21) * kRopePairs};
+                    rope_q_row<0, VS::KSTEPS>(Qr, hh, p21, rope_cs);
                 }
             }
         }
