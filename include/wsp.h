@@ -23,7 +23,8 @@
  *     synchronous step is the first device use of a plan (or of a plan pair
  *     in wsp_relayout, or of a new head/text-length shape in
  *     wsp_window_attn) on a device: its index tables are then copied to that
- *     device once and cached with the plan.
+ *     device once and cached with the plan; and the first attention call on
+ *     a device probes how work groups reach its dies (wsp_device_info).
  *   - Tensors are dense row-major.  A "row" is one token: [n_heads, head_dim]
  *     elements for attention tensors, `row_bytes` bytes for wsp_relayout.
  *   - Calls on different streams that share a plan are safe; output buffers
@@ -62,7 +63,9 @@ enum wsp_status {
 /* Order in which wsp_window_attn hands work to the GPU (tuning/measurement). */
 enum wsp_order {
     WSP_ORDER_LPT_XCD = 0, /* largest window first, (window, head) groups spread
-                              over the 8 XCDs so each group's tiles share one L2 */
+                              over the 8 XCDs so each group's tiles share one L2
+                              (where wsp_device_info finds work groups placed
+                              round-robin over 8 XCDs; else as WSP_ORDER_LPT)  */
     WSP_ORDER_LPT = 1,     /* largest window first, plain block order            */
     WSP_ORDER_ID = 2       /* window id order                                    */
 };
