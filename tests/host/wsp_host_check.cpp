@@ -158,7 +158,7 @@ static void check_plan(int T, int H, int W, int nt, int nh, int nw, int method) 
                         const bool per_window = Lt > 0 && G == int(nwin);
                         auto joint = [&](int32_t w) {
                             const int64_t lw = off[size_t(w) + 1] - off[size_t(w)];
-                            return per_window && (lw + Lt + bm - 1) / bm < (lw + bm - 1) / bm + (Lt + bm - 1) / bm;
+                            return per_window && (lw + Lt + 255) / 256 < (lw + 255) / 256 + (Lt + 255) / 256;
                         };
                         for (const ItemDesc &it : items) {
                             if (it.w < 0) continue;

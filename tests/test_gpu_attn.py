@@ -113,6 +113,10 @@ MID = [  # (name, T, H, W, nt, nh, nw, heads, D, Lt)
     # windows of at most 45 tokens: a joint sequence of one 64-key tile
     ("tiny_windows_bf16", 4, 20, 36, 4, 9, 9, 2, 128, 0),
     ("tiny_windows_text_d64", 4, 20, 36, 4, 9, 9, 2, 64, 19),
+    # 300 text rows: more than one query tile of text (joint tiles whose text
+    # rows span several tiles with one partial per window; multi-tile text
+    # items over chunks of windows otherwise)
+    ("long_text_bf16", 6, 30, 52, 2, 3, 3, 2, 128, 300),
 ]
 
 

@@ -179,10 +179,16 @@ int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int orde
     // With one partial per window, a window whose text rows fit in the empty
     // part of its last video query tile takes tiles of the joint sequence
     // [video rows; text rows] (item chunk = w); the others keep a video
-    // sequence and text items of their own (which then run full tiles).
+    // sequence and text items of their own (which then run full tiles).  The
+    // test uses 256-row tiles whatever bm is, so that every tile height puts
+    // the same rows in each 32-row wave (a wave's rows share its rescaling
+    // steps): the schedules stay bit-identical.  Joint tiles never take more
+    // tiles than separate ones.
+    constexpr int64_t kJointTile = 256;
     auto joint = [&](int32_t w) {
         const int64_t lw = wins[size_t(w)].lw;
-        return per_window && ceil_div(lw + text_len, bm) < ceil_div(lw, bm) + text_tiles;
+        return per_window &&
+               ceil_div(lw + text_len, kJointTile) < ceil_div(lw, kJointTile) + ceil_div(text_len, kJointTile);
     };
     auto query_rows = [&](int32_t w) { return int64_t(wins[size_t(w)].lw) + (joint(w) ? text_len : 0); };
     if (text_tiles > 0xFFFF) return fail(WSP_ERANGE, "text_len needs more than 65535 query tiles");
