@@ -386,12 +386,12 @@ def main():
     if ms_fused is not None:
         f_ms = [a.elapsed_time(b) for a, b in ev["fused_attn"]]
         head_ms, head_avg, io = ms_fused, float(np.mean(f_ms)), "canonical"
-        kernel = "attn_bf16_kernel<128, 8, true> (canonical-order I/O, one work group per item; + " \
+        kernel = "attn_bf16_kernel<128, 8, true> (canonical-order I/O, resident work groups taking items from per-XCD queues; + " \
                  "text_mean_kernel in the same call)"
         breakdown = {"attention+text_mean": round(sum(f_ms) / args.steps, 4)}
     else:
         head_ms, head_avg, io = ms_step, attn_avg_ms, "layout"
-        kernel = "attn_bf16_kernel<128, 8, false> (one work group per item; + text_mean_kernel in the same call)"
+        kernel = "attn_bf16_kernel<128, 8, false> (resident work groups taking items from per-XCD queues; + text_mean_kernel in the same call)"
         breakdown = explicit["breakdown_ms_per_step"]
     value = step_flops / (head_ms * 1e-3) / 1e12
     attn_tflops = per_call_flops / (head_avg * 1e-3) / 1e12

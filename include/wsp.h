@@ -75,7 +75,9 @@ enum wsp_order {
 enum wsp_schedule {
     WSP_SCHED_AUTO = 0,         /* by mean window length (wsp_set_attn_schedule) */
     WSP_SCHED_PER_ITEM = 2,     /* one work group per 256-query-row item         */
-    WSP_SCHED_PER_ITEM_128 = 3  /* one work group per 128-query-row item         */
+    WSP_SCHED_PER_ITEM_128 = 3, /* one work group per 128-query-row item         */
+    WSP_SCHED_QUEUE = 4,        /* resident work groups, 256-row items in turn   */
+    WSP_SCHED_QUEUE_128 = 5     /* resident work groups, 128-row items in turn   */
 };
 
 /*
@@ -148,13 +150,15 @@ int wsp_relayout(const void *x, void *y, int64_t row_bytes, const wsp_plan_t *sr
 
 /*
  * wsp_window_attn_workspace -- the smallest device workspace (bytes)
- * wsp_window_attn accepts: G * text_len * n_heads * head_dim * 4 with
+ * wsp_window_attn accepts: Q + G * text_len * n_heads * head_dim * 4 with
  * G = min(n_windows, 16), one float32 partial text sum per chunk of
  * consecutive windows (the windows split into G runs of ids, run c starting
- * at floor(c * n_windows / G)).  0 when text_len == 0.  1080p-shaped layer
- * (20 x 128, 256 text tokens): 42 MB; 4K-shaped (512 text tokens): 84 MB.
- * A workspace of n_windows * text_len * n_heads * head_dim * 4 bytes or more
- * (262 MB at 1080p, 2.6 GB at 4K) selects one partial per window: a
+ * at floor(c * n_windows / G)), and Q = 256 bytes for WSP_BF16 (the work
+ * queue's ticket counters, cleared by each call), 0 for WSP_F32.  1080p-
+ * shaped layer (20 x 128, 256 text tokens): 42 MB; 4K-shaped (512 text
+ * tokens): 84 MB.  A workspace of Q + n_windows * text_len * n_heads *
+ * head_dim * 4 bytes or more (262 MB at 1080p, 2.6 GB at 4K) selects one
+ * partial per window: a
  * window's text rows are then queried beside its video rows -- in the same
  * query tiles where that saves a tile -- sharing that window's K/V in L2
  * (about 2% faster at 1080p).  The video output of the two modes may differ
@@ -200,10 +204,11 @@ int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, in
  * txt_out           device, [text_len, n_heads, head_dim] of dtype (NULL
  *                   allowed when text_len == 0)
  * workspace         device, >= wsp_window_attn_workspace() bytes, 16-byte
- *                   aligned; contents on entry are ignored; it holds the
- *                   chunk sums until the text-mean kernel of the same call
- *                   has read them (calls sharing a workspace must be ordered
- *                   on one stream)
+ *                   aligned (may be NULL only for WSP_F32 with text_len ==
+ *                   0); contents on entry are ignored; it holds the work
+ *                   queue's counters and the chunk sums until the kernels
+ *                   of the same call have read them (calls sharing a
+ *                   workspace must be ordered on one stream)
  * Errors: WSP_EINVAL (pointer NULL or not 16-byte aligned, unsupported
  * head_dim/dtype, n_heads out of range), WSP_ERANGE (a window longer than
  * the kernel's tile index range), WSP_EWORKSPACE, WSP_ENOMEM, WSP_EDEVICE.
@@ -438,11 +443,16 @@ int wsp_set_attn_order(int order);
  * WSP_SCHED_PER_ITEM: one work group (8 wavefronts) per 256-query-row item.
  * WSP_SCHED_PER_ITEM_128: one work group (4 wavefronts, two per compute
  * unit) per 128-query-row item: less of a window's last query tile is
- * empty.  WSP_SCHED_AUTO: WSP_SCHED_PER_ITEM_128 when a window's joint
- * sequence averages fewer than 1024 rows, else WSP_SCHED_PER_ITEM.  Both run
- * the same per-wavefront arithmetic in the same order, so results are
- * bit-identical; the order set by wsp_set_attn_order applies to both.
- * Errors: WSP_EINVAL.
+ * empty.  WSP_SCHED_QUEUE / WSP_SCHED_QUEUE_128: the same items taken in
+ * turn by resident work groups (as many as fit on the device), each from
+ * the list of its XCD first (with WSP_ORDER_LPT_XCD) and then from the
+ * others until all are empty; the ticket counters sit in the workspace.  An
+ * item's start-up then overlaps the previous item's output stores and no
+ * work group waits for a dispatch.  WSP_SCHED_AUTO: WSP_SCHED_QUEUE_128 when
+ * a window's joint sequence averages fewer than 1024 rows, else
+ * WSP_SCHED_QUEUE.  All four run the same per-wavefront arithmetic in the
+ * same order, so results are bit-identical; the order set by
+ * wsp_set_attn_order applies to all.  Errors: WSP_EINVAL.
  */
 int wsp_set_attn_schedule(int schedule);
 
@@ -472,7 +482,7 @@ const char *wsp_last_error(void);
 /* wsp_version -- ABI version of this header (major*10000 + minor*100 + patch). */
 int wsp_version(void);
 
-#define WSP_VERSION 20200
+#define WSP_VERSION 20300
 
 #ifdef __cplusplus
 }

@@ -45,7 +45,8 @@ int fp8_max_row_chunks() { return 2048; }
 hipError_t launch_relayout(const void *, void *, const int32_t *, int64_t, int64_t, hipStream_t) { reached("relayout"); }
 hipError_t launch_attn_bf16(int, bool, bool, const void *, const void *, const void *, const void *, const void *,
                             const void *, void *, float *, const int32_t *, const ItemDesc *, const WinDesc *, int,
-                            const float *, const float *, const RopeTables *, int, int, float, hipStream_t) {
+                            const float *, const float *, const RopeTables *, int, int, float, uint32_t *, int,
+                            hipStream_t) {
     reached("attn_bf16");
 }
 hipError_t launch_attn_f32(int, const float *, const float *, const float *, const float *, const float *,

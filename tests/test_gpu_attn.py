@@ -103,6 +103,10 @@ def test_mid_f32(gpu, D):
 
 
 # ------------------------------------------------------------------ bfloat16
+# bf16 work distributions (same per-wavefront arithmetic in each)
+SCHEDS = {"per_item": W.SCHED_PER_ITEM, "per_item_128": W.SCHED_PER_ITEM_128,
+          "queue": W.SCHED_QUEUE, "queue_128": W.SCHED_QUEUE_128}
+
 MID = [  # (name, T, H, W, nt, nh, nw, heads, D, Lt)
     ("mid_bf16", 6, 30, 52, 2, 3, 3, 3, 128, 40),
     ("mid_bf16_d64", 6, 30, 52, 2, 3, 3, 3, 64, 40),
@@ -151,7 +155,7 @@ def test_bf16_unscaled_inputs(gpu):
 
 
 @pytest.mark.parametrize("std", [4.0, 8.0])
-@pytest.mark.parametrize("sched", ["per_item", "per_item_128"])
+@pytest.mark.parametrize("sched", ["per_item", "per_item_128", "queue", "queue_128"])
 def test_bf16_large_scores(gpu, std, sched):
     """q, k, v of standard deviation 4 or 8: logits of standard deviation
     ~16 or ~64 (nearly one-hot softmax with near-tied keys in some rows).
@@ -162,7 +166,7 @@ def test_bf16_large_scores(gpu, std, sched):
     import torch
     w = I.custom(f"mid_large_{int(std)}", 6, 30, 52, 2, 3, 3, 2, 128, 40, "bf16", std=std,
                  index=340 + int(std))
-    W.set_attn_schedule({"per_item": W.SCHED_PER_ITEM, "per_item_128": W.SCHED_PER_ITEM_128}[sched])
+    W.set_attn_schedule(SCHEDS[sched])
     try:
         out, txt = run_full(w, "shifted", check_bf16)
         geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
@@ -183,21 +187,29 @@ def test_bf16_explicit_scale(gpu):
 
 
 @pytest.mark.parametrize("per_window", [True, False], ids=["per_window_text", "chunked_text"])
-def test_bf16_order_independent_and_deterministic(gpu, per_window):
+@pytest.mark.parametrize("sched", ["per_item", "queue"])
+def test_bf16_order_independent_and_deterministic(gpu, per_window, sched):
     """Results do not depend on the dispatch order, and repeat bit for bit
     (for either text reduction; the grid has 27 shifted windows, so the
-    minimum workspace gives 16 chunks of one or two windows)."""
+    minimum workspace gives 16 chunks of one or two windows).  In queue mode
+    the order decides which list (one per XCD, or a single one) an item is
+    taken from."""
     import torch
     w = I.custom("mid_order", 6, 30, 52, 2, 3, 3, 3, 128, 40, "bf16", index=330)
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
     p = W.Plan(*geo, W.SHIFTED)
     d = upload(I.qkv(w), "bf16")
     outs = []
-    for order in (W.ORDER_LPT_XCD, W.ORDER_LPT, W.ORDER_ID, W.ORDER_LPT_XCD):
-        W.set_attn_order(order)
-        o, t = W.window_attn(p, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"], per_window=per_window)
-        outs.append((o.clone(), t.clone()))
-    W.set_attn_order(W.ORDER_LPT_XCD)
+    W.set_attn_schedule(SCHEDS[sched])
+    try:
+        for order in (W.ORDER_LPT_XCD, W.ORDER_LPT, W.ORDER_ID, W.ORDER_LPT_XCD):
+            W.set_attn_order(order)
+            o, t = W.window_attn(p, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"],
+                                 per_window=per_window)
+            outs.append((o.clone(), t.clone()))
+    finally:
+        W.set_attn_order(W.ORDER_LPT_XCD)
+        W.set_attn_schedule(W.SCHED_AUTO)
     torch.cuda.synchronize()
     for o, t in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
@@ -208,9 +220,9 @@ def test_bf16_order_independent_and_deterministic(gpu, per_window):
 @pytest.mark.parametrize("canonical", [False, True], ids=["layout_io", "canonical_io"])
 @pytest.mark.parametrize("per_window", [True, False], ids=["per_window_text", "chunked_text"])
 def test_bf16_schedules_bit_identical(gpu, case, canonical, per_window):
-    """One work group per 256-row item and one per 128-row item run the same
-    per-wavefront arithmetic in the same order: identical bits, for both I/O
-    orders."""
+    """One work group per 256-row item, one per 128-row item, and resident
+    work groups taking either from a queue run the same per-wavefront
+    arithmetic in the same order: identical bits, for both I/O orders."""
     import torch
     w = I.custom(*case, "bf16", index=300 + MID.index(case))
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
@@ -218,10 +230,13 @@ def test_bf16_schedules_bit_identical(gpu, case, canonical, per_window):
     res = {}
     for method in (W.REGULAR, W.SHIFTED):
         p = W.Plan(*geo, method)
-        for sched in (W.SCHED_PER_ITEM, W.SCHED_PER_ITEM_128):
+        for sched in SCHEDS.values():
             W.set_attn_schedule(sched)
             try:
+                # outputs start as NaN: a row no item wrote cannot match
                 o, t = W.window_attn(p, d["q"], d["k"], d["v"], d["txt_q"], d["txt_k"], d["txt_v"],
+                                     out=torch.full_like(d["q"], float("nan")),
+                                     txt_out=torch.full_like(d["txt_q"], float("nan")),
                                      canonical=canonical, per_window=per_window)
             finally:
                 W.set_attn_schedule(W.SCHED_AUTO)
@@ -229,7 +244,7 @@ def test_bf16_schedules_bit_identical(gpu, case, canonical, per_window):
     torch.cuda.synchronize()
     for method in (W.REGULAR, W.SHIFTED):
         o1, t1 = res[(method, W.SCHED_PER_ITEM)]
-        for sched in (W.SCHED_PER_ITEM_128,):
+        for sched in (W.SCHED_PER_ITEM_128, W.SCHED_QUEUE, W.SCHED_QUEUE_128):
             o2, t2 = res[(method, sched)]
             assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"{w.name} {method} {sched}: video"
             if w.text_len:
@@ -238,9 +253,9 @@ def test_bf16_schedules_bit_identical(gpu, case, canonical, per_window):
 
 @pytest.mark.parametrize("canonical", [False, True], ids=["layout_io", "canonical_io"])
 def test_1080p_schedules_bit_identical(gpu, canonical):
-    """256-row and 128-row per-item schedules agree bit for bit on
-    the full 1080p grid (both layouts), in the launch configuration the
-    benchmark times."""
+    """256-row and 128-row items, one work group each or taken from a queue
+    by resident work groups, agree bit for bit on the full 1080p grid (both
+    layouts), in the launch configuration the benchmark times."""
     import torch
     w = I.WORKLOADS["1080p_bf16"]
     geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
@@ -254,10 +269,11 @@ def test_1080p_schedules_bit_identical(gpu, canonical):
     for method in (W.REGULAR, W.SHIFTED):
         p = W.Plan(*geo, method)
         outs = []
-        for sched in (W.SCHED_PER_ITEM, W.SCHED_PER_ITEM_128):
+        for sched in SCHEDS.values():
             W.set_attn_schedule(sched)
             try:
-                outs.append(W.window_attn(p, q, k, v, tq, tk, tv, canonical=canonical))
+                outs.append(W.window_attn(p, q, k, v, tq, tk, tv, out=torch.full_like(q, float("nan")),
+                                          txt_out=torch.full_like(tq, float("nan")), canonical=canonical))
             finally:
                 W.set_attn_schedule(W.SCHED_AUTO)
         torch.cuda.synchronize()

@@ -154,8 +154,11 @@ def test_window_attn_argument_errors():
     need = W.window_attn_workspace(p, 4, 64, 16, W.F32)
     assert need == min(p.n_windows, 16) * 16 * 4 * 64 * 4      # one float32 partial per chunk
     big = W.Plan(21, 68, 120, 4, 3, 3, W.REGULAR)                 # 100 windows: 16 chunks
-    assert W.window_attn_workspace(big, 20, 128, 256, W.BF16) == 16 * 256 * 20 * 128 * 4
-    assert W.window_attn_workspace(p, 4, 64, 0, W.BF16) == 0
+    # bf16: 256 more bytes for the kernel's work-queue counters
+    assert W.window_attn_workspace(big, 20, 128, 256, W.BF16) == 16 * 256 * 20 * 128 * 4 + 256
+    assert W.window_attn_workspace(big, 20, 128, 256, W.BF16, per_window=True) == 100 * 256 * 20 * 128 * 4 + 256
+    assert W.window_attn_workspace(p, 4, 64, 0, W.BF16) == 256
+    assert W.window_attn_workspace(p, 4, 64, 0, W.F32) == 0
 
 
 def test_rope_argument_errors():
@@ -185,10 +188,10 @@ def test_rope_argument_errors():
 
 def test_attn_schedule_option():
     L = raw()
-    assert L.wsp_set_attn_schedule(4) == -1
+    assert L.wsp_set_attn_schedule(6) == -1
     assert L.wsp_set_attn_schedule(-1) == -1
-    assert L.wsp_set_attn_schedule(1) == -1      # the removed persistent schedule
-    for sc in (W.SCHED_PER_ITEM, W.SCHED_PER_ITEM_128, W.SCHED_AUTO):
+    assert L.wsp_set_attn_schedule(1) == -1      # the removed static persistent schedule
+    for sc in (W.SCHED_PER_ITEM, W.SCHED_PER_ITEM_128, W.SCHED_QUEUE, W.SCHED_QUEUE_128, W.SCHED_AUTO):
         W.set_attn_schedule(sc)
 
 
@@ -219,7 +222,8 @@ def test_rope_attention_argument_errors():
     assert need.value == W.window_attn_workspace(p, 4, 128, 16, W.BF16) + rot
     assert L.wsp_window_attn_rope_workspace(p.handle, 4, 64, 16, W.BF16, ctypes.byref(need)) == -1
     assert L.wsp_window_attn_rope_workspace(p.handle, 4, 128, 16, W.F32, ctypes.byref(need)) == -1
-    assert W.window_attn_rope_workspace(p, 4, 16, per_window=True) == rot + p.n_windows * 16 * 4 * 128 * 4
+    # + 256 bytes of work-queue counters
+    assert W.window_attn_rope_workspace(p, 4, 16, per_window=True) == rot + p.n_windows * 16 * 4 * 128 * 4 + 256
 
     def call(pl=p, D=128, dt=W.BF16, ws=None, wb=0):
         return L.wsp_window_attn_rope(pl.handle, a, b, a, a, b, a, 4, D, 16, dt, f0, f0, 1, o, o, ws, wb, None)

@@ -5,7 +5,8 @@ The Python surface is a thin ctypes binding with the C entry points' names;
 all device work runs in libwsp's HIP kernels.
 """
 from ._lib import (BF16, CANONICAL, F32, IO_CANONICAL, IO_LAYOUT, ORDER_ID, ORDER_LPT, ORDER_LPT_XCD, REGULAR, SHIFTED,
-                   SCHED_AUTO, SCHED_PER_ITEM, SCHED_PER_ITEM_128, set_attn_schedule,
+                   SCHED_AUTO, SCHED_PER_ITEM, SCHED_PER_ITEM_128, SCHED_QUEUE, SCHED_QUEUE_128,
+                   set_attn_schedule,
                    LIB_PATH, Plan, WspError, canonical, fp8_amax, fp8_quantize, lib, linear, plan, relayout,
                    rope_relayout, rope_text, set_attn_order, version, window_attn, window_attn_noalloc, noalloc_per_window, window_attn_qk8,
                    window_attn_rope, window_attn_rope_workspace, device_info,
@@ -14,5 +15,5 @@ from ._lib import (BF16, CANONICAL, F32, IO_CANONICAL, IO_LAYOUT, ORDER_ID, ORDE
 __all__ = ["BF16", "CANONICAL", "F32", "IO_CANONICAL", "IO_LAYOUT", "ORDER_ID", "ORDER_LPT", "ORDER_LPT_XCD", "REGULAR",
            "SHIFTED", "LIB_PATH", "Plan", "WspError", "canonical", "lib", "plan", "relayout",
            "rope_relayout", "rope_text", "set_attn_order", "version", "window_attn", "window_attn_noalloc", "noalloc_per_window", "window_attn_workspace",
-           "fp8_amax", "fp8_quantize", "window_attn_qk8", "window_attn_rope", "window_attn_rope_workspace", "device_info", "SCHED_AUTO", "SCHED_PER_ITEM", "SCHED_PER_ITEM_128",
+           "fp8_amax", "fp8_quantize", "window_attn_qk8", "window_attn_rope", "window_attn_rope_workspace", "device_info", "SCHED_AUTO", "SCHED_PER_ITEM", "SCHED_PER_ITEM_128", "SCHED_QUEUE", "SCHED_QUEUE_128",
            "set_attn_schedule", "linear"]

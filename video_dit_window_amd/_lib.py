@@ -19,7 +19,7 @@ REGULAR, SHIFTED, CANONICAL = 0, 1, 2
 IO_LAYOUT, IO_CANONICAL = 0, 1
 F32, BF16 = 0, 1
 ORDER_LPT_XCD, ORDER_LPT, ORDER_ID = 0, 1, 2
-SCHED_AUTO, SCHED_PER_ITEM, SCHED_PER_ITEM_128 = 0, 2, 3
+SCHED_AUTO, SCHED_PER_ITEM, SCHED_PER_ITEM_128, SCHED_QUEUE, SCHED_QUEUE_128 = 0, 2, 3, 4, 5
 METHODS = {"regular": REGULAR, "shifted": SHIFTED, "canonical": CANONICAL}
 
 _c_int, _c_i64, _c_sz, _c_vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -226,7 +226,10 @@ def window_attn_workspace(p: Plan, n_heads, head_dim, text_len, dtype, per_windo
     _check("wsp_window_attn_workspace",
            lib().wsp_window_attn_workspace(p.handle, n_heads, head_dim, text_len, code, ctypes.byref(b)))
     if per_window:
-        return p.n_windows * text_len * n_heads * head_dim * 4
+        # the partials of every window, plus what the minimum holds beside them
+        # (the bf16 kernel's work-queue counters)
+        return p.n_windows * text_len * n_heads * head_dim * 4 + \
+            (b.value - min(p.n_windows, 16) * text_len * n_heads * head_dim * 4)
     return b.value
 
 

@@ -362,7 +362,8 @@ int wsp_window_attn_workspace(const wsp_plan_t *p, int n_heads, int head_dim, in
     const int G = text_chunks(p->nwin);
     const double b = double(G) * text_len * n_heads * head_dim * 4.0;
     if (b > 9e18) return fail(WSP_ERANGE, "workspace size overflows");
-    *bytes = size_t(G) * size_t(text_len) * size_t(n_heads) * size_t(head_dim) * 4u;
+    *bytes = size_t(G) * size_t(text_len) * size_t(n_heads) * size_t(head_dim) * 4u +
+             (dtype == WSP_BF16 ? kQueueBytes : 0);
     return WSP_OK;
 }
 
@@ -534,39 +535,6 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
         if (!aligned16(ptr)) return fail(WSP_EINVAL, "q, k, v and out must be 16-byte aligned");
     }
     if (out == q || out == k || out == v) return fail(WSP_EINVAL, "out must not alias q, k or v");
-    if (rope && (!workspace || workspace_bytes < need))
-        return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) + " bytes required, got " +
-                                        std::to_string(workspace_bytes));
-    if (rope && !aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
-    if (text_len > 0) {
-        for (const void *ptr : {txt_q, txt_k, txt_v, static_cast<const void *>(txt_out)}) {
-            if (!ptr) return fail(WSP_EINVAL, "text tensors and txt_out must be non-NULL when text_len > 0");
-            if (!aligned16(ptr)) return fail(WSP_EINVAL, "text tensors must be 16-byte aligned");
-        }
-        if (no_alloc) {
-            if (need > kScratchBytes)
-                return fail(WSP_ERANGE, "wsp_window_attn_noalloc: the text mean needs " + std::to_string(need) +
-                                            " bytes of scratch, more than its fixed " +
-                                            std::to_string(kScratchBytes) + " (use wsp_window_attn_ex)");
-            workspace_bytes = kScratchBytes;
-        } else {
-            if (!workspace || workspace_bytes < need)
-                return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) +
-                                                " bytes required, got " + std::to_string(workspace_bytes));
-            if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
-        }
-    }
-    // Rotated k, text q and text k at the start of the workspace, the
-    // partials after.
-    void *rot_k = nullptr, *rot_tq = nullptr, *rot_tk = nullptr;
-    if (rope) {
-        uint8_t *w = static_cast<uint8_t *>(workspace);
-        rot_k = w;
-        rot_tq = w + rope_part_bytes(p->n, n_heads);
-        rot_tk = static_cast<uint8_t *>(rot_tq) + rope_part_bytes(text_len, n_heads);
-        workspace = w + rot_bytes;
-        workspace_bytes -= rot_bytes;
-    }
     // The matrix-core kernel addresses a window's video rows (canonical
     // order: the rows between its smallest and largest canonical id) and the
     // text rows with 31-bit byte offsets from per-window buffer bases.
@@ -581,19 +549,57 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
         // (n_heads and head_dim checked above), and relative id < span <
         // 2^31 / row_bytes <= 2^24 because row_bytes >= 128.
     }
+    if ((rope || (dtype == WSP_BF16 && !no_alloc)) && (!workspace || workspace_bytes < need))
+        return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) + " bytes required, got " +
+                                        std::to_string(workspace_bytes));
+    if ((rope || (dtype == WSP_BF16 && !no_alloc)) && !aligned16(workspace))
+        return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
+    if (no_alloc && (text_len > 0 || dtype == WSP_BF16)) {
+        if (need > kScratchBytes)
+            return fail(WSP_ERANGE, "wsp_window_attn_noalloc: the text mean needs " + std::to_string(need) +
+                                        " bytes of scratch, more than its fixed " + std::to_string(kScratchBytes) +
+                                        " (use wsp_window_attn_ex)");
+        workspace_bytes = kScratchBytes;
+    }
+    if (text_len > 0) {
+        for (const void *ptr : {txt_q, txt_k, txt_v, static_cast<const void *>(txt_out)}) {
+            if (!ptr) return fail(WSP_EINVAL, "text tensors and txt_out must be non-NULL when text_len > 0");
+            if (!aligned16(ptr)) return fail(WSP_EINVAL, "text tensors must be 16-byte aligned");
+        }
+        if (!no_alloc) {
+            if (!workspace || workspace_bytes < need)
+                return fail(WSP_EWORKSPACE, "workspace of " + std::to_string(need) +
+                                                " bytes required, got " + std::to_string(workspace_bytes));
+            if (!aligned16(workspace)) return fail(WSP_EINVAL, "workspace must be 16-byte aligned");
+        }
+    }
+    // Workspace: rotated k, text q and text k (rotary attention), the work
+    // queue's counters (bf16), then the text partials.
+    void *rot_k = nullptr, *rot_tq = nullptr, *rot_tk = nullptr;
+    if (rope) {
+        uint8_t *w = static_cast<uint8_t *>(workspace);
+        rot_k = w;
+        rot_tq = w + rope_part_bytes(p->n, n_heads);
+        rot_tk = static_cast<uint8_t *>(rot_tq) + rope_part_bytes(text_len, n_heads);
+        workspace = w + rot_bytes;
+        workspace_bytes -= rot_bytes;
+    }
     if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt(float(head_dim));
     // One text partial per window when the workspace holds them (each text
     // item then shares its window's K/V with the video items in L2), else
     // min(n_windows, 16) chunks.
     const size_t per_part = size_t(text_len) * size_t(n_heads) * size_t(head_dim) * 4u;
-    const int n_chunks = workspace_bytes >= per_part * size_t(p->nwin) ? p->nwin : text_chunks(p->nwin);
+    const size_t queue_bytes = dtype == WSP_BF16 ? kQueueBytes : 0;
+    const int n_chunks =
+        workspace_bytes - queue_bytes >= per_part * size_t(p->nwin) ? p->nwin : text_chunks(p->nwin);
     int order = g_attn_order.load();
     // Short windows (joint sequences averaging < 1024 rows) take 128-row
     // query tiles: a window's partly empty last tile then wastes less.
     const int sched = g_attn_sched.load();
     const bool short_items = (double(p->n) / double(p->nwin) + text_len) < 1024.0;
-    const bool small =
-        sched == WSP_SCHED_PER_ITEM_128 || (sched == WSP_SCHED_AUTO && short_items);
+    const bool small = sched == WSP_SCHED_PER_ITEM_128 || sched == WSP_SCHED_QUEUE_128 ||
+                       (sched == WSP_SCHED_AUTO && short_items);
+    const bool use_queue = sched == WSP_SCHED_QUEUE || sched == WSP_SCHED_QUEUE_128 || sched == WSP_SCHED_AUTO;
     const int bm = dtype != WSP_BF16 ? attn_f32_tile_m(head_dim) : attn_bf16_tile_m(small);
 
     int dev = 0;
@@ -616,7 +622,7 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
         if ((rc = resident_tables(*p, dev, n_heads, text_len, bm, order, gather, n_chunks, dtype == WSP_BF16,
                                   &items, &n_items, &wins, &d_ids, &d_rel)))
             return rc;
-        if (text_len > 0 && (rc = scratch_address(dev, &workspace))) return rc;
+        if ((text_len > 0 || dtype == WSP_BF16) && (rc = scratch_address(dev, &workspace))) return rc;
     } else {
         if ((rc = device_items(*p, dev, n_heads, text_len, bm, order, gather, n_chunks, &items, &n_items)))
             return rc;
@@ -625,6 +631,11 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
         if (gather && dtype != WSP_BF16 && (rc = device_ids(*p, dev, &d_ids))) return rc;
     }
     hipStream_t s = hipStream_t(stream);
+    uint32_t *queue = nullptr;
+    if (queue_bytes) {
+        queue = static_cast<uint32_t *>(workspace);
+        workspace = static_cast<uint8_t *>(workspace) + queue_bytes;
+    }
     float *ws = static_cast<float *>(workspace);
     hipError_t e;
     RopeTables rt;
@@ -655,7 +666,8 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
     }
     if (dtype == WSP_BF16)
         e = launch_attn_bf16(head_dim, small, q8, q, k, v, txt_q, txt_k, txt_v, out, ws, d_rel, items, wins,
-                             n_items, amax_q, amax_k, rope ? &rt : nullptr, n_heads, text_len, scale, s);
+                             n_items, amax_q, amax_k, rope ? &rt : nullptr, n_heads, text_len, scale,
+                             use_queue ? queue : nullptr, order == WSP_ORDER_LPT_XCD ? 8 : 1, s);
     else
         e = launch_attn_f32(head_dim, static_cast<const float *>(q), static_cast<const float *>(k),
                             static_cast<const float *>(v), static_cast<const float *>(txt_q),
@@ -851,7 +863,8 @@ int wsp_set_attn_order(int order) {
 
 int wsp_set_attn_schedule(int schedule) {
     g_last_error.clear();
-    if (schedule != WSP_SCHED_AUTO && schedule != WSP_SCHED_PER_ITEM && schedule != WSP_SCHED_PER_ITEM_128)
+    if (schedule != WSP_SCHED_AUTO && schedule != WSP_SCHED_PER_ITEM && schedule != WSP_SCHED_PER_ITEM_128 &&
+        schedule != WSP_SCHED_QUEUE && schedule != WSP_SCHED_QUEUE_128)
         return fail(WSP_EINVAL, "unknown attention schedule");
     g_attn_sched.store(schedule);
     return WSP_OK;

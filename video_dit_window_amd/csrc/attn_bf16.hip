@@ -54,6 +54,8 @@ namespace {
 // per SIMD); or 4 x 32 rows, two work groups per CU (short windows: less of
 // a window's last query tile is empty).  Same per-wave arithmetic.
 constexpr int kItemWaves = 8, kSmallItemWaves = 4;
+// s_getreg operand: hwreg XCC_ID (20), offset 0, 4 bits.
+constexpr int kHwRegXccId = ((4 - 1) << 11) | (0 << 6) | 20;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 constexpr int kE8M0One = 127;  // E8M0 exponent of 1.0
@@ -130,7 +132,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     uint16_t *__restrict__ out, float *__restrict__ ws, const int32_t *__restrict__ rel,
     const ItemDesc *__restrict__ items, const WinDesc *__restrict__ wins,
     const float *__restrict__ amax_q, const float *__restrict__ amax_k, const float2 *__restrict__ rope_cs,
-    const int32_t *__restrict__ rope_pos, int H, int Lt, float c2_unit) {
+    const int32_t *__restrict__ rope_pos, int H, int Lt, float c2_unit, uint32_t *__restrict__ queue,
+    int n_items, int n_lists) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     using VS = Shape<D, kWaves>;       // V tiles (bf16 rows)
     using KS = KShape<D, kWaves, Q8>;  // K tiles
@@ -140,18 +143,151 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     constexpr int QE = Q8 ? 1 : 2;     // bytes per q / k element
     // Two stages, each a K tile followed by a V tile.
     constexpr int kStage = KS::TILE + VS::TILE;
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStage];
+    // The stages; after an item's last tile also the staging area of its
+    // video outputs (32 rows of 2D bytes per wave, rows kOutRow apart: the
+    // 16-byte pad spreads a column over the banks, and the lane's addresses
+    // stay one base plus constants).
+    constexpr int kOutRow = VS::ROW + 16;
+    constexpr int kOut = kWaves * 32 * kOutRow;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage > kOut ? 2 * kStage : kOut];
 
-    // One scalar load: the item and, for a video item, its window's rows.
-    const ItemDesc it = items[blockIdx.x];
-    if (it.w < 0) return;
-    const bool text = it.nwin > 0;
-    const int h = it.hq >> 16, qt = it.hq & 0xFFFF;
-    const int64_t rs = int64_t(H) * D, hd = int64_t(h) * D;  // elements
+    const int64_t rs = int64_t(H) * D;  // elements per tensor row
     const uint32_t krow_bytes = uint32_t(rs) * QE, vrow_bytes = uint32_t(rs) * 2u;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
+
+    // DMA of one K/V tile.  For V, wave `wave` moves rows wave*(64/kWaves)
+    // + ROWS_PER_LOAD*i + lane/CH (i < LOADS); the lane's 16 bytes land at
+    // LDS chunk lane%CH of its row and come from the row's chunk
+    // (lane%CH) ^ swz(row).  K likewise with its own row size.
+    const int vdrow0 = wave * (kBN / kWaves) + lane / VS::CH;
+    const int kdrow0 = wave * (kBN / kWaves) + lane / KS::CH;
+    int vdchunk[VS::LOADS], kdchunk[KS::LOADS];  // bytes into the row
+#pragma unroll
+    for (int i = 0; i < VS::LOADS; ++i)
+        vdchunk[i] = 16 * ((lane % VS::CH) ^ swz<D>(vdrow0 + VS::ROWS_PER_LOAD * i));
+#pragma unroll
+    for (int i = 0; i < KS::LOADS; ++i)
+        kdchunk[i] = 16 * ((lane % KS::CH) ^ kswz<D, Q8>(kdrow0 + KS::ROWS_PER_LOAD * i));
+    auto klo = [&](int i) { return (wave * (kBN / kWaves) + KS::ROWS_PER_LOAD * i) * KS::ROW; };
+    auto vlo = [&](int i) { return KS::TILE + (wave * (kBN / kWaves) + VS::ROWS_PER_LOAD * i) * VS::ROW; };
+    // Every DMA is a buffer load (MUBUF): the global/flat DMA forms would
+    // make the compiler wait for all outstanding LDS reads (lgkmcnt(0)) while
+    // a DMA is in flight.  Video rows come through resources based at the
+    // window's first row (gather mode: its smallest canonical row, the first
+    // in row-major order), text rows through resources based at the text
+    // tensors; the host checks that every offset fits 31 bits.  A resource's
+    // byte range also bounds every access.  (The window's row range is held
+    // in scalar registers: a resource in vector registers would turn every
+    // DMA into a loop over lanes.)
+    auto rsrc = [&](const void *base, uint32_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), kBufferFlags);
+    };
+
+    // LDS byte offsets of this lane's operands inside a stage.
+    //  K (A of S^T), bf16: row 32*mk + l32, logical chunk 2s + hh.
+    //  K, E4M3: row 32*mk + l32, logical chunks 4s + 2hh + e (e < 2).
+    int kaddr[Q8 ? 1 : VS::KSTEPS];
+    int kaddr8[2][2];
+    if constexpr (Q8) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) kaddr8[s][e] = l32 * KS::ROW + 16 * ((4 * s + 2 * hh + e) ^ swz8(l32));
+    } else {
+#pragma unroll
+        for (int s = 0; s < VS::KSTEPS; ++s) kaddr[s] = l32 * KS::ROW + 16 * ((2 * s + hh) ^ swz<D>(l32));
+    }
+    //  V^T (A of O^T) by transpose reads: for O^T block t and half B of a
+    //  16-key k-step, lane i = lane%16 of 16-lane group g reads 8 bytes of
+    //  row 16*cs + 8*B + 4*hh + i/4, dims 32t + 16*(g%2) + 4*(i%4) .. +3;
+    //  the transpose hands lane l dim 32t + l%32 of those four rows.
+    const int gi = lane & 15, ghalf = (lane >> 4) & 1;
+    int vaddr[VS::DT][2];
+#pragma unroll
+    for (int t = 0; t < VS::DT; ++t)
+#pragma unroll
+        for (int B = 0; B < 2; ++B) {
+            const int row = 8 * B + 4 * hh + (gi >> 2);
+            const int dim = 32 * t + 16 * ghalf + 4 * (gi & 3);
+            vaddr[t][B] = KS::TILE + row * VS::ROW + 16 * ((dim >> 3) ^ swz<D>(row)) + 2 * (dim & 7);
+        }
+
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    uint8_t LDS_AS *const st0 = (uint8_t LDS_AS *)lds;
+    uint8_t LDS_AS *const st1 = st0 + kStage;
+
+    // Gather mode: relative ids of the rows of a tile, one set per DMA (V
+    // rows; E4M3 K rows have their own map).
+    struct Ids {
+        int v[VS::LOADS];
+        int k[Q8 ? KS::LOADS : 1];
+    };
+    // Ids of tile j of a window whose relative ids are addressed by `irs`.
+    auto load_ids = [&](__amdgpu_buffer_rsrc_t irs, Ids &d, int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < VS::LOADS; ++i)
+            d.v[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (j * kBN + vdrow0 + VS::ROWS_PER_LOAD * i), 0, 0);
+        if constexpr (Q8) {
+#pragma unroll
+            for (int i = 0; i < KS::LOADS; ++i)
+                d.k[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (j * kBN + kdrow0 + KS::ROWS_PER_LOAD * i), 0, 0);
+        }
+    };
+    // Gather mode: the window's relative ids, read by buffer loads whose
+    // per-lane offset holds the row (the range check covers it: rows past
+    // the window read 0, and such rows only reach the DMA as masked keys).
+    auto ids_rsrc = [&](const WinDesc &wd) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(GATHER ? rel + wd.off : rel), 0,
+                                                 GATHER ? 4 * wd.lw : 0, kBufferFlags);
+    };
+
+    // The work: the item at blockIdx.x; or, with a queue, resident work
+    // groups that take items in turn from a list (list x holds items
+    // n_lists * t + x, then idle padding; queue[x], zero at launch, hands out
+    // its tickets t), so an item's start-up overlaps the previous item's
+    // stores and no work group waits for a dispatch.  A work group starts on
+    // the list of the XCD it runs on (every item of a (window, head) group
+    // then reads the group's K/V from one L2) and, once that list is empty,
+    // moves on to the next ones, so every list drains wherever the work
+    // groups run.  Thread 0 takes the next ticket as an item starts and
+    // publishes it at the item's first barrier; every wave then requests the
+    // next item's descriptor (lanes 0..7 hold its words).  s_next has two
+    // slots used in turn: a slot is rewritten only after every wave has
+    // passed the barrier that follows its reads.
+    __shared__ int s_next[2];
+    int xq = 0, b = blockIdx.x, par = 0, empty_lists = 0;
+    auto take = [&]() __attribute__((always_inline)) {
+        if (tid == 0)
+            s_next[par] = n_lists * int(__hip_atomic_fetch_add(queue + xq, 1u, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT)) + xq;
+        __syncthreads();
+        b = __builtin_amdgcn_readfirstlane(s_next[par]);
+        par ^= 1;
+    };
+    if (queue) {
+        if (n_lists > 1) xq = int(__builtin_amdgcn_s_getreg(kHwRegXccId) & 7u);
+        take();
+    }
+    ItemDesc it{};
+    it.w = -1;
+    if (b < n_items) it = items[b];
+    for (;;) {
+    if (it.w < 0) {  // list xq is empty
+        if (!queue || ++empty_lists >= n_lists) break;
+        xq = xq + 1 == n_lists ? 0 : xq + 1;
+        take();
+        it.w = -1;
+        if (b < n_items) it = items[b];
+        continue;
+    }
+    uint32_t ticket = 0;
+    if (queue && tid == 0)
+        ticket = __hip_atomic_fetch_add(queue + xq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t next_desc = 0;
+    const bool text = it.nwin > 0;
+    const int h = it.hq >> 16, qt = it.hq & 0xFFFF;
+    const int64_t hd = int64_t(h) * D;  // elements
     // Scores in log2 units: S * c2; E4M3 scores carry both dequantisation factors.
     float c2 = c2_unit;
     if constexpr (Q8) c2 = c2_unit * (amax_q[h] * (1.0f / 448.0f)) * (amax_k[h] * (1.0f / 448.0f));
@@ -170,6 +306,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     if constexpr (ROPE) {
         if (qrow < nv) qpk = uint32_t(rope_pos[it.win.off + qrow]);
     }
+    // Gather mode: the first tile's row ids are requested with the query
+    // row's id, so that the query load and the first DMA start together.
+    Ids id0;
+    if constexpr (GATHER) load_ids(ids_rsrc(text ? wins[it.w] : it.win), id0, 0);
     int64_t qtrow;
     {
         const int r = min(qrow, nq - 1);
@@ -204,81 +344,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             }
         }
     }
-
-    // DMA of one K/V tile.  For V, wave `wave` moves rows wave*(64/kWaves)
-    // + ROWS_PER_LOAD*i + lane/CH (i < LOADS); the lane's 16 bytes land at
-    // LDS chunk lane%CH of its row and come from the row's chunk
-    // (lane%CH) ^ swz(row).  K likewise with its own row size.
-    const int vdrow0 = wave * (kBN / kWaves) + lane / VS::CH;
-    const int kdrow0 = wave * (kBN / kWaves) + lane / KS::CH;
-    int vdchunk[VS::LOADS], kdchunk[KS::LOADS];  // bytes into the row
-#pragma unroll
-    for (int i = 0; i < VS::LOADS; ++i)
-        vdchunk[i] = 16 * ((lane % VS::CH) ^ swz<D>(vdrow0 + VS::ROWS_PER_LOAD * i));
-#pragma unroll
-    for (int i = 0; i < KS::LOADS; ++i)
-        kdchunk[i] = 16 * ((lane % KS::CH) ^ kswz<D, Q8>(kdrow0 + KS::ROWS_PER_LOAD * i));
-    auto klo = [&](int i) { return (wave * (kBN / kWaves) + KS::ROWS_PER_LOAD * i) * KS::ROW; };
-    auto vlo = [&](int i) { return KS::TILE + (wave * (kBN / kWaves) + VS::ROWS_PER_LOAD * i) * VS::ROW; };
-    // Every DMA is a buffer load (MUBUF): the global/flat DMA forms would
-    // make the compiler wait for all outstanding LDS reads (lgkmcnt(0)) while
-    // a DMA is in flight.  Video rows come through resources based at the
-    // window's first row (gather mode: its smallest canonical row, the first
-    // in row-major order), text rows through resources based at the text
-    // tensors; the host checks that every offset fits 31 bits.  A resource's
-    // byte range also bounds every access.  (The window's row range is held
-    // in scalar registers: a resource in vector registers would turn every
-    // DMA into a loop over lanes.)
-    auto rsrc = [&](const void *base, uint32_t bytes) {
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), kBufferFlags);
-    };
     const __amdgpu_buffer_rsrc_t tkrs = rsrc(tk + hd * QE, uint32_t(Lt) * krow_bytes);
     const __amdgpu_buffer_rsrc_t tvrs = rsrc(tv + hd, uint32_t(Lt) * vrow_bytes);
 
-    // LDS byte offsets of this lane's operands inside a stage.
-    //  K (A of S^T), bf16: row 32*mk + l32, logical chunk 2s + hh.
-    //  K, E4M3: row 32*mk + l32, logical chunks 4s + 2hh + e (e < 2).
-    int kaddr[Q8 ? 1 : VS::KSTEPS];
-    int kaddr8[2][2];
-    if constexpr (Q8) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) kaddr8[s][e] = l32 * KS::ROW + 16 * ((4 * s + 2 * hh + e) ^ swz8(l32));
-    } else {
-#pragma unroll
-        for (int s = 0; s < VS::KSTEPS; ++s) kaddr[s] = l32 * KS::ROW + 16 * ((2 * s + hh) ^ swz<D>(l32));
-    }
-    //  V^T (A of O^T) by transpose reads: for O^T block t and half B of a
-    //  16-key k-step, lane i = lane%16 of 16-lane group g reads 8 bytes of
-    //  row 16*cs + 8*B + 4*hh + i/4, dims 32t + 16*(g%2) + 4*(i%4) .. +3;
-    //  the transpose hands lane l dim 32t + l%32 of those four rows.
-    const int gi = lane & 15, ghalf = (lane >> 4) & 1;
-    int vaddr[VS::DT][2];
-#pragma unroll
-    for (int t = 0; t < VS::DT; ++t)
-#pragma unroll
-        for (int B = 0; B < 2; ++B) {
-            const int row = 8 * B + 4 * hh + (gi >> 2);
-            const int dim = 32 * t + 16 * ghalf + 4 * (gi & 3);
-            vaddr[t][B] = KS::TILE + row * VS::ROW + 16 * ((dim >> 3) ^ swz<D>(row)) + 2 * (dim & 7);
-        }
-
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     // A wave whose 32 query rows all lie past the item's query rows (the
     // last query tile of a sequence) only moves its share of the K/V tiles
     // and meets the barriers: the SIMD it shares then runs the other wave
     // alone.
     const bool active = qt * kBM + wave * 32 < nq;
-    uint8_t LDS_AS *const st0 = (uint8_t LDS_AS *)stage0;
-    uint8_t LDS_AS *const st1 = (uint8_t LDS_AS *)stage1;
-
-    // Gather mode: relative ids of the rows of a tile, one set per DMA (V
-    // rows; E4M3 K rows have their own map).
-    struct Ids {
-        int v[VS::LOADS];
-        int k[Q8 ? KS::LOADS : 1];
-    };
 
     // A video item runs one window; a text item each window of its chunk.
     const int n_loop = text ? it.nwin : 1;
@@ -288,35 +361,18 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         const int M = Lw + Lt;  // joint key/value sequence [video rows; text rows]
         const int64_t vrow0 = wd.vrow0;
         const uint32_t vrows = uint32_t(wd.vrows);
-        const int32_t *const wrel = GATHER ? rel + wd.off : nullptr;
         const __amdgpu_buffer_rsrc_t krs = rsrc(k + (vrow0 * rs + hd) * QE, vrows * krow_bytes);
         const __amdgpu_buffer_rsrc_t vrs = rsrc(v + vrow0 * rs + hd, vrows * vrow_bytes);
         // Layout order: the lane's first row as a per-lane offset (its chunk
         // added at the load), the tile and row steps in the scalar offset.
         const int kdbase = kdrow0 * int(krow_bytes), vdbase = vdrow0 * int(vrow_bytes);
         // Gather mode: the ids of the next tile's rows are loaded one tile
-        // ahead of their DMA by buffer loads whose per-lane offset holds the
-        // row (the range check covers it: rows past the window read 0, and
-        // such rows only reach the DMA as masked keys).  Two register sets
-        // alternate: the next tile's ids are requested before the current
-        // tile's DMA, so the tile's closing vmcnt wait does not end on them.
-        // The DMA offset is one 24-bit multiply-add, exact because the host's
-        // limits keep the row bytes and the relative ids below 2^24 and every
-        // offset below 2^31.
-        const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<int32_t *>(GATHER ? wrel : rel), 0, GATHER ? 4 * Lw : 0, kBufferFlags);
-        auto load_ids = [&](Ids &d, int j) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < VS::LOADS; ++i)
-                d.v[i] = __builtin_amdgcn_raw_buffer_load_b32(irs, 4 * (j * kBN + vdrow0 + VS::ROWS_PER_LOAD * i),
-                                                              0, 0);
-            if constexpr (Q8) {
-#pragma unroll
-                for (int i = 0; i < KS::LOADS; ++i)
-                    d.k[i] = __builtin_amdgcn_raw_buffer_load_b32(
-                        irs, 4 * (j * kBN + kdrow0 + KS::ROWS_PER_LOAD * i), 0, 0);
-            }
-        };
+        // ahead of their DMA.  Two register sets alternate: the next tile's
+        // ids are requested before the current tile's DMA, so the tile's
+        // closing vmcnt wait does not end on them.  The DMA offset is one
+        // 24-bit multiply-add, exact because the host's limits keep the row
+        // bytes and the relative ids below 2^24 and every offset below 2^31.
+        const __amdgpu_buffer_rsrc_t irs = ids_rsrc(wd);
         auto kid = [&](const Ids &d, int i) { return Q8 ? d.k[i] : d.v[i]; };
         // The window's video rows travel with cache policy CP: 0 where other
         // items of the same XCD read the same K/V from L2 (video items, and a
@@ -331,7 +387,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         auto dma_cp = [&](auto cp_c, uint8_t LDS_AS *dst, int j, Ids &idp,
                           Ids &idn) __attribute__((always_inline)) {
             constexpr int CP = decltype(cp_c)::value;
-            if constexpr (GATHER) load_ids(idn, j + 1);
+            if constexpr (GATHER) load_ids(irs, idn, j + 1);
             if (!GATHER && (j + 1) * kBN <= Lw) {
                 const int ks = j * kBN * int(krow_bytes), vs = j * kBN * int(vrow_bytes);
 #pragma unroll
@@ -531,13 +587,31 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             __syncthreads();
         };
 
-        // Both stages are free here: the previous window (if any) ended on a
-        // tile's closing barrier.
+        // Both stages are free here: the previous window or item (if any)
+        // ended on a tile's closing barrier.
         Ids idA, idB;
-        if constexpr (GATHER) load_ids(idA, 0);
+        if constexpr (GATHER) {
+            if (wi == 0) idA = id0;
+            else load_ids(irs, idA, 0);
+        }
+        if (queue && wi == 0) {
+            // every wave has read back the previous item's staged outputs
+            // (LDS only: that item's global stores may still be in flight)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
         dma(st0, 0, idA, idB);
         __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (queue && wi == 0 && tid == 0) s_next[par] = n_lists * int(ticket) + xq;
         __syncthreads();
+        if (queue && wi == 0) {
+            const int nb = __builtin_amdgcn_readfirstlane(s_next[par]);
+            if (lane < 8)
+                next_desc = nb < n_items ? reinterpret_cast<const uint32_t *>(items)[8 * nb + lane]
+                                         : (lane == 0 ? ~0u : 0u);
+        }
         for (int j = 0; j < ntiles; j += 2) {
             tile(st0, st1, j, idB, idA);
             if (j + 1 < ntiles) tile(st1, st0, j + 1, idA, idB);
@@ -562,18 +636,51 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                     if (wi > 0) val = *p + val;
                     *p = val;
                 }
-        } else if (qrow < nv) {
-            uint16_t *dst = out + qtrow * rs + hd;
-#pragma unroll
-            for (int t = 0; t < VS::DT; ++t)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x2 st;
-                    st[0] = pack_bf16(O[t][4 * g] * inv, O[t][4 * g + 1] * inv);
-                    st[1] = pack_bf16(O[t][4 * g + 2] * inv, O[t][4 * g + 3] * inv);
-                    *reinterpret_cast<u32x2 *>(dst + 32 * t + 8 * g + 4 * hh) = st;
-                }
         }
+        // Video rows go out through LDS: each wave stages its rows in its own
+        // part of the idle stage buffers, then stores whole 16-byte chunks,
+        // CH consecutive lanes per row (full cache lines, instead of 8-byte
+        // pieces of 32 rows per store).
+        const int r0 = qt * kBM + wave * 32;  // the wave's first query row
+        if (r0 < nv) {
+            uint8_t LDS_AS *const ob = st0 + wave * 32 * kOutRow;
+            if (qrow < nv) {
+#pragma unroll
+                for (int t = 0; t < VS::DT; ++t)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        u32x2 st;
+                        st[0] = pack_bf16(O[t][4 * g] * inv, O[t][4 * g + 1] * inv);
+                        st[1] = pack_bf16(O[t][4 * g + 2] * inv, O[t][4 * g + 3] * inv);
+                        *reinterpret_cast<u32x2 LDS_AS *>(ob + l32 * kOutRow + 2 * (32 * t + 8 * g + 4 * hh)) = st;
+                    }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the staged rows are in LDS
+            constexpr int RPI = 64 / VS::CH;      // rows per store
+            const int nrows = min(32, nv - r0), rl = lane / VS::CH, c = lane % VS::CH;
+            const uint8_t LDS_AS *const ib = ob + rl * kOutRow + 16 * c;
+#pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i) {
+                // tensor row of the wave's row RPI*i + rl (held by that lane)
+                const int trow = __builtin_amdgcn_ds_bpermute(4 * rl + 4 * RPI * i, int(qtrow));
+                if (rl < nrows - RPI * i) {
+                    const u32x4 val = *reinterpret_cast<const u32x4 LDS_AS *>(ib + RPI * i * kOutRow);
+                    *reinterpret_cast<u32x4 *>(out + int64_t(trow) * rs + hd + 8 * c) = val;
+                }
+            }
+        }
+    }
+    if (!queue) break;
+    // The next item: its descriptor words from lanes 0..7 (w < 0 ends the list).
+    it.w = __builtin_amdgcn_readlane(int(next_desc), 0);
+    it.hq = __builtin_amdgcn_readlane(int(next_desc), 1);
+    it.nwin = __builtin_amdgcn_readlane(int(next_desc), 2);
+    it.chunk = __builtin_amdgcn_readlane(int(next_desc), 3);
+    it.win.off = __builtin_amdgcn_readlane(int(next_desc), 4);
+    it.win.lw = __builtin_amdgcn_readlane(int(next_desc), 5);
+    it.win.vrow0 = __builtin_amdgcn_readlane(int(next_desc), 6);
+    it.win.vrows = __builtin_amdgcn_readlane(int(next_desc), 7);
+    par ^= 1;
     }
 #endif
 }
@@ -582,12 +689,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 
 int attn_bf16_tile_m(bool small) { return 32 * (small ? kSmallItemWaves : kItemWaves); }
 
+namespace {
+// Clears the work queue's ticket counters ahead of a resident-work-group launch.
+__global__ void clear_queue_kernel(uint32_t *queue) {
+    if (threadIdx.x < kQueueWords) queue[threadIdx.x] = 0u;
+}
+}  // namespace
+
 hipError_t launch_attn_bf16(int head_dim, bool small, bool q8, const void *q, const void *k, const void *v,
                             const void *tq, const void *tk, const void *tv, void *out, float *ws,
                             const int32_t *rel, const ItemDesc *items, const WinDesc *wins, int n_items,
                             const float *amax_q, const float *amax_k, const RopeTables *rope, int n_heads,
-                            int text_len, float scale, hipStream_t s) {
+                            int text_len, float scale, uint32_t *queue, int n_lists, hipStream_t s) {
     if (n_items <= 0) return hipSuccess;
+    if (queue && n_lists != 1 && n_lists != 8) return hipErrorInvalidValue;
     if (q8 && head_dim != 128) return hipErrorInvalidValue;
     if (rope && (q8 || head_dim != 128)) return hipErrorInvalidValue;
     const float c2 = scale * kLog2e;
@@ -595,10 +710,23 @@ hipError_t launch_attn_bf16(int head_dim, bool small, bool q8, const void *q, co
     const RopeTables &rt = rope ? *rope : none;
     auto B = [](const void *p) { return static_cast<const uint8_t *>(p); };
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
+    hipError_t err = hipSuccess;
     auto launch = [&](auto kern, int waves) {
-        kern<<<dim3(n_items), dim3(64 * waves), 0, s>>>(B(q), B(k), U(v), B(tq), B(tk), U(tv),
-                                                         static_cast<uint16_t *>(out), ws, rel, items, wins,
-                                                         amax_q, amax_k, rt.cs, rt.pos, n_heads, text_len, c2);
+        int grid = n_items;
+        if (queue) {
+            // one resident work group per free slot of every compute unit
+            int dev = 0, cus = 0, per_cu = 0;
+            if ((err = hipGetDevice(&dev)) != hipSuccess) return;
+            if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return;
+            if ((err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * waves, 0)) != hipSuccess)
+                return;
+            grid = std::min(n_items, std::max(1, cus * per_cu));
+            clear_queue_kernel<<<1, 64, 0, s>>>(queue);
+        }
+        kern<<<dim3(grid), dim3(64 * waves), 0, s>>>(B(q), B(k), U(v), B(tq), B(tk), U(tv),
+                                                      static_cast<uint16_t *>(out), ws, rel, items, wins, amax_q,
+                                                      amax_k, rt.cs, rt.pos, n_heads, text_len, c2, queue, n_items,
+                                                      n_lists);
     };
     auto dispatch = [&](auto waves_c) {
         constexpr int NW = decltype(waves_c)::value;
@@ -623,6 +751,7 @@ hipError_t launch_attn_bf16(int head_dim, bool small, bool q8, const void *q, co
     const hipError_t e = small ? dispatch(std::integral_constant<int, kSmallItemWaves>{})
                                : dispatch(std::integral_constant<int, kItemWaves>{});
     if (e != hipSuccess) return e;
+    if (err != hipSuccess) return err;
     return hipGetLastError();
 }
 

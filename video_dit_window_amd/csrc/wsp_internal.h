@@ -132,8 +132,16 @@ int device_items(wsp_plan_t &p, int dev, int n_heads, int text_len, int bm, int 
 // relayout.hip
 hipError_t launch_relayout(const void *x, void *y, const int32_t *perm, int64_t n_rows,
                            int64_t row_bytes, hipStream_t s);
+// Ticket counters of the bf16 kernel's work queue, at the start of the
+// caller's workspace (256 bytes, cleared by the launch itself).
+constexpr int kQueueWords = 64;
+constexpr size_t kQueueBytes = sizeof(uint32_t) * kQueueWords;
 // attn_bf16.hip: the matrix-core kernel, one work group per item: 256 query
-// rows, or 128 with `small` (4-wave work groups, two per CU).  rel != NULL
+// rows, or 128 with `small` (4-wave work groups, two per CU).  queue != NULL
+// launches resident work groups instead (as many as fit on the device) that
+// take the items from n_lists lists in turn (n_lists 8: list x = items
+// 8t + x, taken by the work groups running on XCD x; 1: the whole list) --
+// the queue's counters are cleared by a kernel launched just before.  rel != NULL
 // selects canonical-order q/k/v/out: video row r of window w is tensor row
 // vrow0(w) + rel[offsets[w] + r] (the plan's ids relative to the window's
 // smallest id; items and windows resolved to match).  q8: q, k (and the text
@@ -152,7 +160,7 @@ hipError_t launch_attn_bf16(int head_dim, bool small, bool q8, const void *q, co
                             const void *tq, const void *tk, const void *tv, void *out, float *ws,
                             const int32_t *rel, const ItemDesc *items, const WinDesc *wins, int n_items,
                             const float *amax_q, const float *amax_k, const RopeTables *rope, int n_heads,
-                            int text_len, float scale, hipStream_t s);
+                            int text_len, float scale, uint32_t *queue, int n_lists, hipStream_t s);
 // attn_f32.hip: the float32 kernel (same items; ids != NULL: canonical-order
 // tensors, video row r of window w is tensor row ids[offsets[w] + r]).
 int attn_f32_tile_m(int head_dim);
