@@ -255,10 +255,11 @@ int wsp_window_attn_ex(const wsp_plan_t *p, const void *q, const void *k, const 
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same kernels and results, bit for bit;
  * it calls no hipMalloc, hipFree or allocating routine:
- *   - the text mean's float32 partials go to a fixed scratch array of 96 MiB
- *     that the library holds on each GPU it runs on until the process ends.
- *     One partial per window when those fit (n_windows * text_len * n_heads
- *     * head_dim * 4 bytes <= 96 MiB, e.g. the 720p-shaped layer), else
+ *   - the work queue's counters (256 bytes, bf16) and the text mean's
+ *     float32 partials go to a fixed scratch array of 96 MiB that the
+ *     library holds on each GPU it runs on until the process ends.  One
+ *     partial per window when those fit (n_windows * text_len * n_heads *
+ *     head_dim * 4 bytes <= 96 MiB - 256, e.g. the 720p-shaped layer), else
  *     min(n_windows, 16) chunk partials (42 MB for the 1080p-shaped layer,
  *     84 MB for the 4K-shaped one); a larger need returns WSP_ERANGE;
  *   - the plan's device tables must already be on the device: a call of

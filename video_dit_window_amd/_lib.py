@@ -296,10 +296,12 @@ def window_attn_noalloc(p: Plan, q, k, v, txt_q, txt_k, txt_v, out, txt_out, sca
     return out, txt_out
 
 
-def noalloc_per_window(p: Plan, n_heads, head_dim, text_len) -> bool:
+def noalloc_per_window(p: Plan, n_heads, head_dim, text_len, dtype=BF16) -> bool:
     """Whether wsp_window_attn_noalloc reduces the text with one partial per
-    window (they fit in its 96 MiB scratch) rather than in 16 chunks."""
-    return p.n_windows * text_len * n_heads * head_dim * 4 <= (96 << 20)
+    window (they fit in its 96 MiB scratch, beside the 256 bytes of bf16
+    work-queue counters) rather than in 16 chunks."""
+    queue = 256 if (dtype if isinstance(dtype, int) else _dtype_code(dtype)) == BF16 else 0
+    return p.n_windows * text_len * n_heads * head_dim * 4 <= (96 << 20) - queue
 
 
 def rope_relayout(x, src: Plan, dst: Plan, pos: Plan, text_len, theta=None, out=None, stream=None):
