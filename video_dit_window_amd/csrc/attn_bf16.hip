@@ -334,14 +334,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
 #pragma unroll
             for (int s = 0; s < VS::KSTEPS; ++s)
                 Qr[s] = *reinterpret_cast<const bf16x8 *>(p + 2 * (16 * s + 8 * hh));
-            if constexpr (ROPE) {
-                // video queries rotated in registers (chunk 2s + hh of the row)
-                if (qrow < nv) {
-                    const int p21[3] = {(Lt + int(qpk & 1023u)) * kRopePairs, int((qpk >> 10) & 2047u) * kRopePairs,
-                                        int(qpk >> 21) * kRopePairs};
-                    rope_q_row<0, VS::KSTEPS>(Qr, hh, p21, rope_cs);
-                }
-            }
         }
     }
     const __amdgpu_buffer_rsrc_t tkrs = rsrc(tk + hd * QE, uint32_t(Lt) * krow_bytes);
@@ -603,6 +595,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             asm volatile("" ::: "memory");
         }
         dma(st0, 0, idA, idB);
+        if constexpr (ROPE) {
+            // video queries rotated in registers (chunk 2s + hh of the row),
+            // once the first tile's DMA is on its way
+            if (wi == 0 && qrow < nv) {
+                const int p21[3] = {(Lt + int(qpk & 1023u)) * kRopePairs, int((qpk >> 10) & 2047u) * kRopePairs,
+                                    int(qpk >> 21) * kRopePairs};
+                rope_q_row<0, VS::KSTEPS>(Qr, hh, p21, rope_cs);
+            }
+        }
         __builtin_amdgcn_s_waitcnt(0x0F70);
         if (queue && wi == 0 && tid == 0) s_next[par] = n_lists * int(ticket) + xq;
         __syncthreads();
