@@ -45,8 +45,8 @@ int fp8_max_row_chunks() { return 2048; }
 hipError_t launch_relayout(const void *, void *, const int32_t *, int64_t, int64_t, hipStream_t) { reached("relayout"); }
 hipError_t launch_attn_bf16(int, bool, bool, const void *, const void *, const void *, const void *, const void *,
                             const void *, void *, float *, const int32_t *, const ItemDesc *, const WinDesc *, int,
-                            const float *, const float *, const RopeTables *, int, int, float, uint32_t *, int,
-                            hipStream_t) {
+                            const float *, const float *, const RopeTables *, int, int, float, uint32_t *, int, int,
+                            int, hipStream_t) {
     reached("attn_bf16");
 }
 hipError_t launch_attn_f32(int, const float *, const float *, const float *, const float *, const float *,
@@ -175,6 +175,17 @@ static void check_plan(int T, int H, int W, int nt, int nh, int nw, int method) 
                                 CHECK(it.chunk == (joint(it.w) ? it.w : -1));
                                 CHECK(int64_t(t) * bm < d.lw + (joint(it.w) ? Lt : 0));
                                 CHECK(vid.insert({it.w, h, t}).second);
+                                // the box extents give every row's canonical offset in the window
+                                CHECK(it.eh > 0 && it.ew > 0);
+                                if (gather && h == 0 && t == 0) {
+                                    const uint32_t eh = uint32_t(it.eh), ew = uint32_t(it.ew);
+                                    for (int32_t r = 0; r < d.lw; ++r) {
+                                        const uint32_t q1 = uint32_t(r) / ew, dt = q1 / eh;
+                                        const int64_t rel = int64_t(dt) * p->H * p->W + int64_t(q1 - dt * eh) * p->W +
+                                                            int64_t(uint32_t(r) - q1 * ew);
+                                        CHECK(rel == int64_t(ids[size_t(d.off + r)]) - d.vrow0);
+                                    }
+                                }
                             } else {
                                 CHECK(Lt > 0);
                                 CHECK(it.chunk >= 0 && it.chunk < G);

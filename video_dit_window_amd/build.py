@@ -33,9 +33,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libwsp)")
 
 
+# Per-source flags.  attn_bf16.hip: the resident work groups take their next
+# ticket with one atomic from one lane; LLVM's atomic optimizer would rewrite
+# it into a wave-wide form that reads the result back at once, i.e. waits for
+# every outstanding memory operation (the previous item's output stores
+# included) at the start of each item.
+EXTRA_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS
+    cmd = ([hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS +
+           EXTRA_FLAGS.get(src, []))
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

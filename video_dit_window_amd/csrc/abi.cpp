@@ -667,7 +667,7 @@ int window_attn_impl(const wsp_plan_t *pc, const void *q, const void *k, const v
     if (dtype == WSP_BF16)
         e = launch_attn_bf16(head_dim, small, q8, q, k, v, txt_q, txt_k, txt_v, out, ws, d_rel, items, wins,
                              n_items, amax_q, amax_k, rope ? &rt : nullptr, n_heads, text_len, scale,
-                             use_queue ? queue : nullptr, order == WSP_ORDER_LPT_XCD ? 8 : 1, s);
+                             use_queue ? queue : nullptr, order == WSP_ORDER_LPT_XCD ? 8 : 1, p->H * p->W, p->W, s);
     else
         e = launch_attn_f32(head_dim, static_cast<const float *>(q), static_cast<const float *>(k),
                             static_cast<const float *>(v), static_cast<const float *>(txt_q),

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     const ItemDesc *__restrict__ items, const WinDesc *__restrict__ wins,
     const float *__restrict__ amax_q, const float *__restrict__ amax_k, const float2 *__restrict__ rope_cs,
     const int32_t *__restrict__ rope_pos, int H, int Lt, float c2_unit, uint32_t *__restrict__ queue,
-    int n_items, int n_lists) {
+    int n_items, int n_lists, int grid_hw, int grid_w) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     using VS = Shape<D, kWaves>;       // V tiles (bf16 rows)
     using KS = KShape<D, kWaves, Q8>;  // K tiles
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     // moves on to the next ones, so every list drains wherever the work
     // groups run.  Thread 0 takes the next ticket as an item starts and
     // publishes it at the item's first barrier; every wave then requests the
-    // next item's descriptor (lanes 0..7 hold its words).  s_next has two
+    // next item's descriptor (lanes 0..11 hold its words).  s_next has two
     // slots used in turn: a slot is rewritten only after every wave has
     // passed the barrier that follows its reads.
     __shared__ int s_next[2];
@@ -308,13 +308,34 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     }
     // Gather mode: the first tile's row ids are requested with the query
     // row's id, so that the query load and the first DMA start together.
-    Ids id0;
-    if constexpr (GATHER) load_ids(ids_rsrc(text ? wins[it.w] : it.win), id0, 0);
+    // Gather mode: video rows take their ids from the window's box (row r =
+    // (dt*eh + dh)*ew + dw lies dt*H*W + dh*W + dw canonical rows past the
+    // first), so the query and first-tile loads wait for no table read.
+    auto box_rel = [&](int r) {
+        const uint32_t eh = uint32_t(it.eh), ew = uint32_t(it.ew);
+        const uint32_t q1 = uint32_t(r) / ew, dt = q1 / eh;
+        return int(dt * uint32_t(grid_hw) + (q1 - dt * eh) * uint32_t(grid_w) + (uint32_t(r) - q1 * ew));
+    };
+    // (rows past the window get id 0, as from the table's range check)
+    auto box_ids0 = [&](Ids &d) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < VS::LOADS; ++i) {
+            const int r = vdrow0 + VS::ROWS_PER_LOAD * i;
+            d.v[i] = r < nv ? box_rel(r) : 0;
+        }
+        if constexpr (Q8) {
+#pragma unroll
+            for (int i = 0; i < KS::LOADS; ++i) {
+                const int r = kdrow0 + KS::ROWS_PER_LOAD * i;
+                d.k[i] = r < nv ? box_rel(r) : 0;
+            }
+        }
+    };
     int64_t qtrow;
     {
         const int r = min(qrow, nq - 1);
         if (r >= nv) qtrow = r - nv;
-        else if (GATHER) qtrow = int64_t(it.win.vrow0) + rel[it.win.off + r];
+        else if (GATHER) qtrow = int64_t(it.win.vrow0) + box_rel(r);
         else qtrow = int64_t(it.win.off) + r;
     }
     // bf16: lane half hh holds dims 16s + 8hh .. +7 of k-step s.  E4M3:
@@ -582,10 +603,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         // Both stages are free here: the previous window or item (if any)
         // ended on a tile's closing barrier.
         Ids idA, idB;
-        if constexpr (GATHER) {
-            if (wi == 0) idA = id0;
-            else load_ids(irs, idA, 0);
-        }
         if (queue && wi == 0) {
             // every wave has read back the previous item's staged outputs
             // (LDS only: that item's global stores may still be in flight)
@@ -594,7 +611,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
-        dma(st0, 0, idA, idB);
+        // (one DMA call per branch, so that the wait for a table read stays
+        // in its own branch)
+        if (!GATHER || !text) {
+            if constexpr (GATHER) box_ids0(idA);
+            dma(st0, 0, idA, idB);
+        } else {
+            load_ids(irs, idA, 0);
+            dma(st0, 0, idA, idB);
+        }
         if constexpr (ROPE) {
             // video queries rotated in registers (chunk 2s + hh of the row),
             // once the first tile's DMA is on its way
@@ -605,18 +630,25 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);
-        if (queue && wi == 0 && tid == 0) s_next[par] = n_lists * int(ticket) + xq;
+        // (the raw ticket: nothing reads the atomic's result before this
+        // wait, which the first DMA needs anyway)
+        asm volatile("" ::: "memory");
+        if (queue && wi == 0 && tid == 0) s_next[par] = int(ticket);
         __syncthreads();
         if (queue && wi == 0) {
-            const int nb = __builtin_amdgcn_readfirstlane(s_next[par]);
-            if (lane < 8)
-                next_desc = nb < n_items ? reinterpret_cast<const uint32_t *>(items)[8 * nb + lane]
+            const int nb = n_lists * __builtin_amdgcn_readfirstlane(s_next[par]) + xq;
+            if (lane < 12)
+                next_desc = nb < n_items ? reinterpret_cast<const uint32_t *>(items)[12 * nb + lane]
                                          : (lane == 0 ? ~0u : 0u);
         }
         for (int j = 0; j < ntiles; j += 2) {
             tile(st0, st1, j, idB, idA);
             if (j + 1 < ntiles) tile(st1, st0, j + 1, idA, idB);
         }
+        // Nothing is in flight here (the last tile waited); saying so lets
+        // the next item's descriptor be read after the outputs below without
+        // waiting for their stores.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
 
         // Normalise.  The lane holds query qrow, dims 32t + 8g + 4hh + 0..3.
         const float l = halves_sum(l_run);
@@ -658,21 +690,27 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the staged rows are in LDS
             constexpr int RPI = 64 / VS::CH;      // rows per store
+            constexpr int NS = 32 / RPI;          // stores per wave
             const int nrows = min(32, nv - r0), rl = lane / VS::CH, c = lane % VS::CH;
             const uint8_t LDS_AS *const ib = ob + rl * kOutRow + 16 * c;
+            // All row ids and staged chunks are requested before the first
+            // store (rows past nrows read stale staging bytes that are never
+            // stored), so the LDS round trips overlap.
+            int trow[NS];
+            u32x4 val[NS];
 #pragma unroll
-            for (int i = 0; i < 32 / RPI; ++i) {
-                // tensor row of the wave's row RPI*i + rl (held by that lane)
-                const int trow = __builtin_amdgcn_ds_bpermute(4 * rl + 4 * RPI * i, int(qtrow));
-                if (rl < nrows - RPI * i) {
-                    const u32x4 val = *reinterpret_cast<const u32x4 LDS_AS *>(ib + RPI * i * kOutRow);
-                    *reinterpret_cast<u32x4 *>(out + int64_t(trow) * rs + hd + 8 * c) = val;
-                }
-            }
+            for (int i = 0; i < NS; ++i)  // tensor row of the wave's row RPI*i + rl (held by that lane)
+                trow[i] = __builtin_amdgcn_ds_bpermute(4 * rl + 4 * RPI * i, int(qtrow));
+#pragma unroll
+            for (int i = 0; i < NS; ++i) val[i] = *reinterpret_cast<const u32x4 LDS_AS *>(ib + RPI * i * kOutRow);
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                if (rl < nrows - RPI * i)
+                    *reinterpret_cast<u32x4 *>(out + int64_t(trow[i]) * rs + hd + 8 * c) = val[i];
         }
     }
     if (!queue) break;
-    // The next item: its descriptor words from lanes 0..7 (w < 0 ends the list).
+    // The next item: its descriptor words from lanes 0..11 (w < 0 ends the list).
     it.w = __builtin_amdgcn_readlane(int(next_desc), 0);
     it.hq = __builtin_amdgcn_readlane(int(next_desc), 1);
     it.nwin = __builtin_amdgcn_readlane(int(next_desc), 2);
@@ -681,6 +719,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
     it.win.lw = __builtin_amdgcn_readlane(int(next_desc), 5);
     it.win.vrow0 = __builtin_amdgcn_readlane(int(next_desc), 6);
     it.win.vrows = __builtin_amdgcn_readlane(int(next_desc), 7);
+    it.eh = __builtin_amdgcn_readlane(int(next_desc), 8);
+    it.ew = __builtin_amdgcn_readlane(int(next_desc), 9);
     par ^= 1;
     }
 #endif
@@ -701,7 +741,8 @@ hipError_t launch_attn_bf16(int head_dim, bool small, bool q8, const void *q, co
                             const void *tq, const void *tk, const void *tv, void *out, float *ws,
                             const int32_t *rel, const ItemDesc *items, const WinDesc *wins, int n_items,
                             const float *amax_q, const float *amax_k, const RopeTables *rope, int n_heads,
-                            int text_len, float scale, uint32_t *queue, int n_lists, hipStream_t s) {
+                            int text_len, float scale, uint32_t *queue, int n_lists, int grid_hw, int grid_w,
+                            hipStream_t s) {
     if (n_items <= 0) return hipSuccess;
     if (queue && n_lists != 1 && n_lists != 8) return hipErrorInvalidValue;
     if (q8 && head_dim != 128) return hipErrorInvalidValue;
@@ -727,7 +768,7 @@ hipError_t launch_attn_bf16(int head_dim, bool small, bool q8, const void *q, co
         kern<<<dim3(grid), dim3(64 * waves), 0, s>>>(B(q), B(k), U(v), B(tq), B(tk), U(tv),
                                                       static_cast<uint16_t *>(out), ws, rel, items, wins, amax_q,
                                                       amax_k, rt.cs, rt.pos, n_heads, text_len, c2, queue, n_items,
-                                                      n_lists);
+                                                      n_lists, grid_hw, grid_w);
     };
     auto dispatch = [&](auto waves_c) {
         constexpr int NW = decltype(waves_c)::value;

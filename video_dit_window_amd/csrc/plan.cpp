@@ -241,6 +241,9 @@ int build_items(const wsp_plan_t &p, int n_heads, int text_len, int bm, int orde
                 d.hq = (h << 16) | int(t);
                 d.chunk = joint(w) ? w : -1;
                 d.win = wins[size_t(w)];
+                const int32_t *bx = &p.boxes[6 * size_t(w)];
+                d.eh = bx[3] - bx[2];
+                d.ew = bx[5] - bx[4];
                 g.items.push_back(d);
             }
             if (own_text) text_items(w, h, g.items);

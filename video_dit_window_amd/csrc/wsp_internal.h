@@ -53,14 +53,20 @@ struct alignas(16) WinDesc {
 //    per-plan WinDesc table); the normalised outputs are summed into the
 //    float32 partial `chunk` of the workspace.
 //  w < 0: nothing to do.
-struct alignas(32) ItemDesc {
+//  eh, ew (video items): the window's box extents along h and w: row r of
+//    the window, (dt, dh, dw) with r = (dt * eh + dh) * ew + dw, lies
+//    dt*H*W + dh*W + dw canonical rows past its first row, so canonical-order
+//    kernels form the row ids of a video item without reading the ids table.
+struct alignas(16) ItemDesc {
     int32_t w;
     int32_t hq;
     int32_t nwin;
     int32_t chunk;
     WinDesc win;
+    int32_t eh, ew;
+    int32_t pad[2];
 };
-static_assert(sizeof(ItemDesc) == 32, "one 32-byte scalar load per work item");
+static_assert(sizeof(ItemDesc) == 48, "one 48-byte scalar load per work item");
 
 struct DeviceTables {
     int32_t *offsets = nullptr;                                 // [n_windows + 1]
@@ -141,7 +147,9 @@ constexpr size_t kQueueBytes = sizeof(uint32_t) * kQueueWords;
 // launches resident work groups instead (as many as fit on the device) that
 // take the items from n_lists lists in turn (n_lists 8: list x = items
 // 8t + x, taken by the work groups running on XCD x; 1: the whole list) --
-// the queue's counters are cleared by a kernel launched just before.  rel != NULL
+// the queue's counters are cleared by a kernel launched just before.
+// grid_hw = H*W and grid_w = W of the plan's grid (canonical-order row ids of
+// video items from their window boxes).  rel != NULL
 // selects canonical-order q/k/v/out: video row r of window w is tensor row
 // vrow0(w) + rel[offsets[w] + r] (the plan's ids relative to the window's
 // smallest id; items and windows resolved to match).  q8: q, k (and the text
@@ -160,7 +168,8 @@ hipError_t launch_attn_bf16(int head_dim, bool small, bool q8, const void *q, co
                             const void *tq, const void *tk, const void *tv, void *out, float *ws,
                             const int32_t *rel, const ItemDesc *items, const WinDesc *wins, int n_items,
                             const float *amax_q, const float *amax_k, const RopeTables *rope, int n_heads,
-                            int text_len, float scale, uint32_t *queue, int n_lists, hipStream_t s);
+                            int text_len, float scale, uint32_t *queue, int n_lists, int grid_hw, int grid_w,
+                            hipStream_t s);
 // attn_f32.hip: the float32 kernel (same items; ids != NULL: canonical-order
 // tensors, video row r of window w is tensor row ids[offsets[w] + r]).
 int attn_f32_tile_m(int head_dim);
