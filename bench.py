@@ -145,25 +145,43 @@ def stack_measure(w, n_layers, attn_flops_per_layer, reps=2):
     st = Stack(*geo, n_layers, w.heads, w.head_dim, Lt, canonical_io=True)
     ov, ot = torch.empty_like(xv), torch.empty_like(xt)
     stream = torch.cuda.current_stream()
-    # one projection launch on the stack's own buffers, timed alone
+    # one projection launch on the stack's own buffers, timed alone; beside
+    # it the q / k projection with the window-local rotation in its epilogue
+    # (wsp_linear_rope: canonical rows, layer 0's layout), plain - rotated -
+    # plain so that both see the same minutes of the box
+    plain = lambda: W.linear(st.X[0], wts[0][0], out=st.q)
+    rot = lambda: W.linear_rope(st.X[0], wts[0][0], st.canon, st.layout(0), Lt, out=st.q)
     for _ in range(3):
-        W.linear(st.X[0], wts[0][0], out=st.q)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(10):
-        W.linear(st.X[0], wts[0][0], out=st.q)
-    b.record(stream)
-    st.forward(xv, xt, wts, out_vid=ov, out_txt=ot)      # warm-up pass
+        plain()
+        rot()
+    marks = []
+    for fn in (plain, rot, plain):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(10):
+            fn()
+        b.record(stream)
+        marks.append((a, b))
+    # the same passes with rotated q / k (the q and k projections rotate as
+    # they store; attention unchanged), alternating with the plain passes
+    st_r = Stack(*geo, n_layers, w.heads, w.head_dim, Lt, canonical_io=True, rope_theta=10000.0)
+    st.forward(xv, xt, wts, out_vid=ov, out_txt=ot)      # warm-up passes
+    st_r.forward(xv, xt, wts, out_vid=ov, out_txt=ot)
     torch.cuda.synchronize()
-    lin_ms = a.elapsed_time(b) / 10
+    lin_ms = (marks[0][0].elapsed_time(marks[0][1]) + marks[2][0].elapsed_time(marks[2][1])) / 20
+    lin_rope_ms = marks[1][0].elapsed_time(marks[1][1]) / 10
     lin_flops = 2 * (N + Lt) * E * E
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
+    passes = {"plain": [], "rope": []}
     for _ in range(reps):
-        st.forward(xv, xt, wts, out_vid=ov, out_txt=ot)
-    s1.record(stream)
+        for name, s_ in (("plain", st), ("rope", st_r)):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            s_.forward(xv, xt, wts, out_vid=ov, out_txt=ot)
+            s1.record(stream)
+            passes[name].append((s0, s1))
     torch.cuda.synchronize()
-    ms = s0.elapsed_time(s1) / reps
+    ms = float(np.mean([a.elapsed_time(b) for a, b in passes["plain"]]))
+    ms_rope = float(np.mean([a.elapsed_time(b) for a, b in passes["rope"]]))
     layer_flops = 4 * lin_flops + attn_flops_per_layer
     return {"note": f"{n_layers}-layer stack: q/k/v/out projections (wsp_linear) + window attention + "
                     "regular/shifted alternating; the stream stays in canonical order and each layer's attention reads "
@@ -174,6 +192,8 @@ def stack_measure(w, n_layers, attn_flops_per_layer, reps=2):
             "tflops_per_pass": round(n_layers * layer_flops / (ms * 1e-3) / 1e12, 2),
             "linear_avg_ms": round(lin_ms, 4),
             "linear_kernel_tflops": round(lin_flops / (lin_ms * 1e-3) / 1e12, 2),
+            "linear_rope_avg_ms": round(lin_rope_ms, 4),
+            "rope_ms_per_pass": round(ms_rope, 3), "rope_ms_per_layer": round(ms_rope / n_layers, 4),
             "flop_per_layer": {"projections": 4 * lin_flops, "attention": attn_flops_per_layer}}
 
 
@@ -512,6 +532,19 @@ def main():
         res["configs"] = config_launches([("720p_bf16", "regular"), ("4k_bf16", "shifted")])
     if not args.no_stack:
         res["stack"] = stack_measure(w, args.stack_layers, per_call_flops)
+        if "rope_attention" in res:
+            # RoPE where the real block has it: the q and k projections rotate
+            # as they store (wsp_linear_rope) and attention runs unchanged, so
+            # the layer's extra cost is what the two rotating epilogues add
+            sm, ra = res["stack"], res["rope_attention"]
+            extra = 2.0 * (sm["linear_rope_avg_ms"] - sm["linear_avg_ms"])
+            ra["fused_projection"] = {
+                "note": "q / k rotated in the epilogue of their projections (wsp_linear_rope), plain attention "
+                        "launch: extra ms per layer = 2 x (rotating - plain projection launch); ratio = (plain "
+                        "attention launch + extra) / plain attention launch; per layer of the stack passes too",
+                "qk_projection_extra_ms": round(extra, 4),
+                "ratio_vs_plain_layer": round((ra["plain_layer_ms"] + extra) / ra["plain_layer_ms"], 4),
+                "stack_layer_extra_ms": round(sm["rope_ms_per_layer"] - sm["ms_per_layer"], 4)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(res), flush=True)

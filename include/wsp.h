@@ -477,13 +477,47 @@ int wsp_set_attn_schedule(int schedule);
 int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, int N, int K,
                int dtype, void *stream);
 
+/*
+ * wsp_linear_rope -- the q or k projection of a window layer with the
+ * window-local 3D rotary embedding applied as the products are stored:
+ * y = rotate(bf16(x w^T)), bit for bit what wsp_linear (r = NULL) followed by
+ * wsp_rope_relayout (src = dst = rows, pos) on the video rows and
+ * wsp_rope_text on the text rows would leave, without that second pass over
+ * y.
+ *
+ * "Window-Aligned Sequence Parallelism (SeedVR2)", section "Reference quirks
+ * reproduced on purpose" (a video token turns by its offset from its own
+ * window's corner, the temporal index raised by text_len; 126 of 128
+ * channels); the readings of wsp_rope_relayout (axis blocks, pair layout,
+ * theta, text positions (i, i, i)).
+ *
+ * x [M, K], w [N, K], y [M, N]: row-major bfloat16 device arrays owned by the
+ * caller, 16-byte aligned, y aliasing neither x nor w.  M = rows' token count
+ * + text_len: rows 0 .. n-1 are the video tokens in the row order of plan
+ * `rows` (a canonical plan for canonical order, or a layout), rows n ..
+ * n+text_len-1 the text tokens 0 .. text_len-1.  Every 128 output features
+ * form one head (N a positive multiple of 256), rotated alike; each video row
+ * turns by its token's window-local position in layout `pos` (same grid as
+ * `rows`; window extents <= 1024 (t), 2048 (h, w)).  K as wsp_linear.
+ * theta: rotary base (<= 0 or non-finite: 10000).  dtype must be WSP_BF16.
+ * The first call for a plan uploads its id / position tables and the first
+ * call for a (theta, position count) pair its (cos, sin) table, kept until the
+ * process ends (as wsp_rope_relayout).  Asynchronous on `stream`; errors:
+ * WSP_EINVAL (arguments as wsp_linear, NULL plans, grids differ, M, text_len
+ * outside 0..2^20), WSP_ERANGE (M, window extents), WSP_ENOMEM, WSP_EDEVICE;
+ * nothing is launched on error.
+ */
+int wsp_linear_rope(const void *x, const void *w, void *y, int64_t M, int N, int K, int dtype,
+                    const wsp_plan_t *rows, const wsp_plan_t *pos, int text_len, float theta,
+                    void *stream);
+
 /* wsp_last_error -- message of the calling thread's last failed call ("" if none). */
 const char *wsp_last_error(void);
 
 /* wsp_version -- ABI version of this header (major*10000 + minor*100 + patch). */
 int wsp_version(void);
 
-#define WSP_VERSION 20300
+#define WSP_VERSION 20400
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,11 @@ follows (the pages fix none of it):
   * storage points are bfloat16, rounded to nearest even exactly where the
     GPU path stores them: q / k / v, the attention output and the text mean,
     and the residual stream after each update.  Everything in between is
-    float64 here (the GPU path accumulates in float32).
+    float64 here (the GPU path accumulates in float32);
+  * optionally (rope_theta given) q and k turn by the window-local 3D rotary
+    embedding of the layer's layout after their projection (oracle/wsp_rope.py,
+    "Reference quirks reproduced on purpose"; text token i at (i, i, i)) and
+    are rounded to bfloat16 again.
 
 Parity pins (tests/test_stack_pins.py): Wo = 0 leaves the stream unchanged;
 zero query/key projections with identity value and output projections give
@@ -35,6 +39,7 @@ from __future__ import annotations
 import numpy as np
 
 from .wsp_oracle import canonical_plan, layer_schedule, plan, relayout, window_attn
+from .wsp_rope import rope, text_positions, window_positions
 
 __all__ = ["bf16_round", "linear", "stack_forward"]
 
@@ -55,7 +60,8 @@ def linear(x, w, r=None) -> np.ndarray:
     return bf16_round(y)
 
 
-def stack_forward(x_vid, x_txt, geo, weights, heads: int, head_dim: int, scale=None, first_layer: int = 0):
+def stack_forward(x_vid, x_txt, geo, weights, heads: int, head_dim: int, scale=None, first_layer: int = 0,
+                  rope_theta=None):
     """One pass of the stack.
 
     x_vid: [N, E] video hidden state in canonical token order, x_txt: [Lt, E]
@@ -64,6 +70,7 @@ def stack_forward(x_vid, x_txt, geo, weights, heads: int, head_dim: int, scale=N
     first_layer: schedule index of weights[0] (the layers run are
     first_layer .. first_layer + len(weights) - 1 of the alternating
     schedule, so a pass can be resumed from any layer's state).
+    rope_theta: rotary base of the optional q / k rotation (None: none).
     Returns the video state back in canonical order and the text state."""
     T, H, W = geo[:3]
     n_layers = len(weights)
@@ -76,6 +83,11 @@ def stack_forward(x_vid, x_txt, geo, weights, heads: int, head_dim: int, scale=N
     for l, (wq, wk, wv, wo) in enumerate(weights):
         X = np.concatenate([x, t], axis=0)
         q, k, v = linear(X, wq), linear(X, wk), linear(X, wv)
+        if rope_theta is not None:
+            # rows of X are the video tokens in layout l's order, then the text
+            pos3 = np.concatenate([window_positions(layouts[l], Lt)[layouts[l].ids], text_positions(Lt)], axis=0)
+            q, k = (bf16_round(rope(a.reshape(N + Lt, heads, head_dim), pos3, rope_theta)).reshape(N + Lt, -1)
+                    for a in (q, k))
         split = lambda a: (a[:N].reshape(N, heads, head_dim), a[N:].reshape(Lt, heads, head_dim))
         (qv, qt), (kv, kt), (vv, vt) = split(q), split(k), split(v)
         out, mean = window_attn(layouts[l], qv, kv, vv, qt, kt, vt, scale=scale)

@@ -62,7 +62,8 @@ hipError_t launch_fp8_amax(const void *, float *, int64_t, int, int, int, hipStr
 hipError_t launch_fp8_quantize(const void *, void *, const float *, int64_t, int, int, int, hipStream_t) {
     reached("fp8_quantize");
 }
-hipError_t launch_gemm_bf16(const void *, const void *, void *, const void *, int64_t, int, int, hipStream_t) {
+hipError_t launch_gemm_bf16(const void *, const void *, void *, const void *, int64_t, int, int, const GemmRope *,
+                            hipStream_t) {
     reached("gemm");
 }
 hipError_t launch_text_mean(const float *, void *, int64_t, int, int, int, hipStream_t) { reached("text_mean"); }

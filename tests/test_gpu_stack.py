@@ -287,3 +287,175 @@ def test_stack_1080p_two_layers_sampled(gpu):
     got = rows(x2)(ids)
     check_bf16(got, ref, f"1080p stack layer 1, shifted window {win}")
     check_update(got, ref, rows(x1)(ids), f"1080p stack layer 1 update, shifted window {win}")
+
+
+# ---- q / k projections with the window-local rotary embedding (wsp_linear_rope)
+
+ROPE_GEO = (6, 30, 52, 2, 3, 3)     # 9360 video rows: the last 256-row tile is ragged
+ROPE_CASES = [("canonical", "regular"), ("canonical", "shifted"), ("regular", "regular"),
+              ("shifted", "shifted"), ("canonical", "canonical")]
+
+
+def rope_plans(geo):
+    return {"canonical": W.canonical(*geo[:3]), "regular": W.Plan(*geo, W.REGULAR),
+            "shifted": W.Plan(*geo, W.SHIFTED)}
+
+
+def linear_rope_chain(dx, dw, g, rows, pos, text_len, theta):
+    """wsp_linear, then wsp_rope_relayout (src = dst = rows) over the video
+    rows and wsp_rope_text over the text rows."""
+    import torch
+    plain = W.linear(dx, dw)
+    n, heads = g[rows].n_tokens, dw.shape[0] // 128
+    ref = torch.empty_like(plain)
+    W.rope_relayout(plain[:n].view(n, heads, 128), g[rows], g[rows], g[pos], text_len, theta=theta,
+                    out=ref[:n].view(n, heads, 128))
+    if text_len:
+        W.rope_text(plain[n:].view(text_len, heads, 128), theta=theta, out=ref[n:].view(text_len, heads, 128))
+    return ref
+
+
+@pytest.mark.parametrize("text_len", [0, 19])
+@pytest.mark.parametrize("case", ROPE_CASES, ids=["-".join(c) for c in ROPE_CASES])
+def test_linear_rope_bit_identical_to_chain(gpu, case, text_len):
+    """The rotation in the projection's epilogue leaves exactly what the
+    projection followed by the stand-alone rotation kernels leaves (4 heads,
+    K = 192, rows in canonical or layout order; theta 500 with text)."""
+    import torch
+    rows, pos = case
+    g = rope_plans(ROPE_GEO)
+    M = g[rows].n_tokens + text_len
+    seed = 300 + 7 * ROPE_CASES.index(case) + text_len
+    dx, dw = bf16_dev(rnd_bf16((M, 192), seed)), bf16_dev(rnd_bf16((512, 192), seed + 1, std=0.08))
+    theta = 500.0 if text_len else None
+    y = W.linear_rope(dx, dw, g[rows], g[pos], text_len, theta=theta)
+    ref = linear_rope_chain(dx, dw, g, rows, pos, text_len, theta)
+    torch.cuda.synchronize()
+    same = torch.equal(y.view(torch.int16), ref.view(torch.int16))
+    log(f"  linear_rope rows {rows}, positions of {pos}, text_len {text_len}: bit-identical = {same}")
+    assert same
+
+
+def oracle_linear_rope(x, w, ids_rows, pos_plan, text_len, theta=O.ROPE_THETA):
+    """Oracle of the rotated projection for rows x (video rows first, tokens
+    ids_rows, then text rows): bf16(rope(bf16(x w^T))) and the per-element
+    error allowance of the GPU's float32 arithmetic."""
+    n = len(ids_rows)
+    p = O.linear(x, w)
+    heads = w.shape[0] // 128
+    pos3 = np.concatenate([O.window_positions(pos_plan, text_len)[ids_rows], O.text_positions(text_len)], axis=0)
+    ref = O.bf16_round(O.rope(p.reshape(-1, heads, 128), pos3, theta).reshape(p.shape))
+    # the product may round to the neighbouring bf16 value (float32
+    # accumulation, as test_linear's bound); a rotated pair mixes both of its
+    # channels' errors; the result rounds once more (2^-8 relative)
+    acc = 2.0 * x.shape[1] * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T)
+    d = (ulp_bf16(np.abs(p) + acc) + acc).reshape(-1, heads, 64, 2)
+    pair = np.repeat(d.sum(axis=3, keepdims=True), 2, axis=3)
+    pair[:, :, 63, :] = d[:, :, 63, :]                 # channels 126, 127 pass through
+    return ref, 2.0 ** -8 * np.abs(ref) + 1e-6 + pair.reshape(p.shape)
+
+
+@pytest.mark.parametrize("method", ["regular", "shifted"])
+@pytest.mark.parametrize("rows", ["canonical", "layout"])
+def test_linear_rope_oracle(gpu, method, rows):
+    """Against the float64 oracle: the projection rounded to bf16, rotated by
+    the oracle's window-local positions (text rows at (i, i, i)), rounded
+    again -- element by element within the float32 allowance, and at the bf16
+    bar."""
+    import torch
+    T, H, Wd, nt, nh, nw = ROPE_GEO
+    om = O.REGULAR if method == "regular" else O.SHIFTED
+    op = O.plan(*ROPE_GEO, om)
+    g = rope_plans(ROPE_GEO)
+    ids = np.arange(T * H * Wd) if rows == "canonical" else op.ids
+    rp = g["canonical"] if rows == "canonical" else g[method]
+    Lt = 40
+    x = rnd_bf16((len(ids) + Lt, 256), 330 + len(method) + len(rows))
+    w = rnd_bf16((512, 256), 331, std=0.08)
+    y = W.linear_rope(bf16_dev(x), bf16_dev(w), rp, g[method], Lt)
+    torch.cuda.synchronize()
+    ref, bound = oracle_linear_rope(x, w, ids, op, Lt)
+    got = from_dev(y)
+    err = np.abs(got - ref)
+    log(f"  linear_rope {rows} rows, {method} positions: max|err| {err.max():.3e}, "
+        f"{int((err > bound).sum())} beyond the allowance")
+    assert np.all(err <= bound)
+    check_bf16(got, ref, f"linear_rope {rows} rows, {method} positions")
+
+
+def test_linear_rope_1080p(gpu):
+    """The 1080p q / k projection (171360 video rows in canonical order + 256
+    text rows, 2560 -> 2560, 20 heads of 128), rotated for the shifted layout:
+    bit-identical to the two-pass chain over the whole output, and sampled
+    rows (video rows of several windows and text rows) against the oracle."""
+    import torch
+    w = I.WORKLOADS["1080p_bf16"]
+    geo = (w.T, w.H, w.W, w.nt, w.nh, w.nw)
+    E, Lt, N = w.heads * w.head_dim, w.text_len, w.n_tokens
+    g = rope_plans(geo)
+    rng = np.random.default_rng(91)
+    log("  generating 1080p projection inputs")
+    xb = I.f32_to_bf16_bits(rng.standard_normal((N + Lt, E), dtype=np.float32))
+    wb = I.f32_to_bf16_bits(rng.standard_normal((E, E), dtype=np.float32) * np.float32(0.02))
+    dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    dx, dw = dev(xb), dev(wb)
+    y = W.linear_rope(dx, dw, g["canonical"], g["shifted"], Lt)
+    ref = linear_rope_chain(dx, dw, g, "canonical", "shifted", Lt, None)
+    torch.cuda.synchronize()
+    same = torch.equal(y.view(torch.int16), ref.view(torch.int16))
+    log(f"  1080p linear_rope vs chain: bit-identical = {same}")
+    assert same
+    del ref
+    sample = np.concatenate([rng.choice(N, 96, replace=False), [0, N - 1], N + np.arange(0, Lt, 37), [N + Lt - 1]])
+    x = I.bf16_bits_to_f32(xb[sample]).astype(np.float64)
+    wv = I.bf16_bits_to_f32(wb).astype(np.float64)
+    op = O.plan(*geo, O.SHIFTED)
+    vid = sample < N
+    pos = np.concatenate([O.window_positions(op, Lt)[sample[vid]], O.text_positions(Lt)[sample[~vid] - N]], axis=0)
+    p = O.linear(x, wv)
+    want = O.bf16_round(O.rope(p.reshape(-1, w.heads, 128), pos).reshape(p.shape))
+    got = from_dev(y[torch.from_numpy(sample.astype(np.int64)).cuda()])
+    check_bf16(got, want, "1080p linear_rope, sampled rows")
+
+
+def test_linear_rope_rejects_bad_arguments(gpu):
+    """Row count not the plan's tokens + text, float32 operands, N not a
+    multiple of 256: refused before any launch."""
+    import torch
+    g = rope_plans(ROPE_GEO)
+    n = g["canonical"].n_tokens
+    z = lambda *shape, dt=torch.bfloat16: torch.zeros(shape, dtype=dt, device="cuda")
+    with pytest.raises(ValueError):
+        W.linear_rope(z(n + 3, 64), z(256, 64), g["canonical"], g["regular"], 2)
+    with pytest.raises(W.WspError):
+        W.linear_rope(z(n, 64, dt=torch.float32), z(256, 64, dt=torch.float32), g["canonical"], g["regular"], 0)
+    with pytest.raises(W.WspError):
+        W.linear_rope(z(n, 64), z(128, 64), g["canonical"], g["regular"], 0)
+
+
+@pytest.mark.parametrize("n_layers", [1, 3])
+def test_stack_rope_tiny(gpu, n_layers):
+    """Layers with rotated q / k (2 heads of 128, 16 text tokens) on the tiny
+    grid: explicit permutations and canonical-order I/O agree bit for bit and
+    match the oracle's stack with the rotation."""
+    import torch
+    heads, hd, lt = 2, 128, 16
+    E, N = heads * hd, GEO[0] * GEO[1] * GEO[2]
+    rng = np.random.default_rng(500 + n_layers)
+    x, t = O.bf16_round(rng.standard_normal((N, E))), O.bf16_round(rng.standard_normal((lt, E)))
+    weights = [tuple(O.bf16_round(rng.standard_normal((E, E)) * 0.05) for _ in range(4)) for _ in range(n_layers)]
+    dw = [tuple(bf16_dev(a) for a in wl) for wl in weights]
+    res = {}
+    for canon in (False, True):
+        st = Stack(*GEO, n_layers, heads, hd, lt, canonical_io=canon, rope_theta=10000.0)
+        res[canon] = st.forward(bf16_dev(x), bf16_dev(t), dw)
+    plain = Stack(*GEO, n_layers, heads, hd, lt, canonical_io=True).forward(bf16_dev(x), bf16_dev(t), dw)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_bits(res[False][0]), dev_bits(res[True][0])), "video state: I/O orders differ"
+    assert np.array_equal(dev_bits(res[False][1]), dev_bits(res[True][1])), "text state: I/O orders differ"
+    assert not np.array_equal(dev_bits(res[True][0]), dev_bits(plain[0])), "the rotation changed nothing"
+    ref_x, ref_t = O.stack_forward(x, t, GEO, weights, heads, hd, rope_theta=10000.0)
+    check_bf16(from_dev(res[True][0]), ref_x, f"rope stack {n_layers} layers video")
+    check_bf16(from_dev(res[True][1]), ref_t, f"rope stack {n_layers} layers text")
+    for got, ref, inp, what in ((res[True][0], ref_x, x, "video"), (res[True][1], ref_t, t, "text")):
+        check_update(from_dev(got), ref, inp, f"rope stack {n_layers} layers {what} update")

@@ -186,6 +186,35 @@ def test_rope_argument_errors():
     assert L.wsp_rope_text(a, b, 0, 4, 128, W.BF16, f0, None) == 0      # nothing to do
 
 
+def test_linear_rope_argument_errors():
+    """wsp_linear_rope validates everything before touching the device."""
+    c = W.canonical(5, 20, 36)
+    p = W.Plan(5, 20, 36, 2, 3, 3, W.REGULAR)
+    other = W.Plan(5, 20, 40, 2, 3, 3, W.REGULAR)
+    tall = W.Plan(2, 6000, 2, 1, 1, 1, W.REGULAR)          # windows 3286 rows high > 2048
+    tall_c = W.canonical(2, 6000, 2)
+    L = raw()
+    x, w, y = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    f0 = ctypes.c_float(0)
+    n = 5 * 20 * 36
+
+    def call(x=x, w=w, y=y, M=n + 16, N=256, K=64, dt=W.BF16, rows=c, pos=p, Lt=16):
+        return L.wsp_linear_rope(x, w, y, M, N, K, dt, rows.handle if rows else None,
+                                 pos.handle if pos else None, Lt, f0, None)
+
+    assert call(M=n) == -1 and b"token count" in L.wsp_last_error()
+    assert call(rows=None) == -1 and call(pos=None) == -1
+    assert call(pos=other) == -1 and b"grids" in L.wsp_last_error()
+    assert call(Lt=-1, M=n - 1) == -1
+    assert call(dt=W.F32) == -1
+    assert call(N=128) == -1                                 # not a multiple of 256
+    assert call(K=96) == -1
+    assert call(x=None) == -1
+    assert call(y=x) == -1                                   # y aliases x
+    assert call(w=ctypes.c_void_p(0x2008)) == -1             # misaligned
+    assert call(rows=tall_c, pos=tall, M=2 * 6000 * 2, Lt=0) == -2 and b"extents" in L.wsp_last_error()
+
+
 def test_attn_schedule_option():
     L = raw()
     assert L.wsp_set_attn_schedule(6) == -1

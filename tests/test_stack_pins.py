@@ -7,7 +7,9 @@ path: bfloat16 rounding on exactly representable values and ties, the
 orientation of the projection by selection matrices, a zero output
 projection that must leave the stream unchanged, and zero query/key
 projections whose uniform attention gives window means computed from
-coordinates.
+coordinates.  With the optional q / k rotation: zero q / k projections are
+unaffected by it (it touches q and k only), and windows of one shape and the
+same content give equal outputs (positions restart in every window).
 """
 import numpy as np
 import pytest
@@ -114,3 +116,44 @@ def test_resumed_layer_uses_its_schedule_layout(first_layer):
     x1, t1 = O.stack_forward(x, t, GEO, w[:1], HEADS, HD)
     rest = O.stack_forward(x1, t1, GEO, w[1:], HEADS, HD, first_layer=1)
     assert np.array_equal(full[0], rest[0]) and np.array_equal(full[1], rest[1])
+
+
+def test_rope_stack_with_zero_qk_is_plain():
+    """The rotation acts on q and k only: with Wq = Wk = 0 every score is 0
+    with or without it, so the two stacks agree exactly."""
+    rng = np.random.default_rng(12)
+    heads, hd, lt = 1, 128, 3
+    e = heads * hd
+    N = GEO[0] * GEO[1] * GEO[2]
+    x, t = O.bf16_round(rng.standard_normal((N, e))), O.bf16_round(rng.standard_normal((lt, e)))
+    z = np.zeros((e, e))
+    w = [(z, z) + tuple(O.bf16_round(rng.standard_normal((e, e)) * 0.1) for _ in range(2)) for _ in range(2)]
+    plain = O.stack_forward(x, t, GEO, w, heads, hd)
+    rot = O.stack_forward(x, t, GEO, w, heads, hd, rope_theta=10000.0)
+    assert np.array_equal(plain[0], rot[0]) and np.array_equal(plain[1], rot[1])
+
+
+def test_rope_stack_positions_restart_per_window():
+    """The shifted layout of a 2 x 4 x 6 grid (nt = 1, nh = nw = 2) has two
+    windows, the frames t = 0 and t = 1 (4 x 6 tokens each).  Video rows that
+    depend on (h, w) only give both windows the same content at the same
+    window-local positions, so one shifted layer with the rotation leaves
+    both frames' rows equal; in the regular layout (one 2 x 4 x 6 window) the
+    frames sit at temporal positions text_len + 0 and + 1 and come out
+    different, so the rotation does see the temporal position."""
+    geo = (2, 4, 6, 1, 2, 2)
+    heads, hd, lt = 1, 128, 3
+    e = heads * hd
+    for method, boxes in ((O.SHIFTED, [(0, 1, 0, 4, 0, 6), (1, 2, 0, 4, 0, 6)]), (O.REGULAR, [(0, 2, 0, 4, 0, 6)])):
+        assert [tuple(int(v) for v in b) for b in O.plan(*geo, method).boxes] == boxes
+    rng = np.random.default_rng(13)
+    frame = O.bf16_round(rng.standard_normal((24, e)))
+    x = np.concatenate([frame, frame], axis=0)         # canonical order: t = 0 rows, then t = 1 rows
+    t = O.bf16_round(rng.standard_normal((lt, e)))
+    w = [tuple(O.bf16_round(rng.standard_normal((e, e)) * 0.1) for _ in range(4))]
+    xs, _ = O.stack_forward(x, t, geo, w, heads, hd, first_layer=1, rope_theta=10000.0)
+    assert np.array_equal(xs[:24], xs[24:])
+    xr, _ = O.stack_forward(x, t, geo, w, heads, hd, first_layer=0, rope_theta=10000.0)
+    assert not np.array_equal(xr[:24], xr[24:])
+    xn, _ = O.stack_forward(x, t, geo, w, heads, hd, first_layer=0)
+    assert np.array_equal(xn[:24], xn[24:])             # without the rotation the frames stay equal

@@ -51,6 +51,8 @@ _SIGNATURES = {
     "wsp_window_attn_qk8": (_c_int, [_c_vp] * 9 + [_c_int, _c_int, _c_int, ctypes.c_float, ctypes.c_uint,
                                                     _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "wsp_linear": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp]),
+    "wsp_linear_rope": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_int,
+                                 ctypes.c_float, _c_vp]),
     "wsp_set_attn_order": (_c_int, [_c_int]),
     "wsp_device_info": (_c_int, [_i32p, _i32p]),
     "wsp_set_attn_schedule": (_c_int, [_c_int]),
@@ -213,6 +215,30 @@ def linear(x, w, residual=None, out=None, stream=None):
     rp = None if residual is None else _dev_ptr(residual, "residual")
     _check("wsp_linear", lib().wsp_linear(_dev_ptr(x, "x"), _dev_ptr(w, "w"), rp, _dev_ptr(out, "out"), M, N, K,
                                           _dtype_code(x.dtype), _stream(stream)))
+    return out
+
+
+def linear_rope(x, w, rows: Plan, pos: Plan, text_len, theta=None, out=None, stream=None):
+    """q or k projection with the window-local rotary embedding applied as it
+    is stored (wsp_linear_rope): x [n + text_len, K] holds the video rows in
+    the row order of `rows` followed by the text rows, w [N, K] with N =
+    heads * 128; each video row turns by its token's window-local position in
+    layout `pos`, text row i by (i, i, i)."""
+    torch = _torch()
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [M, K] and w [N, K]")
+    M, K = x.shape
+    N = w.shape[0]
+    if M != rows.n_tokens + int(text_len):
+        raise ValueError("x must hold the plan's tokens followed by text_len text rows")
+    if out is None:
+        with _on(stream):
+            out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if tuple(out.shape) != (M, N) or out.dtype != x.dtype or w.dtype != x.dtype:
+        raise ValueError("out must be [M, N] with the dtype of x and w")
+    _check("wsp_linear_rope", lib().wsp_linear_rope(
+        _dev_ptr(x, "x"), _dev_ptr(w, "w"), _dev_ptr(out, "out"), M, N, K, _dtype_code(x.dtype), rows.handle,
+        pos.handle, int(text_len), ctypes.c_float(0.0 if theta is None else theta), _stream(stream)))
     return out
 
 

@@ -820,10 +820,13 @@ int wsp_window_attn_qk8(const wsp_plan_t *pc, const void *q8, const void *k8, co
                             amax_q, amax_k, scale, flags, out, txt_out, workspace, workspace_bytes, stream);
 }
 
-int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, int N, int K,
-               int dtype, void *stream) {
-    g_last_error.clear();
-    if (dtype != WSP_BF16) return fail(WSP_EINVAL, "wsp_linear supports WSP_BF16 only");
+namespace {
+
+// Checks shared by wsp_linear and wsp_linear_rope; WSP_OK with M == 0 means
+// nothing to do.
+int linear_args(const void *x, const void *w, const void *r, const void *y, int64_t M, int N, int K,
+                int dtype, const char *name) {
+    if (dtype != WSP_BF16) return fail(WSP_EINVAL, std::string(name) + " supports WSP_BF16 only");
     if (M < 0) return fail(WSP_EINVAL, "M must be >= 0");
     if (N <= 0 || N % gemm_bf16_tile_n() != 0)
         return fail(WSP_EINVAL, "N must be a positive multiple of " + std::to_string(gemm_bf16_tile_n()));
@@ -833,10 +836,50 @@ int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, 
     if (M == 0) return WSP_OK;
     if (M > int64_t(0x7FFFFFFF) - 256) return fail(WSP_ERANGE, "M is too large");
     if (!x || !w || !y) return fail(WSP_EINVAL, "x, w and y must be non-NULL");
-    for (const void *ptr : {x, w, r, static_cast<const void *>(y)})
+    for (const void *ptr : {x, w, r, y})
         if (ptr && !aligned16(ptr)) return fail(WSP_EINVAL, "x, w, r and y must be 16-byte aligned");
     if (y == x || y == w) return fail(WSP_EINVAL, "y must not alias x or w");
-    hipError_t e = launch_gemm_bf16(x, w, y, r, M, N, K, hipStream_t(stream));
+    return WSP_OK;
+}
+
+}  // namespace
+
+int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, int N, int K,
+               int dtype, void *stream) {
+    g_last_error.clear();
+    int rc = linear_args(x, w, r, y, M, N, K, dtype, "wsp_linear");
+    if (rc || M == 0) return rc;
+    hipError_t e = launch_gemm_bf16(x, w, y, r, M, N, K, nullptr, hipStream_t(stream));
+    if (e != hipSuccess) return hip_fail(e, "linear kernel launch");
+    return WSP_OK;
+}
+
+int wsp_linear_rope(const void *x, const void *w, void *y, int64_t M, int N, int K, int dtype,
+                    const wsp_plan_t *rows, const wsp_plan_t *pos, int text_len, float theta,
+                    void *stream) {
+    g_last_error.clear();
+    if (!rows || !pos) return fail(WSP_EINVAL, "plan is NULL");
+    if (rows->T != pos->T || rows->H != pos->H || rows->W != pos->W)
+        return fail(WSP_EINVAL, "plans of different grids");
+    if (text_len < 0 || text_len > (1 << 20)) return fail(WSP_EINVAL, "text_len must be in 0..2^20");
+    if (M != rows->n + int64_t(text_len))
+        return fail(WSP_EINVAL, "M must be the plan's token count plus text_len (" +
+                                    std::to_string(rows->n + int64_t(text_len)) + "), got " + std::to_string(M));
+    int rc = linear_args(x, w, nullptr, y, M, N, K, dtype, "wsp_linear_rope");
+    if (rc || M == 0) return rc;
+    if (pos->max_ext[0] > 1024 || pos->max_ext[1] > 2048 || pos->max_ext[2] > 2048)
+        return fail(WSP_ERANGE, "window extents beyond 1024 (t) / 2048 (h, w)");
+    if (!(theta > 0.0f) || !std::isfinite(theta)) theta = 10000.0f;
+    const int P = std::max({text_len + pos->max_ext[0], pos->max_ext[1], pos->max_ext[2], 1});
+    int dev = 0;
+    WSP_HIP(hipGetDevice(&dev));
+    int32_t *cid = nullptr, *ptab = nullptr;
+    const float2 *cs = nullptr;
+    if ((rc = device_ids(*const_cast<wsp_plan_t *>(rows), dev, &cid))) return rc;
+    if ((rc = device_positions(*const_cast<wsp_plan_t *>(pos), dev, &ptab))) return rc;
+    if ((rc = rope_table(dev, theta, P, &cs))) return rc;
+    const GemmRope rp{cid, ptab, cs, int(rows->n), text_len};
+    hipError_t e = launch_gemm_bf16(x, w, y, nullptr, M, N, K, &rp, hipStream_t(stream));
     if (e != hipSuccess) return hip_fail(e, "linear kernel launch");
     return WSP_OK;
 }

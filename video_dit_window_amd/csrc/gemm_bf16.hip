@@ -22,6 +22,20 @@
 // Tiles are mapped so that the 256-row slabs of x go round-robin to the 8
 // XCDs (work group b runs on XCD b % 8) and the N tiles of one x slab run
 // side by side on one XCD, sharing the slab through its L2.
+//
+// ROPE: the q / k projections of a window layer, with the window-local 3D
+// rotary embedding applied where the products are stored ("Window-Aligned
+// Sequence Parallelism (SeedVR2)", section "Reference quirks reproduced on
+// purpose": a video token turns by its offset from its own window's corner,
+// the temporal index raised by the text length; 126 of 128 channels turn, in
+// three 42-channel axis blocks of adjacent pairs; text token i uses (i, i, i)).
+// Every 128 output features form one head.  The epilogue holds four
+// consecutive features of a row per lane, i.e. two whole pairs, so each pair
+// turns in registers: the product is rounded to bfloat16 first and the
+// rotation runs in float32 from that value, then rounds again -- the same
+// steps as the stand-alone rotation kernel applied to the stored projection,
+// so the result is bit-identical to that two-pass chain without its extra
+// read and write of q and k.
 
 #include "wsp_internal.h"
 
@@ -50,10 +64,25 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <bool RES>
+constexpr int kRopeSpanPairs = 63;  // pairs 0..62 turn, pair 63 (channels 126, 127) passes
+constexpr int kRopeAxisPairs = 21;  // 42 channels per axis block
+
+// Pair k (two bf16 channels packed in w) of a head rotated by the row's
+// (cos, sin) entry cs[pb[axis of k] + k]: float32 arithmetic, one rounding;
+// pair 63 passes through.
+__device__ inline uint32_t rope_pair(uint32_t w, int k, const int (&pb)[3], const float2 *__restrict__ cs) {
+    if (k >= kRopeSpanPairs) return w;
+    const int ax = k >= 2 * kRopeAxisPairs ? 2 : (k >= kRopeAxisPairs ? 1 : 0);
+    const float2 t = cs[pb[ax] + k];
+    const f32x2 f = __builtin_convertvector(__builtin_bit_cast(bf16x2, w), f32x2);
+    const f32x2 o = {fmaf(f.x, t.x, -f.y * t.y), fmaf(f.x, t.y, f.y * t.x)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2));
+}
+
+template <bool RES, bool ROPE>
 __global__ __launch_bounds__(64 * kGWaves, 2) void gemm_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *y,
-    const uint16_t *r, int M, int N, int K, int m_tiles, int n_tiles) {
+    const uint16_t *r, int M, int N, int K, int m_tiles, int n_tiles, GemmRope rp) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     __shared__ __attribute__((aligned(1024))) uint8_t sx0[kGTile];
     __shared__ __attribute__((aligned(1024))) uint8_t sw0[kGTile];
@@ -165,13 +194,33 @@ __global__ __launch_bounds__(64 * kGWaves, 2) void gemm_bf16_kernel(
     }
 
     // Epilogue: acc[mb][nb] register 4g + e holds y[m][n] with m = m0 +
-    // wm*64 + 32mb + l32 and n = n0 + wn*128 + 32nb + 8g + 4hh + e.
+    // wm*64 + 32mb + l32 and n = n0 + wn*128 + 32nb + 8g + 4hh + e.  The
+    // wave's 128 features are one head (n0 + wn*128 is a multiple of 128):
+    // feature pair 16nb + 4g + 2hh + h of it sits in register pair (4g + 2h,
+    // 4g + 2h + 1).
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
         const int m = m0 + wm * 64 + 32 * mb + l32;
         if (m >= M) continue;
         uint16_t *yrow = y + int64_t(m) * N + n0 + wn * 128 + 4 * hh;
         const uint16_t *rrow = RES ? r + int64_t(m) * N + n0 + wn * 128 + 4 * hh : nullptr;
+        // ROPE: cs index of pair k of the row is pb[axis of k] + k (the
+        // row's axial position times 21, less the axis block's first pair).
+        int pb[3] = {0, 0, 0};
+        if constexpr (ROPE) {
+            int p0, p1, p2;
+            if (m < rp.n_video) {
+                const uint32_t v = uint32_t(rp.pos[rp.cid[m]]);
+                p0 = rp.text_len + int(v & 1023u);
+                p1 = int((v >> 10) & 2047u);
+                p2 = int(v >> 21);
+            } else {
+                p0 = p1 = p2 = m - rp.n_video;
+            }
+            pb[0] = p0 * kRopeAxisPairs;
+            pb[1] = (p1 - 1) * kRopeAxisPairs;
+            pb[2] = (p2 - 2) * kRopeAxisPairs;
+        }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -187,10 +236,14 @@ __global__ __launch_bounds__(64 * kGWaves, 2) void gemm_bf16_kernel(
                         v[e] += __builtin_bit_cast(float, bits << 16);
                     }
                 }
-                u32x2 st;
-                st[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2));
-                st[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2));
-                *reinterpret_cast<u32x2 *>(yrow + 32 * nb + 8 * g) = st;
+                uint32_t s0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2));
+                uint32_t s1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2));
+                if constexpr (ROPE) {
+                    const int k0 = 16 * nb + 4 * g + 2 * hh;  // pair of s0; s1 holds pair k0 + 1
+                    s0 = rope_pair(s0, k0, pb, rp.cs);
+                    s1 = rope_pair(s1, k0 + 1, pb, rp.cs);
+                }
+                *reinterpret_cast<u32x2 *>(yrow + 32 * nb + 8 * g) = u32x2{s0, s1};
             }
     }
 #endif
@@ -202,18 +255,24 @@ int gemm_bf16_tile_n() { return kGBN; }
 int gemm_bf16_tile_k() { return kGBK; }
 
 hipError_t launch_gemm_bf16(const void *x, const void *w, void *y, const void *r, int64_t M, int N,
-                            int K, hipStream_t s) {
+                            int K, const GemmRope *rope, hipStream_t s) {
     if (M <= 0) return hipSuccess;
+    if (rope && (r || N % 128 != 0 || !rope->cid || !rope->pos || !rope->cs)) return hipErrorInvalidValue;
     const int m_tiles = int((M + kGBM - 1) / kGBM), n_tiles = N / kGBN;
     const int64_t blocks = int64_t((m_tiles + 7) / 8) * 8 * n_tiles;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
-    if (r)
-        gemm_bf16_kernel<true><<<dim3(unsigned(blocks)), dim3(64 * kGWaves), 0, s>>>(
-            U(x), U(w), static_cast<uint16_t *>(y), U(r), int(M), N, K, m_tiles, n_tiles);
+    const dim3 grid{unsigned(blocks)}, block{64 * kGWaves};
+    uint16_t *Y = static_cast<uint16_t *>(y);
+    if (rope)
+        gemm_bf16_kernel<false, true><<<grid, block, 0, s>>>(U(x), U(w), Y, nullptr, int(M), N, K, m_tiles,
+                                                             n_tiles, *rope);
+    else if (r)
+        gemm_bf16_kernel<true, false><<<grid, block, 0, s>>>(U(x), U(w), Y, U(r), int(M), N, K, m_tiles,
+                                                             n_tiles, GemmRope{});
     else
-        gemm_bf16_kernel<false><<<dim3(unsigned(blocks)), dim3(64 * kGWaves), 0, s>>>(
-            U(x), U(w), static_cast<uint16_t *>(y), nullptr, int(M), N, K, m_tiles, n_tiles);
+        gemm_bf16_kernel<false, false><<<grid, block, 0, s>>>(U(x), U(w), Y, nullptr, int(M), N, K, m_tiles,
+                                                              n_tiles, GemmRope{});
     return hipGetLastError();
 }
 

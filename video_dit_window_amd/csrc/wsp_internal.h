@@ -190,11 +190,21 @@ hipError_t launch_fp8_amax(const void *x, float *amax, int64_t n_rows, int n_hea
 hipError_t launch_fp8_quantize(const void *x, void *y, const float *amax, int64_t n_rows,
                                int n_heads, int head_dim, int dtype, hipStream_t s);
 // gemm_bf16.hip: y[M,N] = x[M,K] w[N,K]^T (+ r), bf16; N % tile_n == 0,
-// K % tile_k == 0 (checked by the caller).
+// K % tile_k == 0 (checked by the caller).  rope != NULL (r must be NULL):
+// every 128-feature head of row m is rotated after the bf16 rounding, by the
+// axial position of pos[cid[m]] (+ text_len on t) for m < n_video, else
+// (m - n_video) on all three axes; cs = [P][21] (cos, sin) pairs.
+struct GemmRope {
+    const int32_t *cid = nullptr;
+    const int32_t *pos = nullptr;
+    const float2 *cs = nullptr;
+    int n_video = 0;
+    int text_len = 0;
+};
 int gemm_bf16_tile_n();
 int gemm_bf16_tile_k();
 hipError_t launch_gemm_bf16(const void *x, const void *w, void *y, const void *r, int64_t M, int N,
-                            int K, hipStream_t s);
+                            int K, const GemmRope *rope, hipStream_t s);
 // xcd_probe.hip: xcc[b] = the XCD that work group b of an n_blocks launch ran on.
 hipError_t launch_xcd_probe(int32_t *xcc, int n_blocks, hipStream_t s);
 // abi.cpp: the XCD count of device dev and whether work group b of a launch

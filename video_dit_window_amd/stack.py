@@ -10,9 +10,13 @@ canonical token order.  With ``canonical_io=True`` the stream stays in
 canonical order throughout and the attention kernel reads and writes through
 each layout's ids table instead (no standalone permutations).
 
+With ``rope_theta`` set, the q and k projections apply the window-local 3D
+rotary embedding of the layer's layout as they store (wsp_linear_rope; text
+row i at (i, i, i)), the step right before attention in the real block.
+
 Orchestration only: every step is a libwsp call (wsp_linear,
-wsp_window_attn_ex, wsp_relayout); this module allocates buffers with torch
-and passes pointers.
+wsp_linear_rope, wsp_window_attn_ex, wsp_relayout); this module allocates
+buffers with torch and passes pointers.
 """
 from __future__ import annotations
 
@@ -26,9 +30,10 @@ class Stack:
     tensor (one output feature per row), E = heads * head_dim."""
 
     def __init__(self, T, H, W, nt, nh, nw, n_layers, heads, head_dim, text_len, device="cuda",
-                 canonical_io=False):
+                 canonical_io=False, rope_theta=None):
         torch = L._torch()
         self.geo = (T, H, W, nt, nh, nw)
+        self.rope_theta = rope_theta
         self.n_layers, self.heads, self.head_dim, self.text_len = n_layers, heads, head_dim, text_len
         self.E = heads * head_dim
         self.canonical_io = canonical_io
@@ -58,8 +63,14 @@ class Stack:
         (video rows in layer l's layout, or canonical with canonical_io)."""
         wq, wk, wv, wo = weights
         N, Lt = self.N, self.text_len
-        for w, dst in ((wq, self.q), (wk, self.k), (wv, self.v)):
-            L.linear(X, w, out=dst, stream=stream)
+        if self.rope_theta is None:
+            for w, dst in ((wq, self.q), (wk, self.k)):
+                L.linear(X, w, out=dst, stream=stream)
+        else:
+            rows = self.canon if self.canonical_io else self.layout(l)
+            for w, dst in ((wq, self.q), (wk, self.k)):
+                L.linear_rope(X, w, rows, self.layout(l), Lt, theta=self.rope_theta, out=dst, stream=stream)
+        L.linear(X, wv, out=self.v, stream=stream)
         hv = lambda t: self._heads(t[:N], N)
         ht = lambda t: self._heads(t[N:], Lt)
         L.window_attn(self.layout(l), hv(self.q), hv(self.k), hv(self.v), ht(self.q), ht(self.k), ht(self.v),
