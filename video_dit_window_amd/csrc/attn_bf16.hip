@@ -24,7 +24,10 @@
 // waves per SIMD, < 256 registers each (or, for short windows, 4 wavefronts
 // and 128 rows, two work groups per CU).
 //
-// Per 64-key tile and wavefront:
+// Per 64-key tile and wavefront, in two 32-key halves (block 1's score
+// products run between the pieces of block 0's softmax, and the products of
+// block 0's probabilities between the pieces of block 1's, so that a wave
+// keeps its own matrix and vector work overlapped):
 //   S^T = K Q^T     K from LDS as the A operand, Q in registers as B:
 //                   v_mfma_f32_32x32x16_bf16 (bf16), or
 //                   v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 codes (unit E8M0
@@ -32,8 +35,8 @@
 //                   The transposed product leaves each lane with ONE query
 //                   column and 32 of its keys.
 //   softmax         float32, exp2 with the scale folded into one FMA; the
-//                   running maximum is set on a window's first tile and moves
-//                   only when a tile's probabilities would exceed 2^20
+//                   running maximum is set on a window's first half tile and
+//                   moves only when a half's probabilities would exceed 2^20
 //                   (detected from the row sum).
 //   O^T += V^T P^T  the probabilities stay in registers as bf16 B operands;
 //                   V^T comes from the row-major V tile through the gfx950
@@ -474,7 +477,79 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             if (active) {
 
             // S^T for 64 keys (two 32-key blocks) x this wave's 32 queries.
+            // Block 0's products first; block 1's run while block 0's softmax
+            // goes, and the products of block 0's probabilities while block
+            // 1's softmax goes (the online softmax takes the tile in two
+            // 32-key halves).
             f32x16 S[2] = {f32x16{}, f32x16{}};
+            const bool last = (j + 1) * kBN > M;  // keys past the end of the joint sequence
+            // element r of S[mk] is key 32mk + 8(r/4) + (r%4) of the tile
+            // counted from this lane's first, j*kBN + 4hh
+            auto mask = [&](int mk) __attribute__((always_inline)) {
+                const int lim = M - j * kBN - 4 * hh;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * mk + 8 * (r >> 2) + (r & 3) >= lim) S[mk][r] = -INFINITY;
+            };
+            // p = 2^(s*c2 - m_run*c2) of half h packed to bf16 pairs (P^T B
+            // operands, one per 16-key k-step); the row sum adds the same
+            // rounded values.
+            bf16x8 P[4];
+            // Piece q (0..7) of half h: the probabilities of S[h] registers
+            // 8(q/4) + 2(q%4) and + 1, into word q%4 of pk[q/4].
+            auto piece = [&](int h, int q, float mc, float &sum, u32x4 (&pk)[2]) __attribute__((always_inline)) {
+                const int r = 8 * (q >> 2) + 2 * (q & 3);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[h][r], c2, -mc));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[h][r + 1], c2, -mc));
+                const bf16x2 pp = to_bf16x2(p0, p1);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
+                pk[q >> 2][q & 3] = __builtin_bit_cast(uint32_t, pp);
+            };
+            auto probs = [&](int h) __attribute__((always_inline)) {
+                const float mc = m_run * c2;
+                float sum = 0.f;
+                u32x4 pk[2];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) piece(h, q, mc, sum, pk);
+                P[2 * h] = __builtin_bit_cast(bf16x8, pk[0]);
+                P[2 * h + 1] = __builtin_bit_cast(bf16x8, pk[1]);
+                return sum;
+            };
+            // Only on a window's first half tile (m_run = -inf) and when some
+            // probability of a half would exceed 2^20 does the wave take the
+            // exact path: the half's maximum, rescale of O and l by
+            // 2^((m_old - m_new)*c2), recompute.
+            auto settle = [&](int h, float hsum, bool first) __attribute__((always_inline)) {
+                if (first || __builtin_amdgcn_ballot_w64(!(hsum <= kMaxTileSum))) {
+                    float m = S[h][0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) m = fmaxf(m, S[h][r]);
+                    const float m_new = fmaxf(m_run, halves_max(m));
+                    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+                    m_run = m_new;
+                    if (!first) {  // on the first half O and l are still zero
+                        l_run *= alpha;
+#pragma unroll
+                        for (int t = 0; t < VS::DT; ++t) O[t] *= alpha;
+                    }
+                    hsum = probs(h);
+                }
+                l_run += hsum;
+            };
+            // V^T operands (transpose reads) of one 16-key step.
+            auto vread = [&](int cs, bf16x8 (&dst)[VS::DT]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int t = 0; t < VS::DT; ++t) {
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (s16x4 LDS_AS *)(cur + vaddr[t][0] + cs * 16 * VS::ROW));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (s16x4 LDS_AS *)(cur + vaddr[t][1] + cs * 16 * VS::ROW));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                    dst[t] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+                }
+            };
+            bf16x8 va[2][VS::DT];
+            float hs0 = 0.f, hs1 = 0.f;
             if constexpr (Q8) {
                 // two 64-dim k-steps of E4M3 codes per key block
                 v8i ka[2][2];
@@ -489,106 +564,94 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                                         int(b[0]), int(b[1]), int(b[2]), int(b[3])};
                     }
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
+                for (int s = 0; s < 2; ++s) S[0] = mfma8(ka[s][0], Qr8[s], S[0]);
+                if (last) mask(0);
 #pragma unroll
-                    for (int mk = 0; mk < 2; ++mk) S[mk] = mfma8(ka[s][mk], Qr8[s], S[mk]);
+                for (int s = 0; s < 2; ++s) S[1] = mfma8(ka[s][1], Qr8[s], S[1]);
+                vread(0, va[0]);
+                hs0 = probs(0);
             } else {
-                // The K operands of k-step s+2 are read while step s multiplies.
-                bf16x8 ka[VS::KSTEPS][2];
-                auto kread = [&](int s) {
-#pragma unroll
-                    for (int mk = 0; mk < 2; ++mk)
-                        ka[s][mk] = *reinterpret_cast<const bf16x8 LDS_AS *>(cur + kaddr[s] + mk * 32 * KS::ROW);
+                // The K operands run two k-steps ahead of the products, over
+                // block 0's eight k-steps and then block 1's.
+                constexpr int KS2 = 2 * VS::KSTEPS;
+                bf16x8 ka[KS2];
+                auto kread = [&](int f) __attribute__((always_inline)) {
+                    const int mk = f / VS::KSTEPS, st = f % VS::KSTEPS;
+                    ka[f] = *reinterpret_cast<const bf16x8 LDS_AS *>(cur + kaddr[st] + mk * 32 * KS::ROW);
                 };
                 kread(0);
                 kread(1);
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-                for (int s = 0; s < VS::KSTEPS; ++s) {
-#pragma unroll
-                    for (int mk = 0; mk < 2; ++mk) S[mk] = mfma(ka[s][mk], Qr[s], S[mk]);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                    if (s + 2 < VS::KSTEPS) {
-                        kread(s + 2);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    }
+                for (int f = 0; f < VS::KSTEPS; ++f) {
+                    S[0] = mfma(ka[f], Qr[f], S[0]);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    kread(f + 2);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
-            }
-            if ((j + 1) * kBN > M) {  // keys past the end of the joint sequence
-                // element r of S[mk] is key 32mk + 8(r/4) + (r%4) of the tile
-                // counted from this lane's first, j*kBN + 4hh
-                const int lim = M - j * kBN - 4 * hh;
-#pragma unroll
-                for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * mk + 8 * (r >> 2) + (r & 3) >= lim) S[mk][r] = -INFINITY;
-            }
-
-            // p = 2^(s*c2 - m_run*c2) packed to bf16 pairs (P^T B operands, one
-            // per 16-key k-step); the row sum adds the same rounded values.
-            bf16x8 P[4];
-            auto probs = [&]() {
+                if (last) mask(0);
+                // block 1's products, each followed by its operand reads and
+                // a piece of block 0's softmax (six vector instructions,
+                // transcendental ones included).  Also on a window's first
+                // tile, where m_run = -inf makes the softmax non-finite and
+                // the exact path recomputes it: no branch splits this block.
                 const float mc = m_run * c2;
-                float sum = 0.f;
+                u32x4 pk[2];
+                constexpr int PP = 8 / VS::KSTEPS;  // softmax pieces per product
 #pragma unroll
-                for (int cs = 0; cs < 4; ++cs) {
-                    const int mk = cs >> 1, r0 = 8 * (cs & 1);
-                    u32x4 pk;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i], c2, -mc));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[mk][r0 + 2 * i + 1], c2, -mc));
-                        const bf16x2 pp = to_bf16x2(p0, p1);
-                        sum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum, false);
-                        pk[i] = __builtin_bit_cast(uint32_t, pp);
+                for (int f = 0; f < VS::KSTEPS; ++f) {
+                    S[1] = mfma(ka[VS::KSTEPS + f], Qr[f], S[1]);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (f + 2 < VS::KSTEPS) {
+                        kread(VS::KSTEPS + f + 2);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     }
-                    P[cs] = __builtin_bit_cast(bf16x8, pk);
+                    if (f == 0) {
+                        vread(0, va[0]);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VS::DT, 0);
+                    }
+#pragma unroll
+                    for (int q = PP * f; q < PP * f + PP; ++q) piece(0, q, mc, hs0, pk);
+                    __builtin_amdgcn_sched_group_barrier(0x402, 6 * PP, 0);
                 }
-                return sum;
-            };
-            // V^T operands (transpose reads) of one 16-key step; those of the
-            // first step are read while the softmax runs.
-            auto vread = [&](int cs, bf16x8 (&dst)[VS::DT]) {
-#pragma unroll
-                for (int t = 0; t < VS::DT; ++t) {
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (s16x4 LDS_AS *)(cur + vaddr[t][0] + cs * 16 * VS::ROW));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (s16x4 LDS_AS *)(cur + vaddr[t][1] + cs * 16 * VS::ROW));
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                    dst[t] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-                }
-            };
-            bf16x8 va[2][VS::DT];
-            vread(0, va[0]);
-            // Only on a window's first tile (m_run = -inf) and when some
-            // probability would exceed 2^20 does the wave take the exact
-            // path: tile maximum, rescale of O and l by 2^((m_old -
-            // m_new)*c2), recompute.  The first tile goes there directly.
-            float tsum = j == 0 ? 0.f : probs();
-            if (j == 0 || __builtin_amdgcn_ballot_w64(!(tsum <= kMaxTileSum))) {
-                float m = S[0][0];
-#pragma unroll
-                for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) m = fmaxf(m, S[mk][r]);
-                const float m_new = fmaxf(m_run, halves_max(m));
-                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-                m_run = m_new;
-                if (j != 0) {  // on the first tile O and l are still zero
-                    l_run *= alpha;
-#pragma unroll
-                    for (int t = 0; t < VS::DT; ++t) O[t] *= alpha;
-                }
-                tsum = probs();
+                P[0] = __builtin_bit_cast(bf16x8, pk[0]);
+                P[1] = __builtin_bit_cast(bf16x8, pk[1]);
+                // (kept here on every tile: on a window's first tile these
+                // values are recomputed, and the compiler would otherwise
+                // move the softmax under that branch, after the products)
+                asm volatile("" : "+v"(hs0), "+v"(P[0]), "+v"(P[1]));
             }
-            l_run += tsum;
+            settle(0, hs0, j == 0);
+            if (last) mask(1);
 
             // O^T += V^T P^T over the tile's four 16-key k-steps, the operands
-            // of step cs+1 read while step cs multiplies.
+            // of step cs+1 read while step cs multiplies; a piece of block
+            // 1's softmax follows each product of steps 0 and 1.
+            {
+                const float mc = m_run * c2;
+                u32x4 pk[2];
+                constexpr int PP = 4 / VS::DT;  // softmax pieces per product
 #pragma unroll
-            for (int cs = 0; cs < 4; ++cs) {
+                for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+                    for (int t = 0; t < VS::DT; ++t) {
+                        O[t] = mfma(va[cs & 1][t], P[cs], O[t]);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (t == 0) {
+                            vread(cs + 1, va[(cs + 1) & 1]);
+                            __builtin_amdgcn_sched_group_barrier(0x100, 2 * VS::DT, 0);
+                        }
+#pragma unroll
+                        for (int q = PP * (VS::DT * cs + t); q < PP * (VS::DT * cs + t) + PP; ++q)
+                            piece(1, q, mc, hs1, pk);
+                        __builtin_amdgcn_sched_group_barrier(0x402, 6 * PP, 0);
+                    }
+                P[2] = __builtin_bit_cast(bf16x8, pk[0]);
+                P[3] = __builtin_bit_cast(bf16x8, pk[1]);
+            }
+            settle(1, hs1, false);
+#pragma unroll
+            for (int cs = 2; cs < 4; ++cs) {
                 if (cs + 1 < 4) vread(cs + 1, va[(cs + 1) & 1]);
 #pragma unroll
                 for (int t = 0; t < VS::DT; ++t) O[t] = mfma(va[cs & 1][t], P[cs], O[t]);
