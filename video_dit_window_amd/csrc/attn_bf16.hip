@@ -469,6 +469,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
         for (int t = 0; t < VS::DT; ++t) O[t] = f32x16{};
         float m_run = -INFINITY, l_run = 0.f;
         const int ntiles = (M + kBN - 1) / kBN;
+        // A tile's last PV k-step (V^T operands va[1], probabilities P[3])
+        // is multiplied at the start of the next tile, after that tile's
+        // first K operand reads are issued (their latency hides under it),
+        // and after the window's last tile.  Zero operands make the first
+        // tile's deferred step a no-op.
+        bf16x8 P[4];
+        bf16x8 va[2][VS::DT];
+        P[3] = bf16x8{};
+#pragma unroll
+        for (int t = 0; t < VS::DT; ++t) va[1][t] = bf16x8{};
+        auto deferred = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int t = 0; t < VS::DT; ++t) O[t] = mfma(va[1][t], P[3], O[t]);
+        };
 
         // One tile: cur holds tile j; the DMA of tile j+1 goes to nxt.
         auto tile = [&](const uint8_t LDS_AS *cur, uint8_t LDS_AS *nxt, int j, Ids &idu,
@@ -494,7 +508,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             // p = 2^(s*c2 - m_run*c2) of half h packed to bf16 pairs (P^T B
             // operands, one per 16-key k-step); the row sum adds the same
             // rounded values.
-            bf16x8 P[4];
             // Piece q (0..7) of half h: the probabilities of S[h] registers
             // 8(q/4) + 2(q%4) and + 1, into word q%4 of pk[q/4].
             auto piece = [&](int h, int q, float mc, float &sum, u32x4 (&pk)[2]) __attribute__((always_inline)) {
@@ -548,7 +561,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                     dst[t] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
                 }
             };
-            bf16x8 va[2][VS::DT];
             float hs0 = 0.f, hs1 = 0.f;
             if constexpr (Q8) {
                 // two 64-dim k-steps of E4M3 codes per key block
@@ -563,6 +575,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                         ka[s][mk] = v8i{int(a[0]), int(a[1]), int(a[2]), int(a[3]),
                                         int(b[0]), int(b[1]), int(b[2]), int(b[3])};
                     }
+                deferred();
 #pragma unroll
                 for (int s = 0; s < 2; ++s) S[0] = mfma8(ka[s][0], Qr8[s], S[0]);
                 if (last) mask(0);
@@ -582,6 +595,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                 kread(0);
                 kread(1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                deferred();
+                __builtin_amdgcn_sched_group_barrier(0x008, VS::DT, 0);
 #pragma unroll
                 for (int f = 0; f < VS::KSTEPS; ++f) {
                     S[0] = mfma(ka[f], Qr[f], S[0]);
@@ -650,12 +665,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                 P[3] = __builtin_bit_cast(bf16x8, pk[1]);
             }
             settle(1, hs1, false);
+            vread(3, va[1]);
 #pragma unroll
-            for (int cs = 2; cs < 4; ++cs) {
-                if (cs + 1 < 4) vread(cs + 1, va[(cs + 1) & 1]);
-#pragma unroll
-                for (int t = 0; t < VS::DT; ++t) O[t] = mfma(va[cs & 1][t], P[cs], O[t]);
-            }
+            for (int t = 0; t < VS::DT; ++t) O[t] = mfma(va[0][t], P[2], O[t]);
+            // (k-step 3 is multiplied at the start of the next tile)
             }
             // The DMA of tile j+1 has landed (vmcnt) and every wave is done with
             // `cur` before it is overwritten two tiles later.
@@ -708,6 +721,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
             tile(st0, st1, j, idB, idA);
             if (j + 1 < ntiles) tile(st1, st0, j + 1, idA, idB);
         }
+        if (active) deferred();
         // Nothing is in flight here (the last tile waited); saying so lets
         // the next item's descriptor be read after the outputs below without
         // waiting for their stores.
