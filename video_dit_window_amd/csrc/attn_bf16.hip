@@ -489,6 +489,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                         Ids &idn) __attribute__((always_inline)) {
             if (j + 1 < ntiles) dma(nxt, j + 1, idu, idn);
             if (active) {
+            // Wave priority 1 until block 0's softmax is settled, then 0:
+            // of the two waves of a SIMD, the one behind in its tile wins
+            // issue, so the pair reaches the closing barrier together.
+            __builtin_amdgcn_s_setprio(1);
 
             // S^T for 64 keys (two 32-key blocks) x this wave's 32 queries.
             // Block 0's products first; block 1's run while block 0's softmax
@@ -636,6 +640,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_bf16_kernel(
                 // move the softmax under that branch, after the products)
                 asm volatile("" : "+v"(hs0), "+v"(P[0]), "+v"(P[1]));
             }
+            __builtin_amdgcn_s_setprio(0);
             settle(0, hs0, j == 0);
             if (last) mask(1);
 
