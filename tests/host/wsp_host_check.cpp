@@ -299,6 +299,18 @@ static void check_arguments() {
     CHECK(wsp_linear(a, b, nullptr, o, 8, 256, 60, WSP_BF16, nullptr) == WSP_EINVAL);
     CHECK(wsp_linear(a, b, nullptr, a, 8, 256, 64, WSP_BF16, nullptr) == WSP_EINVAL);
     CHECK(wsp_linear(a, b, nullptr, o, 0, 256, 64, WSP_BF16, nullptr) == WSP_OK);
+    // wsp_linear_rope: M must be the plan's tokens + text rows; plans of one grid
+    const int64_t n_p = 5 * 20 * 36;
+    CHECK(wsp_linear_rope(a, b, o, n_p, 256, 64, WSP_BF16, p, p, 16, 0.f, nullptr) == WSP_EINVAL);
+    CHECK(wsp_linear_rope(a, b, o, n_p + 16, 256, 64, WSP_BF16, nullptr, p, 16, 0.f, nullptr) == WSP_EINVAL);
+    CHECK(wsp_linear_rope(a, b, o, n_p + 16, 256, 64, WSP_BF16, p, other, 16, 0.f, nullptr) == WSP_EINVAL);
+    CHECK(wsp_linear_rope(a, b, o, n_p + 16, 128, 64, WSP_BF16, p, p, 16, 0.f, nullptr) == WSP_EINVAL);
+    CHECK(wsp_linear_rope(a, b, a, n_p + 16, 256, 64, WSP_BF16, p, p, 16, 0.f, nullptr) == WSP_EINVAL);
+    CHECK(wsp_linear_rope(a, b, o, n_p - 1, 256, 64, WSP_BF16, p, p, -1, 0.f, nullptr) == WSP_EINVAL);
+    wsp_plan_t *tall2 = nullptr;
+    CHECK(wsp_plan(2, 6000, 2, 1, 1, 1, WSP_REGULAR, &tall2) == WSP_OK);
+    CHECK(wsp_linear_rope(a, b, o, 2 * 6000 * 2, 256, 64, WSP_BF16, tall2, tall2, 0, 0.f, nullptr) == WSP_ERANGE);
+    wsp_plan_free(tall2);
     CHECK(wsp_set_attn_order(7) == WSP_EINVAL);
     int nx = 0, rr = 0;
     CHECK(wsp_device_info(nullptr, &rr) == WSP_EINVAL);
