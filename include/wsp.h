@@ -487,9 +487,10 @@ int wsp_linear(const void *x, const void *w, const void *r, void *y, int64_t M, 
  *
  * "Window-Aligned Sequence Parallelism (SeedVR2)", section "Reference quirks
  * reproduced on purpose" (a video token turns by its offset from its own
- * window's corner, the temporal index raised by text_len; 126 of 128
- * channels); the readings of wsp_rope_relayout (axis blocks, pair layout,
- * theta, text positions (i, i, i)).
+ * window's corner, the temporal index raised by text_len; a 128-wide head
+ * turns its first 126 channels and copies the last two); the readings of
+ * wsp_rope_relayout (axis blocks, pair layout, theta, text positions
+ * (i, i, i)).
  *
  * x [M, K], w [N, K], y [M, N]: row-major bfloat16 device arrays owned by the
  * caller, 16-byte aligned, y aliasing neither x nor w.  M = rows' token count

@@ -27,8 +27,9 @@
 // rotary embedding applied where the products are stored ("Window-Aligned
 // Sequence Parallelism (SeedVR2)", section "Reference quirks reproduced on
 // purpose": a video token turns by its offset from its own window's corner,
-// the temporal index raised by the text length; 126 of 128 channels turn, in
-// three 42-channel axis blocks of adjacent pairs; text token i uses (i, i, i)).
+// the temporal index raised by the text length; a 128-wide head turns its
+// first 126 channels, in three 42-channel axis blocks of adjacent pairs, and
+// copies the last two; text token i uses (i, i, i)).
 // Every 128 output features form one head.  The epilogue holds four
 // consecutive features of a row per lane, i.e. two whole pairs, so each pair
 // turns in registers: the product is rounded to bfloat16 first and the
