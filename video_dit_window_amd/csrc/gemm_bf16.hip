@@ -20,8 +20,9 @@
 // XOR-swizzled by (row / 2) % 8 so that the 32-row operand reads spread over
 // the banks), double-buffered against the products of the previous slab.
 // Tiles are mapped so that the 256-row slabs of x go round-robin to the 8
-// XCDs (work group b runs on XCD b % 8) and the N tiles of one x slab run
-// side by side on one XCD, sharing the slab through its L2.
+// XCDs (work group b runs on XCD b % 8); on an XCD, groups of four slabs
+// run w tile by w tile, so that work groups running side by side share
+// their x slabs and w tiles through the XCD's L2.
 //
 // ROPE: the q / k projections of a window layer, with the window-local 3D
 // rotary embedding applied where the products are stored ("Window-Aligned
@@ -58,6 +59,7 @@ constexpr int kGRow = kGBK * 2;              // bytes per slab row in LDS
 constexpr int kGTile = kGBM * kGRow;         // one 256-row slab: 32 KB
 constexpr int kGLoads = kGBM / 8 / kGWaves;  // DMA instructions per wave per slab (8 rows each)
 constexpr int kBufferFlags = 0x00020000;     // raw buffer resource word 3 on gfx9-family parts
+constexpr int kGroup = 4;                    // x slabs per group of an XCD's tile order
 
 __device__ __host__ constexpr int gswz(int r) { return (r >> 1) & 7; }
 
@@ -90,10 +92,18 @@ __global__ __launch_bounds__(64 * kGWaves, 2) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t sx1[kGTile];
     __shared__ __attribute__((aligned(1024))) uint8_t sw1[kGTile];
 
-    // Tile of this work group: x slab m_t goes to XCD m_t % 8; on that XCD
-    // the slab's n_tiles tiles take consecutive slots.
+    // Tile of this work group: x slab m_t goes to XCD m_t % 8.  On that XCD
+    // the slots run through groups of kGroup x slabs (the last group: the
+    // slabs left over), and within a group through the w tiles, each w tile
+    // for the group's slabs side by side: the ~32 work groups that run at a
+    // time on an XCD then cover a few x slabs and w tiles, whose K slabs
+    // they share through the XCD's L2.
     const int b = int(blockIdx.x), xcd = b & 7, slot = b >> 3;
-    const int m_t = (slot / n_tiles) * 8 + xcd, n_t = slot % n_tiles;
+    const int m8 = (m_tiles + 7) / 8, full = (m8 / kGroup) * kGroup * n_tiles;
+    const int gs = slot < full ? kGroup : m8 - (m8 / kGroup) * kGroup;  // > 0 wherever used
+    const int g0 = slot < full ? (slot / (kGroup * n_tiles)) * kGroup : (m8 / kGroup) * kGroup;
+    const int in = slot < full ? slot % (kGroup * n_tiles) : slot - full;
+    const int m_t = (g0 + in % gs) * 8 + xcd, n_t = in / gs;
     if (m_t >= m_tiles) return;
     const int m0 = m_t * kGBM, n0 = n_t * kGBN;
     const int rows_x = min(kGBM, M - m0);
