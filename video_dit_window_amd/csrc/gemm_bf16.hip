@@ -20,9 +20,9 @@
 // XOR-swizzled by (row / 2) % 8 so that the 32-row operand reads spread over
 // the banks), double-buffered against the products of the previous slab.
 // Tiles are mapped so that the 256-row slabs of x go round-robin to the 8
-// XCDs (work group b runs on XCD b % 8); on an XCD, groups of four slabs
-// run w tile by w tile, so that work groups running side by side share
-// their x slabs and w tiles through the XCD's L2.
+// XCDs (work group b runs on XCD b % 8); on an XCD, groups of slabs that
+// fill its 32 CUs once run w tile by w tile, so that work groups running
+// side by side share their x slabs and w tiles through the XCD's L2.
 //
 // ROPE: the q / k projections of a window layer, with the window-local 3D
 // rotary embedding applied where the products are stored ("Window-Aligned
@@ -59,7 +59,7 @@ constexpr int kGRow = kGBK * 2;              // bytes per slab row in LDS
 constexpr int kGTile = kGBM * kGRow;         // one 256-row slab: 32 KB
 constexpr int kGLoads = kGBM / 8 / kGWaves;  // DMA instructions per wave per slab (8 rows each)
 constexpr int kBufferFlags = 0x00020000;     // raw buffer resource word 3 on gfx9-family parts
-constexpr int kGroup = 4;                    // x slabs per group of an XCD's tile order
+constexpr int kCusPerXcd = 32;               // MI355X: 256 CUs in 8 XCDs
 
 __device__ __host__ constexpr int gswz(int r) { return (r >> 1) & 7; }
 
@@ -85,7 +85,7 @@ __device__ inline uint32_t rope_pair(uint32_t w, int k, const int (&pb)[3], cons
 template <bool RES, bool ROPE>
 __global__ __launch_bounds__(64 * kGWaves, 2) void gemm_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *y,
-    const uint16_t *r, int M, int N, int K, int m_tiles, int n_tiles, GemmRope rp) {
+    const uint16_t *r, int M, int N, int K, int m_tiles, int n_tiles, int group, GemmRope rp) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
     __shared__ __attribute__((aligned(1024))) uint8_t sx0[kGTile];
     __shared__ __attribute__((aligned(1024))) uint8_t sw0[kGTile];
@@ -93,16 +93,17 @@ __global__ __launch_bounds__(64 * kGWaves, 2) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t sw1[kGTile];
 
     // Tile of this work group: x slab m_t goes to XCD m_t % 8.  On that XCD
-    // the slots run through groups of kGroup x slabs (the last group: the
+    // the slots run through groups of `group` x slabs (the last group: the
     // slabs left over), and within a group through the w tiles, each w tile
-    // for the group's slabs side by side: the ~32 work groups that run at a
-    // time on an XCD then cover a few x slabs and w tiles, whose K slabs
-    // they share through the XCD's L2.
+    // for the group's slabs side by side.  The host sizes a group so that it
+    // fills the XCD's CUs once (group x n_tiles ~ 32): the work groups that
+    // run at a time on an XCD then share their x slabs and w tiles through
+    // the XCD's L2.
     const int b = int(blockIdx.x), xcd = b & 7, slot = b >> 3;
-    const int m8 = (m_tiles + 7) / 8, full = (m8 / kGroup) * kGroup * n_tiles;
-    const int gs = slot < full ? kGroup : m8 - (m8 / kGroup) * kGroup;  // > 0 wherever used
-    const int g0 = slot < full ? (slot / (kGroup * n_tiles)) * kGroup : (m8 / kGroup) * kGroup;
-    const int in = slot < full ? slot % (kGroup * n_tiles) : slot - full;
+    const int m8 = (m_tiles + 7) / 8, full = (m8 / group) * group * n_tiles;
+    const int gs = slot < full ? group : m8 - (m8 / group) * group;  // > 0 wherever used
+    const int g0 = slot < full ? (slot / (group * n_tiles)) * group : (m8 / group) * group;
+    const int in = slot < full ? slot % (group * n_tiles) : slot - full;
     const int m_t = (g0 + in % gs) * 8 + xcd, n_t = in / gs;
     if (m_t >= m_tiles) return;
     const int m0 = m_t * kGBM, n0 = n_t * kGBN;
@@ -270,6 +271,7 @@ hipError_t launch_gemm_bf16(const void *x, const void *w, void *y, const void *r
     if (M <= 0) return hipSuccess;
     if (rope && (r || N % 128 != 0 || !rope->cid || !rope->pos || !rope->cs)) return hipErrorInvalidValue;
     const int m_tiles = int((M + kGBM - 1) / kGBM), n_tiles = N / kGBN;
+    const int group = std::max(1, (kCusPerXcd + n_tiles / 2) / n_tiles);
     const int64_t blocks = int64_t((m_tiles + 7) / 8) * 8 * n_tiles;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     auto U = [](const void *p) { return static_cast<const uint16_t *>(p); };
@@ -277,13 +279,13 @@ hipError_t launch_gemm_bf16(const void *x, const void *w, void *y, const void *r
     uint16_t *Y = static_cast<uint16_t *>(y);
     if (rope)
         gemm_bf16_kernel<false, true><<<grid, block, 0, s>>>(U(x), U(w), Y, nullptr, int(M), N, K, m_tiles,
-                                                             n_tiles, *rope);
+                                                             n_tiles, group, *rope);
     else if (r)
         gemm_bf16_kernel<true, false><<<grid, block, 0, s>>>(U(x), U(w), Y, U(r), int(M), N, K, m_tiles,
-                                                             n_tiles, GemmRope{});
+                                                             n_tiles, group, GemmRope{});
     else
         gemm_bf16_kernel<false, false><<<grid, block, 0, s>>>(U(x), U(w), Y, nullptr, int(M), N, K, m_tiles,
-                                                              n_tiles, GemmRope{});
+                                                              n_tiles, group, GemmRope{});
     return hipGetLastError();
 }
 
